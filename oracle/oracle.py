@@ -1,0 +1,258 @@
+"""CPU oracle for the Whisper-style pre-LN encoder block (float64, numpy).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or execute this module;
+only the tests, the smoke check and the benchmark's CPU-baseline leg use it.  It shares no code
+with the HIP library: it reads plain numpy arrays in PyTorch layout (weights ``[n_out, n_in]``).
+
+Every step is written the plain way, in float64 from fp32 inputs, with a library matmul or
+``erf`` as the only primitives.  The steps and their sources (three Rust engines whose source
+pages describe the same block):
+
+  * LayerNorm - two passes: mean, then biased variance of the centred values, ``eps = 1e-5``
+    inside the square root, then the affine (inferencelayer ``whisper_gpu.rs``, ``LN_SRC``
+    shader; oxinfer ``whisper/model.rs``, ``LN_EPS``).
+  * Q, K, V projections, K without a bias (turbospark-runtime ``whisper/metal.rs``,
+    ``EncLayerGpu`` doc and ``encode_layer``; oxinfer ``encode``).
+  * Bidirectional scaled-dot-product attention per head, ``score = q.k * hd^-0.5`` over every key,
+    softmax, weighted sum of V, evaluated with the online (running max / running denominator)
+    recurrence over tiles of 128 keys (inferencelayer ``VANILLA_ATTN`` doc and shader).
+  * Output projection and residual add; second LayerNorm; fc1, erf-GELU, fc2 and residual add
+    (inferencelayer ``WhisperEncoderGpu::forward``; turbospark-runtime ``encode_layer``;
+    oxinfer ``encode``).
+  * A stack repeats the block and ends in an optional final LayerNorm (inferencelayer
+    ``forward``, ``ln_post``; oxinfer ``encode``, ``enc_ln``).
+
+Readings taken where the pages leave a step open:
+  * GELU is the exact-erf form ``0.5 z (1 + erf(z / sqrt 2))``; the pages name it ("GeluErf",
+    ``gelu_erf``) without printing it.
+  * A missing K bias is a zero bias; softmax is shift-invariant per query, so any K bias leaves the
+    output unchanged (tested).
+  * Windows of a batch never attend across each other (each page encodes one window at a time).
+  * The ``exp`` is the exact one (oxinfer's decoder uses a fast approximation; the encoder
+    attention the pages describe uses ``exp``).
+
+Cross-check formulations (used only by the tests):
+  * ``attention_two_pass`` - exact max pass, exponent/sum pass, weighted sum (inferencelayer
+    ``DEC_QATTN`` shader; turbospark-runtime ``encode_layer`` score planes + ``softmax_rows``).
+  * ``attention_split_kv`` - per-chunk (max, denominator, unnormalised sum) partials merged by
+    rescaling with ``exp(m_chunk - m)`` (oxinfer ``CrossLayer::attend``).
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+from scipy.special import erf as _erf
+
+LN_EPS = 1e-5
+KEY_TILE = 128
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def layer_norm(x, gamma, beta, eps: float = LN_EPS) -> np.ndarray:
+    """Row-wise LayerNorm over the last axis: two-pass mean and biased variance.
+
+    inferencelayer ``whisper_gpu.rs``, ``LN_SRC``: mean of the row, then the mean of squared
+    deviations from it, ``inv = 1/sqrt(var + 1e-5)``, ``y = (x - mean) * inv * w + b``.
+    """
+    x = _f64(x)
+    h = x.shape[-1]
+    mean = x.sum(axis=-1, keepdims=True) / h
+    dev = x - mean
+    var = (dev * dev).sum(axis=-1, keepdims=True) / h
+    inv = 1.0 / np.sqrt(var + eps)
+    return dev * inv * _f64(gamma) + _f64(beta)
+
+
+def gelu_erf(z) -> np.ndarray:
+    """Exact-erf GELU, ``0.5 * z * (1 + erf(z / sqrt(2)))``."""
+    z = _f64(z)
+    return 0.5 * z * (1.0 + _erf(z / math.sqrt(2.0)))
+
+
+def linear(a, w, b=None) -> np.ndarray:
+    """``a @ w.T + b`` with ``w`` in PyTorch ``[n_out, n_in]`` layout."""
+    y = _f64(a) @ _f64(w).T
+    if b is not None:
+        y = y + _f64(b)
+    return y
+
+
+def _heads(x: np.ndarray, heads: int) -> np.ndarray:
+    """``[t, d]`` -> ``[heads, t, hd]``: head ``h`` owns columns ``h*hd .. h*hd + hd - 1``."""
+    t, d = x.shape
+    return x.reshape(t, heads, d // heads).transpose(1, 0, 2)
+
+
+def _merge_heads(o: np.ndarray) -> np.ndarray:
+    h, t, hd = o.shape
+    return o.transpose(1, 0, 2).reshape(t, h * hd)
+
+
+def attention_online(q, k, v, heads: int, tile: int = KEY_TILE, return_probs: bool = False):
+    """Bidirectional attention of one window via the online-softmax recurrence.
+
+    inferencelayer ``VANILLA_ATTN``: for each (query row, head), keys are visited in tiles of
+    128; for each tile the running max ``m`` becomes ``max(m, max_j s_j)``, the old state is
+    scaled by ``corr = exp(m_old - m_new)``, ``p_j = exp(s_j - m_new)``, the denominator becomes
+    ``l * corr + sum_j p_j`` and the accumulator ``acc * corr + sum_j p_j v_j``; the output is
+    ``acc / l``.  ``s_j = (q . k_j) * hd^-0.5`` and there is no mask (bidirectional).  Here every
+    query row of a head runs the same recurrence side by side (one row per numpy row).
+
+    ``q``: ``[tq, d]`` (any subset of the window's query rows), ``k, v``: ``[t, d]``.  Returns
+    ``[tq, d]`` (and, with ``return_probs``, the normalised probabilities ``[heads, tq, t]``
+    rebuilt from the final ``m`` and ``l``, for invariant checks).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    tq, t = q.shape[0], k.shape[0]
+    qh, kh, vh = _heads(q, heads), _heads(k, heads), _heads(v, heads)
+    hd = qh.shape[-1]
+    scale = hd ** -0.5
+    out = np.empty_like(qh)
+    probs = np.empty((heads, tq, t)) if return_probs else None
+    for h in range(heads):
+        m = np.full(tq, -np.inf)
+        den = np.zeros(tq)
+        acc = np.zeros((tq, hd))
+        for j0 in range(0, t, tile):
+            j1 = min(j0 + tile, t)
+            s = (qh[h] @ kh[h, j0:j1].T) * scale
+            m_new = np.maximum(m, s.max(axis=1))
+            corr = np.exp(m - m_new)
+            p = np.exp(s - m_new[:, None])
+            den = den * corr + p.sum(axis=1)
+            acc = acc * corr[:, None] + p @ vh[h, j0:j1]
+            m = m_new
+        out[h] = acc / den[:, None]
+        if return_probs:
+            s_all = (qh[h] @ kh[h].T) * scale
+            probs[h] = np.exp(s_all - m[:, None]) / den[:, None]
+    o = _merge_heads(out)
+    return (o, probs) if return_probs else o
+
+
+def attention_two_pass(q, k, v, heads: int) -> np.ndarray:
+    """Same attention with the softmax taken in two explicit passes over a materialised score row.
+
+    inferencelayer ``DEC_QATTN``: pass 1 finds the exact row max, pass 2 forms ``exp(s - max)``
+    and its sum, then the output is ``sum_j p_j v_j / sum_j p_j``.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    qh, kh, vh = _heads(q, heads), _heads(k, heads), _heads(v, heads)
+    scale = qh.shape[-1] ** -0.5
+    out = np.empty_like(qh)
+    for h in range(heads):
+        s = (qh[h] @ kh[h].T) * scale
+        mx = s.max(axis=1, keepdims=True)
+        e = np.exp(s - mx)
+        out[h] = (e @ vh[h]) / e.sum(axis=1, keepdims=True)
+    return _merge_heads(out)
+
+
+def attention_split_kv(q, k, v, heads: int, chunks: int) -> np.ndarray:
+    """Same attention over ``chunks`` key ranges, merged from per-chunk partial softmax states.
+
+    oxinfer ``CrossLayer::attend``: each chunk keeps its own max ``m_c``, denominator ``l_c`` and
+    unnormalised sum ``o_c``; the merge takes ``m = max_c m_c`` and sums ``exp(m_c - m) * l_c`` and
+    ``exp(m_c - m) * o_c``.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    qh, kh, vh = _heads(q, heads), _heads(k, heads), _heads(v, heads)
+    t = qh.shape[1]
+    scale = qh.shape[-1] ** -0.5
+    bounds = np.linspace(0, t, chunks + 1).round().astype(int)
+    out = np.empty_like(qh)
+    for h in range(heads):
+        parts = []
+        for c in range(chunks):
+            j0, j1 = bounds[c], bounds[c + 1]
+            if j1 <= j0:
+                continue
+            s = (qh[h] @ kh[h, j0:j1].T) * scale
+            mc = s.max(axis=1)
+            e = np.exp(s - mc[:, None])
+            parts.append((mc, e.sum(axis=1), e @ vh[h, j0:j1]))
+        m = np.max(np.stack([p[0] for p in parts]), axis=0)
+        den = np.zeros(t)
+        acc = np.zeros_like(out[h])
+        for mc, lc, oc in parts:
+            w = np.exp(mc - m)
+            den += w * lc
+            acc += w[:, None] * oc
+        out[h] = acc / den[:, None]
+    return _merge_heads(out)
+
+
+def _window_block(x: np.ndarray, p: Dict[str, Optional[np.ndarray]], heads: int) -> np.ndarray:
+    """One pre-LN block on one window ``x [t, d]`` (float64 in, float64 out)."""
+    a = layer_norm(x, p["ln1_g"], p["ln1_b"])
+    q = linear(a, p["wq"], p["bq"])
+    k = linear(a, p["wk"], p.get("bk"))
+    v = linear(a, p["wv"], p["bv"])
+    o = attention_online(q, k, v, heads)
+    x1 = x + linear(o, p["wo"], p["bo"])
+    a2 = layer_norm(x1, p["ln2_g"], p["ln2_b"])
+    hid = gelu_erf(linear(a2, p["w1"], p["b1"]))
+    return x1 + linear(hid, p["w2"], p["b2"])
+
+
+def encoder_block(x, p: Dict[str, Optional[np.ndarray]], heads: int) -> np.ndarray:
+    """Pre-LN encoder block over ``x`` of shape ``[t, d]`` or ``[batch, t, d]``.
+
+    ``x += out(attn(LN1 x))`` then ``x += fc2(gelu(fc1(LN2 x)))``; each window attends only
+    within itself.
+    """
+    x = _f64(x)
+    if x.ndim == 2:
+        return _window_block(x, p, heads)
+    return np.stack([_window_block(w, p, heads) for w in x])
+
+
+def encoder_stack(x, layers: Sequence[Dict[str, Optional[np.ndarray]]], heads: int,
+                  ln_post=None) -> np.ndarray:
+    """``len(layers)`` blocks in order, then the final LayerNorm when ``ln_post = (g, b)``."""
+    h = _f64(x)
+    for p in layers:
+        h = encoder_block(h, p, heads)
+    if ln_post is not None:
+        h = layer_norm(h, ln_post[0], ln_post[1])
+    return h
+
+
+def encoder_block_rows(x_window, p: Dict[str, Optional[np.ndarray]], heads: int,
+                       rows: Sequence[int]) -> np.ndarray:
+    """Block output for the selected rows of one window ``[t, d]``.
+
+    Same arithmetic as ``encoder_block`` applied to those rows only: every key and value of the
+    window is still formed (attention reads all of them), but queries, the residual branch and the
+    FFN run for the selected rows.  Lets a test check sampled outputs of a large batch.
+    """
+    x = _f64(x_window)
+    rows = np.asarray(rows, dtype=np.int64)
+    a = layer_norm(x, p["ln1_g"], p["ln1_b"])
+    k = linear(a, p["wk"], p.get("bk"))
+    v = linear(a, p["wv"], p["bv"])
+    q = linear(a[rows], p["wq"], p["bq"])
+    o = attention_online(q, k, v, heads)
+    x1 = x[rows] + linear(o, p["wo"], p["bo"])
+    a2 = layer_norm(x1, p["ln2_g"], p["ln2_b"])
+    return x1 + linear(gelu_erf(linear(a2, p["w1"], p["b1"])), p["w2"], p["b2"])
+
+
+def max_rel_error(got, ref) -> float:
+    """``max_i |g_i - o_i| / max(|o_i|, rms(o))``: each element's relative error, floored at the
+    reference tensor's RMS so that entries near zero do not dominate."""
+    g, o = _f64(got), _f64(ref)
+    rms = math.sqrt(float(np.mean(o * o))) if o.size else 0.0
+    floor = np.maximum(np.abs(o), rms if rms > 0 else 1.0)
+    return float(np.max(np.abs(g - o) / floor)) if o.size else 0.0
+
+
+def mean_abs_error(got, ref) -> float:
+    g, o = _f64(got), _f64(ref)
+    return float(np.mean(np.abs(g - o))) if o.size else 0.0

@@ -1,0 +1,372 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself.
+
+Independent library implementations (PyTorch's float64 CPU LayerNorm, GELU and scaled-dot-product
+attention, and the Hugging Face ``WhisperEncoderLayer``), closed forms, invariants and brute force
+on tiny inputs.  The mutation tests at the end plant plausible mistakes into the oracle and show
+that the pins catch them.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import oracle as orc
+from speech_transformer_encoder_amd import synth
+
+pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
+
+
+def _rng(seed):
+    return np.random.default_rng([seed, 4242])
+
+
+def _rand_layer(seed, d, f, affine=True):
+    r = _rng(seed)
+    p = {
+        "wq": r.standard_normal((d, d)) * 0.08, "bq": r.standard_normal(d) * 0.1,
+        "wk": r.standard_normal((d, d)) * 0.08, "bk": None,
+        "wv": r.standard_normal((d, d)) * 0.08, "bv": r.standard_normal(d) * 0.1,
+        "wo": r.standard_normal((d, d)) * 0.08, "bo": r.standard_normal(d) * 0.1,
+        "w1": r.standard_normal((f, d)) * 0.08, "b1": r.standard_normal(f) * 0.1,
+        "w2": r.standard_normal((d, f)) * 0.08, "b2": r.standard_normal(d) * 0.1,
+        "ln1_g": 1 + r.standard_normal(d) * 0.2 if affine else np.ones(d),
+        "ln1_b": r.standard_normal(d) * 0.2 if affine else np.zeros(d),
+        "ln2_g": 1 + r.standard_normal(d) * 0.2 if affine else np.ones(d),
+        "ln2_b": r.standard_normal(d) * 0.2 if affine else np.zeros(d),
+    }
+    return p
+
+
+def _hf_layer(p, d, heads, f):
+    from transformers import WhisperConfig
+    from transformers.models.whisper.modeling_whisper import WhisperEncoderLayer
+    cfg = WhisperConfig(d_model=d, encoder_attention_heads=heads, encoder_ffn_dim=f,
+                        activation_function="gelu", dropout=0.0, attention_dropout=0.0,
+                        activation_dropout=0.0)
+    cfg._attn_implementation = "eager"
+    layer = WhisperEncoderLayer(cfg).double().eval()
+    t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64))
+    sa = layer.self_attn
+    with torch.no_grad():
+        sa.q_proj.weight.copy_(t(p["wq"])); sa.q_proj.bias.copy_(t(p["bq"]))
+        sa.k_proj.weight.copy_(t(p["wk"]))
+        sa.v_proj.weight.copy_(t(p["wv"])); sa.v_proj.bias.copy_(t(p["bv"]))
+        sa.out_proj.weight.copy_(t(p["wo"])); sa.out_proj.bias.copy_(t(p["bo"]))
+        layer.self_attn_layer_norm.weight.copy_(t(p["ln1_g"]))
+        layer.self_attn_layer_norm.bias.copy_(t(p["ln1_b"]))
+        layer.final_layer_norm.weight.copy_(t(p["ln2_g"]))
+        layer.final_layer_norm.bias.copy_(t(p["ln2_b"]))
+        layer.fc1.weight.copy_(t(p["w1"])); layer.fc1.bias.copy_(t(p["b1"]))
+        layer.fc2.weight.copy_(t(p["w2"])); layer.fc2.bias.copy_(t(p["b2"]))
+    return layer
+
+
+def _hf_block(p, x, heads):
+    d = x.shape[-1]
+    f = p["w1"].shape[0]
+    layer = _hf_layer(p, d, heads, f)
+    xt = torch.tensor(np.asarray(x, np.float64))
+    if xt.ndim == 2:
+        xt = xt[None]
+    with torch.no_grad():
+        y = layer(xt, attention_mask=None)
+    if isinstance(y, tuple):
+        y = y[0]
+    return y.numpy().reshape(np.shape(x))
+
+
+def _sdpa(q, k, v, heads):
+    t, d = q.shape
+    hd = d // heads
+    f = lambda a: torch.tensor(a).reshape(-1, heads, hd).transpose(0, 1)[None]
+    o = torch.nn.functional.scaled_dot_product_attention(f(q), f(k), f(v))
+    return o[0].transpose(0, 1).reshape(-1, d).numpy()
+
+
+# ---------------------------------------------------------------- attention
+
+
+@pytest.mark.parametrize("t,heads,hd", [(300, 2, 64), (129, 3, 32), (1500, 1, 64), (1, 2, 64)])
+def test_attention_matches_torch_sdpa(t, heads, hd):
+    r = _rng(t)
+    q, k, v = (r.standard_normal((t, heads * hd)) for _ in range(3))
+    got = oracle.attention_online(q, k, v, heads)
+    np.testing.assert_allclose(got, _sdpa(q, k, v, heads), rtol=0, atol=1e-12)
+
+
+def test_attention_brute_force_loops():
+    """Pure-Python definition on a tiny case: softmax over all keys, weighted sum of V."""
+    r = _rng(7)
+    t, heads, hd = 5, 2, 4
+    q, k, v = (r.standard_normal((t, heads * hd)) for _ in range(3))
+    ref = np.zeros((t, heads * hd))
+    for h in range(heads):
+        c = slice(h * hd, (h + 1) * hd)
+        for i in range(t):
+            s = [sum(q[i, c][u] * k[j, c][u] for u in range(hd)) / math.sqrt(hd) for j in range(t)]
+            mx = max(s)
+            e = [math.exp(x - mx) for x in s]
+            z = sum(e)
+            for u in range(hd):
+                ref[i, h * hd + u] = sum(e[j] * v[j, c][u] for j in range(t)) / z
+    np.testing.assert_allclose(oracle.attention_online(q, k, v, heads, tile=2), ref, atol=1e-14)
+
+
+@pytest.mark.parametrize("tile", [1, 7, 64, 128, 2000])
+def test_online_two_pass_split_kv_agree(tile):
+    r = _rng(11)
+    t, heads = 1500, 2
+    q, k, v = (r.standard_normal((t, heads * 64)) for _ in range(3))
+    q[r.choice(t, 75, replace=False)] *= 20.0  # logit spreads of ~100: corr underflows to 0
+    a = oracle.attention_online(q, k, v, heads, tile=tile)
+    b = oracle.attention_two_pass(q, k, v, heads)
+    c = oracle.attention_split_kv(q, k, v, heads, chunks=5)
+    np.testing.assert_allclose(a, b, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(c, b, atol=1e-12, rtol=0)
+
+
+def test_attention_single_key_returns_v():
+    r = _rng(3)
+    q, k, v = (r.standard_normal((1, 128)) for _ in range(3))
+    np.testing.assert_array_equal(oracle.attention_online(q, k, v, 2), v)
+
+
+def test_attention_identical_keys_give_mean_of_v():
+    r = _rng(4)
+    t, heads = 257, 2
+    q, v = r.standard_normal((t, 128)), r.standard_normal((t, 128))
+    k = np.tile(r.standard_normal((1, 128)), (t, 1))
+    got = oracle.attention_online(q, k, v, heads)
+    np.testing.assert_allclose(got, np.tile(v.mean(axis=0), (t, 1)), atol=1e-13)
+
+
+def test_attention_probabilities_sum_to_one_and_k_bias_invariance():
+    r = _rng(5)
+    t, heads = 300, 2
+    q, k, v = (r.standard_normal((t, 128)) for _ in range(3))
+    o, p = oracle.attention_online(q, k, v, heads, return_probs=True)
+    np.testing.assert_allclose(p.sum(axis=-1), 1.0, atol=1e-13)
+    assert (p >= 0).all()
+    # each output row is the probability-weighted mean of V
+    np.testing.assert_allclose(o[:, :64], p[0] @ v[:, :64], atol=1e-12)
+    # a K bias adds q_i.b to every score of row i: the softmax does not move
+    kb = k + r.standard_normal(128)
+    np.testing.assert_allclose(oracle.attention_online(q, kb, v, heads), o, atol=1e-12)
+
+
+def test_attention_query_subset_matches_full():
+    r = _rng(6)
+    t, heads = 300, 2
+    q, k, v = (r.standard_normal((t, 128)) for _ in range(3))
+    rows = [0, 5, 128, 299]
+    full = oracle.attention_online(q, k, v, heads)
+    np.testing.assert_allclose(oracle.attention_online(q[rows], k, v, heads), full[rows], atol=1e-14)
+
+
+# ---------------------------------------------------------------- LayerNorm and GELU
+
+
+def test_layer_norm_matches_torch_and_invariants():
+    r = _rng(8)
+    x = r.standard_normal((50, 384)) * 3 + 1.5
+    g, b = r.standard_normal(384), r.standard_normal(384)
+    ref = torch.nn.functional.layer_norm(torch.tensor(x), (384,), torch.tensor(g), torch.tensor(b),
+                                         eps=1e-5).numpy()
+    np.testing.assert_allclose(oracle.layer_norm(x, g, b), ref, atol=1e-12)
+    y = oracle.layer_norm(x, np.ones(384), np.zeros(384))
+    np.testing.assert_allclose(y.mean(axis=1), 0.0, atol=1e-13)
+    var = x.var(axis=1)
+    np.testing.assert_allclose(y.var(axis=1), var / (var + 1e-5), rtol=1e-12)
+    # a constant row maps to beta
+    np.testing.assert_allclose(oracle.layer_norm(np.full((2, 384), 7.0), g, b), np.tile(b, (2, 1)),
+                               atol=1e-12)
+    # scale and shift invariance up to the eps term
+    y2 = oracle.layer_norm(20.0 * x - 3.0, np.ones(384), np.zeros(384))
+    np.testing.assert_allclose(y2, y, atol=1e-5)
+
+
+def test_gelu_erf_values_and_identities():
+    z = np.linspace(-8, 8, 2001)
+    ref = torch.nn.functional.gelu(torch.tensor(z), approximate="none").numpy()
+    np.testing.assert_allclose(oracle.gelu_erf(z), ref, atol=1e-15)
+    assert oracle.gelu_erf(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(oracle.gelu_erf(z) - oracle.gelu_erf(-z), z, atol=1e-14)
+    # Phi(1) and Phi(-1) of the standard normal distribution
+    np.testing.assert_allclose(oracle.gelu_erf(np.array([1.0, -1.0, 2.0])),
+                               [0.8413447460685429, -0.15865525393145707, 2 * 0.9772498680518208],
+                               rtol=1e-15)
+    from scipy.special import erfc
+    np.testing.assert_allclose(oracle.gelu_erf(z), 0.5 * z * erfc(-z / math.sqrt(2)), atol=1e-15)
+
+
+def test_linear_loops():
+    r = _rng(9)
+    a, w, b = r.standard_normal((3, 5)), r.standard_normal((4, 5)), r.standard_normal(4)
+    ref = [[sum(a[i, k] * w[n, k] for k in range(5)) + b[n] for n in range(4)] for i in range(3)]
+    np.testing.assert_allclose(oracle.linear(a, w, b), ref, atol=1e-14)
+
+
+# ---------------------------------------------------------------- block and stack
+
+
+@pytest.mark.parametrize("t,d,heads,f,batch", [(150, 128, 2, 512, 1), (70, 192, 3, 256, 2)])
+def test_block_matches_hf_whisper_encoder_layer(t, d, heads, f, batch):
+    p = _rand_layer(t + d, d, f)
+    x = _rng(t).standard_normal((batch, t, d)) * 2
+    got = oracle.encoder_block(x, p, heads)
+    np.testing.assert_allclose(got, _hf_block(p, x, heads), atol=1e-11, rtol=0)
+
+
+def test_block_with_synth_layer_matches_hf():
+    cfg = synth.CONFIGS["tiny_block"].with_(t=200)
+    w = synth.make_workload(cfg)
+    got = oracle.encoder_block(w.x, w.layers[0], cfg.heads)
+    np.testing.assert_allclose(got, _hf_block(w.layers[0], w.x, cfg.heads), atol=1e-11)
+
+
+def test_block_zero_weights_closed_form():
+    d, f = 64, 128
+    p = _rand_layer(1, d, f)
+    for n in ("wq", "wk", "wv", "wo", "w1", "w2"):
+        p[n] = np.zeros_like(p[n])
+    x = _rng(2).standard_normal((33, d))
+    np.testing.assert_allclose(oracle.encoder_block(x, p, 1), x + p["bo"] + p["b2"], atol=1e-14)
+
+
+def test_block_zero_qk_gives_mean_of_values():
+    d, f, t = 128, 256, 97
+    p = _rand_layer(3, d, f)
+    p["wq"][:] = 0
+    p["wk"][:] = 0
+    p["bq"][:] = 0
+    x = _rng(3).standard_normal((t, d))
+    a = oracle.layer_norm(x, p["ln1_g"], p["ln1_b"])
+    v = oracle.linear(a, p["wv"], p["bv"])
+    o = np.tile(v.mean(axis=0), (t, 1))
+    x1 = x + oracle.linear(o, p["wo"], p["bo"])
+    a2 = oracle.layer_norm(x1, p["ln2_g"], p["ln2_b"])
+    ref = x1 + oracle.linear(oracle.gelu_erf(oracle.linear(a2, p["w1"], p["b1"])), p["w2"], p["b2"])
+    np.testing.assert_allclose(oracle.encoder_block(x, p, 2), ref, atol=1e-12)
+
+
+def test_block_row_permutation_and_window_independence():
+    d, f, t = 128, 256, 90
+    p = _rand_layer(4, d, f)
+    r = _rng(4)
+    x = r.standard_normal((3, t, d))
+    y = oracle.encoder_block(x, p, 2)
+    perm = r.permutation(t)
+    np.testing.assert_allclose(oracle.encoder_block(x[:, perm], p, 2), y[:, perm], atol=1e-12)
+    x2 = x.copy()
+    x2[1] = r.standard_normal((t, d))
+    y2 = oracle.encoder_block(x2, p, 2)
+    np.testing.assert_array_equal(y2[0], y[0])
+    np.testing.assert_array_equal(y2[2], y[2])
+    wperm = [2, 0, 1]
+    np.testing.assert_allclose(oracle.encoder_block(x[wperm], p, 2), y[wperm], atol=1e-13)
+
+
+def test_block_rows_matches_block():
+    cfg = synth.CONFIGS["tiny_block"].with_(t=260)
+    w = synth.make_workload(cfg)
+    full = oracle.encoder_block(w.x[0], w.layers[0], cfg.heads)
+    rows = [0, 1, 127, 128, 259]
+    np.testing.assert_allclose(oracle.encoder_block_rows(w.x[0], w.layers[0], cfg.heads, rows),
+                               full[rows], atol=1e-13)
+
+
+def test_stack_matches_hf_layers_and_final_norm():
+    d, f, t, heads = 128, 256, 64, 2
+    layers = [_rand_layer(10 + i, d, f) for i in range(3)]
+    g, b = 1 + _rng(5).standard_normal(d) * 0.1, _rng(6).standard_normal(d) * 0.1
+    x = _rng(7).standard_normal((t, d))
+    got = oracle.encoder_stack(x, layers, heads, ln_post=(g, b))
+    h = x
+    for p in layers:
+        h = _hf_block(p, h, heads)
+    ref = torch.nn.functional.layer_norm(torch.tensor(h), (d,), torch.tensor(g), torch.tensor(b),
+                                         eps=1e-5).numpy()
+    np.testing.assert_allclose(got, ref, atol=1e-11)
+    # no final norm: the last block's output is the stack output
+    np.testing.assert_allclose(oracle.encoder_stack(x, layers, heads), h, atol=1e-11)
+
+
+# ---------------------------------------------------------------- metrics
+
+
+def test_error_metrics():
+    ref = np.array([1.0, -2.0, 0.0, 4.0])
+    got = ref + np.array([0.01, 0.0, 0.05, -0.04])
+    rms = math.sqrt(np.mean(ref ** 2))
+    assert orc.max_rel_error(got, ref) == pytest.approx(max(0.01 / rms, 0.05 / rms, 0.04 / 4.0))
+    assert orc.mean_abs_error(got, ref) == pytest.approx(0.025)
+
+
+# ---------------------------------------------------------------- mutations: the pins bite
+
+
+def _hf_check(monkeypatch_fn=None):
+    p = _rand_layer(99, 128, 256)
+    x = _rng(99).standard_normal((140, 128))
+    return np.abs(oracle.encoder_block(x, p, 2) - _hf_block(p, x, 2)).max()
+
+
+@pytest.mark.parametrize("mutation", ["transposed_weight", "no_corr", "scale_sqrt_d", "ln_unbiased",
+                                      "gelu_tanh", "no_bias_v", "drop_residual"])
+def test_planted_mistakes_are_caught(monkeypatch, mutation):
+    if mutation == "transposed_weight":
+        monkeypatch.setattr(orc, "linear", lambda a, w, b=None: orc._f64(a) @ orc._f64(w)
+                            + (0 if b is None else orc._f64(b)) if w.shape[0] == w.shape[1]
+                            else orc._f64(a) @ orc._f64(w).T + (0 if b is None else orc._f64(b)))
+    elif mutation == "no_corr":
+        real = np.exp
+
+        def bad_online(q, k, v, heads, tile=orc.KEY_TILE, return_probs=False):
+            q, k, v = orc._f64(q), orc._f64(k), orc._f64(v)
+            qh, kh, vh = orc._heads(q, heads), orc._heads(k, heads), orc._heads(v, heads)
+            out = np.empty_like(qh)
+            for h in range(heads):
+                m = np.full(q.shape[0], -np.inf)
+                den = np.zeros(q.shape[0])
+                acc = np.zeros((q.shape[0], qh.shape[-1]))
+                for j0 in range(0, k.shape[0], tile):
+                    s = qh[h] @ kh[h, j0:j0 + tile].T * qh.shape[-1] ** -0.5
+                    m = np.maximum(m, s.max(axis=1))
+                    pr = real(s - m[:, None])
+                    den = den + pr.sum(axis=1)          # corr dropped
+                    acc = acc + pr @ vh[h, j0:j0 + tile]
+                out[h] = acc / den[:, None]
+            return orc._merge_heads(out)
+        monkeypatch.setattr(orc, "attention_online", bad_online)
+    elif mutation == "scale_sqrt_d":
+        real = orc.attention_online
+        monkeypatch.setattr(orc, "attention_online",
+                            lambda q, k, v, heads, **kw: real(q * 0.5, k, v, heads, **kw))
+    elif mutation == "ln_unbiased":
+        def ln(x, g, b, eps=orc.LN_EPS):
+            x = orc._f64(x)
+            mu = x.mean(-1, keepdims=True)
+            var = ((x - mu) ** 2).sum(-1, keepdims=True) / (x.shape[-1] - 1)
+            return (x - mu) / np.sqrt(var + eps) * g + b
+        monkeypatch.setattr(orc, "layer_norm", ln)
+    elif mutation == "gelu_tanh":
+        monkeypatch.setattr(orc, "gelu_erf", lambda z: 0.5 * z * (1 + np.tanh(
+            math.sqrt(2 / math.pi) * (z + 0.044715 * z ** 3))))
+    elif mutation == "no_bias_v":
+        real_lin = orc.linear
+        calls = {"n": 0}
+
+        def lin(a, w, b=None):
+            calls["n"] += 1
+            return real_lin(a, w, None if calls["n"] == 3 else b)
+        monkeypatch.setattr(orc, "linear", lin)
+    elif mutation == "drop_residual":
+        real_block = orc._window_block
+
+        def blk(x, p, heads):
+            return real_block(x, p, heads) - x
+        monkeypatch.setattr(orc, "_window_block", blk)
+    assert _hf_check() > 1e-6

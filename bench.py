@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Throughput of the Whisper-style encoder block forward on one MI355X.
+
+A step is one call of the C ABI over the whole workload (every step of the block: LN1, QKV
+projection, attention, out-projection + residual, LN2, fc1 + GELU, fc2 + residual; for a stack
+every block and the final LayerNorm).  The default workload is the batched large-v3 block:
+16 windows x 1500 positions, d_model 1280, 20 heads, ffn 5120, bf16-valued weights, 5 % of the
+input rows scaled by 20.  Inputs are seeded synthetic data resident in HBM before timing starts.
+
+Prints ONE JSON line: frames/s (frames = encoder positions), the per-kernel breakdown timed with
+HIP events on the launch stream, the roofline entry of the dominant kernel, and the CPU oracle
+timed on a bounded sample of the same workload on the host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "encoder frames/sec per 1500-frame window + attention/GEMM TFLOP/s (% MFMA peak)"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
+PEAK_HBM_GBS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CSRC = os.path.join(ROOT, "speech_transformer_encoder_amd", "csrc")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="large_v3_batch16_block")
+    ap.add_argument("--path", default="bf16", choices=["bf16", "fp16", "fp32"])
+    ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-windows", type=int, default=3)
+    ap.add_argument("--cpu-sample-layers", type=int, default=2)
+    return ap.parse_args()
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in sorted(files):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def time_events(fn, reps, stream):
+    """Average duration of fn() over reps launches, from HIP events on `stream`."""
+    import torch
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    s.record(stream)
+    for _ in range(reps):
+        fn()
+    e.record(stream)
+    e.synchronize()
+    return s.elapsed_time(e) / reps  # ms
+
+
+def kernel_breakdown(cfg, path_name, reps):
+    """Each kernel of one block at the workload's shapes, timed alone on the current stream."""
+    import torch
+    from speech_transformer_encoder_amd import binding as B
+    path = B.PATHS[path_name]
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[path_name]
+    es = 4 if path_name == "fp32" else 2
+    M, d, f, H = cfg.batch * cfg.t, cfg.d_model, cfg.ffn_dim, cfg.heads
+    dev = "cuda"
+    g = torch.Generator(device=dev).manual_seed(0)
+    rnd = lambda *s: torch.randn(*s, device=dev, generator=g)  # noqa: E731
+    x = rnd(M, d)
+    y = x.clone()
+    a = torch.empty(M, d, device=dev, dtype=dt)
+    o = rnd(M, d).to(dt)
+    qkv = rnd(M, 3 * d).to(dt) * 0.5
+    h = rnd(M, f).to(dt)
+    hid = torch.empty(M, f, device=dev, dtype=dt)
+    qkv_out = torch.empty(M, 3 * d, device=dev, dtype=dt)
+    wqkv, wo = (rnd(3 * d, d) * 0.02).to(dt), (rnd(d, d) * 0.02).to(dt)
+    w1, w2 = (rnd(f, d) * 0.02).to(dt), (rnd(d, f) * 0.02).to(dt)
+    ones, zeros = torch.ones(d, device=dev), torch.zeros(d, device=dev)
+    b3, bf = torch.zeros(3 * d, device=dev), torch.zeros(f, device=dev)
+    ln_dt = {"bf16": B.WENC_DTYPE_BF16, "fp16": B.WENC_DTYPE_F16, "fp32": B.WENC_DTYPE_F32}[path_name]
+    st = torch.cuda.current_stream()
+    qp = qkv.data_ptr()
+    kernels = {
+        "ln": (lambda: B.whisper_enc_layernorm(x, ones, zeros, a, M, d, ln_dt),
+               "hbm", M * d * (4 + es) + 2 * d * 4),
+        "gemm_qkv": (lambda: B.whisper_enc_linear(a, wqkv, b3, None, qkv_out, M, 3 * d, d, path,
+                                                  B.WENC_EPI_BIAS), "mfma", 2.0 * M * 3 * d * d),
+        "attention": (lambda: B.whisper_enc_attention(qp, qp + d * es, qp + 2 * d * es, o,
+                                                      cfg.batch, cfg.t, H, 3 * d, d, path),
+                      "mfma", 4.0 * cfg.batch * cfg.t * cfg.t * d),
+        "gemm_out_residual": (lambda: B.whisper_enc_linear(o, wo, zeros, y, y, M, d, d, path,
+                                                           B.WENC_EPI_BIAS_RESIDUAL), "mfma",
+                              2.0 * M * d * d),
+        "gemm_fc1_gelu": (lambda: B.whisper_enc_linear(a, w1, bf, None, hid, M, f, d, path,
+                                                       B.WENC_EPI_BIAS_GELU), "mfma", 2.0 * M * f * d),
+        "gemm_fc2_residual": (lambda: B.whisper_enc_linear(h, w2, zeros, y, y, M, d, f, path,
+                                                           B.WENC_EPI_BIAS_RESIDUAL), "mfma",
+                              2.0 * M * d * f),
+    }
+    per_block = {"ln": 2}  # LN1 and LN2
+    out = {}
+    for name, (fn, bound, work) in kernels.items():
+        ms = time_events(fn, reps, st)
+        if bound == "hbm":
+            ach = work / (ms * 1e-3) / 1e9
+            peak = PEAK_HBM_GBS
+            unit = "GB/s"
+        else:
+            ach = work / (ms * 1e-3) / 1e12
+            peak = PEAK_TFLOPS[path_name]
+            unit = "TFLOP/s"
+        out[name] = {"ms": round(ms, 5), "bound": bound, "achieved": round(ach, 2), "unit": unit,
+                     "peak": peak, "frac": round(ach / peak, 4), "work": work,
+                     "launches_per_block": per_block.get(name, 1)}
+    return out
+
+
+def cpu_baseline(cfg, windows, layers):
+    """The oracle as it stands, on a bounded sample of the workload (first windows / layers)."""
+    import numpy as np
+    import oracle
+    from speech_transformer_encoder_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    nw = min(windows, cfg.batch)
+    nl = min(layers, cfg.n_layers)
+    sub = cfg.with_(batch=nw, n_layers=nl)
+    w = synth.make_workload(sub)
+    t0 = time.perf_counter()
+    y = oracle.encoder_stack(w.x, w.layers, cfg.heads, w.ln_post if nl == cfg.n_layers else None)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(y).all()
+    # frames/s of the full workload: the sample did nw/batch of the windows and nl/n_layers of
+    # the blocks, so the full call would take dt * (batch/nw) * (n_layers/nl).
+    full_s = dt * (cfg.batch / nw) * (cfg.n_layers / nl)
+    return {"value": round(cfg.batch * cfg.t / full_s, 2), "unit": "frames/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{nw} of {cfg.batch} windows x {nl} of {cfg.n_layers} blocks "
+                      f"({dt:.1f} s float64 numpy, scaled to the full workload)"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(windows shard by data parallelism with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np  # noqa: F401
+    import torch
+    from speech_transformer_encoder_amd import binding as B
+    from speech_transformer_encoder_amd import synth
+    from speech_transformer_encoder_amd.encoder import build_from_workload, to_device_input
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.load()
+    cfg = synth.CONFIGS[args.config]
+    path = B.PATHS[args.path]
+    w = synth.make_workload(cfg)
+    enc = build_from_workload(w, path)
+    x = to_device_input(w.x)
+    y = torch.empty_like(x)
+    enc.workspace(cfg.batch, cfg.t)
+    for _ in range(args.warmup):
+        enc.forward(x, y)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    s.record(st)
+    for _ in range(args.steps):
+        enc.forward(x, y)
+    e.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = s.elapsed_time(e) / args.steps
+    frames = cfg.batch * cfg.t
+    flops = cfg.flops()
+
+    kern = kernel_breakdown(cfg, args.path, args.kernel_reps)
+    # Kernel time per step: every kernel runs once per block (LN twice), n_layers blocks.
+    for k in kern.values():
+        k["ms_per_step"] = round(k["ms"] * k["launches_per_block"] * cfg.n_layers, 4)
+    dom_name = max(kern, key=lambda n: kern[n]["ms_per_step"])
+    dom = kern[dom_name]
+    traffic = None
+    if os.path.exists(COUNTERS):
+        with open(COUNTERS) as fh:
+            c = json.load(fh)
+        ent = c.get("kernels", {}).get(dom_name)
+        if ent and ent.get("source_hash") == source_hash(ent.get("sources", [])) \
+                and ent.get("config") == args.config and ent.get("path") == args.path:
+            traffic = ent.get("bytes_per_launch")
+    roof = {"kernel": dom_name, "bound": dom["bound"], "achieved": dom["achieved"],
+            "peak": dom["peak"], "unit": dom["unit"], "frac": dom["frac"], "traffic": traffic,
+            "work_per_launch": dom["work"], "ms_per_launch": dom["ms"]}
+
+    gemm_ms = sum(v["ms_per_step"] for n, v in kern.items() if n.startswith("gemm"))
+    attn_ms = kern["attention"]["ms_per_step"]
+    gemm_tf = flops["gemm"] / (gemm_ms * 1e-3) / 1e12
+    attn_tf = flops["attention"] / (attn_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[args.path]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, args.cpu_sample_windows, args.cpu_sample_layers)
+
+    out = {
+        "metric": METRIC, "value": round(frames / (ms * 1e-3), 1), "unit": "frames/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.path,
+        "data": "synthetic (seeded N(0,1) inputs, N(0,0.02^2) weights; no checkpoint)",
+        "config": {"workload": cfg.name, "batch_windows": cfg.batch, "t": cfg.t,
+                   "d_model": cfg.d_model, "heads": cfg.heads, "ffn_dim": cfg.ffn_dim,
+                   "n_layers": cfg.n_layers, "final_layernorm": cfg.ln_post,
+                   "weights": "bf16-valued" if cfg.bf16_weights else "fp32",
+                   "operands": args.path, "parallelism": "single GPU"},
+        "tflops": {"total": round(flops["total"] / (ms * 1e-3) / 1e12, 1),
+                   "gemm": round(gemm_tf, 1), "gemm_frac_peak": round(gemm_tf / peak, 4),
+                   "attention": round(attn_tf, 1), "attention_frac_peak": round(attn_tf / peak, 4),
+                   "peak": peak},
+        "roofline": roof,
+        "kernels": kern,
+        "wall_s_timed": round(wall, 4),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

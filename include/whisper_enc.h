@@ -1,0 +1,169 @@
+/*
+ * whisper_enc.h - C ABI of the MI355X (gfx950) Whisper-style encoder block library.
+ *
+ * The library computes the forward pass of the pre-LayerNorm transformer block of the Whisper
+ * audio encoder over 30 s windows (t = 1500 positions), for one block or a stack of blocks
+ * ending in an optional final LayerNorm:
+ *
+ *   a  = LN1(x)                               LayerNorm, eps 1e-5, biased variance
+ *   q  = a Wq^T + bq,  k = a Wk^T,  v = a Wv^T + bv          (K has no bias)
+ *   o  = softmax(q_h k_h^T / sqrt(64)) v_h  per head h, bidirectional, per window
+ *   x1 = x + o Wo^T + bo
+ *   y  = x1 + gelu(LN2(x1) W1^T + b1) W2^T + b2              gelu(z) = z/2 (1 + erf(z/sqrt 2))
+ *
+ * Sources: inferencelayer 0.2.4 "whisper_gpu.rs" (VANILLA_ATTN and LN_SRC shaders,
+ * WhisperEncoderGpu::forward), turbospark-runtime 0.3.0 "src/whisper/metal.rs" (module doc,
+ * EncLayerGpu, encode_layer, encode_partial), oxinfer "src/whisper/model.rs" (WhisperConfig,
+ * Precision, WhisperModel::encode).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers (memory of the current HIP device) unless marked "host".
+ *     The caller owns every buffer; the library never allocates, frees or synchronises, keeps
+ *     no mutable global state, and enqueues all work on `stream` (a hipStream_t; NULL = the
+ *     default stream).  Results are ready when the stream's work completes.
+ *   - Matrices are row-major.  Activations x, y are [batch, t, d_model] fp32; weights are in
+ *     PyTorch layout [n_out, n_in].
+ *   - Every argument is validated before anything is enqueued; a call that returns an error
+ *     has enqueued nothing.  A launch failure reported by HIP returns WENC_ERR_HIP; faults
+ *     inside kernels surface at the caller's next synchronisation.
+ *   - Calls with zero rows (batch * t == 0) enqueue nothing and return WENC_OK; their data
+ *     pointers may then be NULL.
+ *   - Calls on one stream run in order; concurrent calls on different streams need separate
+ *     workspaces and outputs.
+ */
+#ifndef WHISPER_ENC_H
+#define WHISPER_ENC_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define WENC_OK 0
+#define WENC_ERR_ARG 1         /* NULL pointer, misaligned pointer, bad size or enum value   */
+#define WENC_ERR_UNSUPPORTED 2 /* valid model shape the kernels do not implement (hd != 64) */
+#define WENC_ERR_WORKSPACE 3   /* workspace_bytes below whisper_enc_workspace_bytes()       */
+#define WENC_ERR_HIP 4         /* HIP reported an error for a launch                         */
+
+/* Arithmetic paths: the type of every matrix-multiply operand.  Accumulation, LayerNorm
+ * statistics, softmax state and the residual stream are fp32 on every path.
+ *   BF16 - bfloat16 MFMA operands (weights rounded to nearest even when packed);
+ *   FP32 - fp32 operands and intermediates (fp32 MFMA), the fallback path;
+ *   FP16 - IEEE half MFMA operands, same MFMA rate as BF16 with 3 more mantissa bits. */
+#define WENC_PATH_BF16 0
+#define WENC_PATH_FP32 1
+#define WENC_PATH_FP16 2
+
+/* Element types of step-level outputs. */
+#define WENC_DTYPE_F32 0
+#define WENC_DTYPE_BF16 1
+#define WENC_DTYPE_F16 2
+
+/* Projection epilogues (whisper_enc_linear). */
+#define WENC_EPI_BIAS 0          /* c = a w^T + bias                        (path dtype) */
+#define WENC_EPI_BIAS_GELU 1     /* c = gelu_erf(a w^T + bias)              (path dtype) */
+#define WENC_EPI_BIAS_RESIDUAL 2 /* c = residual + a w^T + bias              (fp32)      */
+
+/* Limits checked by every entry point. */
+#define WENC_HEAD_DIM 64
+#define WENC_MAX_D_MODEL 4096
+#define WENC_MAX_FFN_DIM 65536
+#define WENC_MAX_ROWS (1 << 24)
+
+/* Human-readable text of a status code (static storage; never NULL). */
+const char* whisper_enc_strerror(int code);
+
+/*
+ * Size in bytes of one packed layer blob (256-byte aligned sections), 0 if the arguments are
+ * invalid.  The blob holds LN1/LN2 gamma and beta, the QKV bias with a zero K slot, the out,
+ * fc1 and fc2 biases (all fp32), and Wqkv [3d, d] (Q, K, V row blocks), Wo [d, d],
+ * W1 [ffn, d], W2 [d, ffn] in the path's operand type (oxinfer Precision: norms and biases
+ * always stay f32; turbospark-runtime DecLayerGpu: packed [3d, d] QKV with a zero K bias).
+ * The blob is opaque: only whisper_enc_pack_layer writes it.
+ */
+size_t whisper_enc_layer_bytes(int d_model, int ffn_dim, int path);
+
+/*
+ * Pack one block's parameters into `dst_layer` (device, layer_bytes(), 256-byte aligned).
+ * Sources are device fp32 arrays in PyTorch layout: ln*_g/ln*_b [d]; wq, wk, wv, wo [d, d];
+ * w1 [ffn, d]; w2 [d, ffn]; bq, bv, bo, b2 [d]; b1 [ffn].  `bk` may be NULL (Whisper's K
+ * projection has no bias), which packs zeros.  Matrices are rounded to the path's operand type
+ * (round to nearest even), fp32 on WENC_PATH_FP32.  Runs asynchronously on `stream`; the sources
+ * must stay valid until it completes.
+ */
+int whisper_enc_pack_layer(const float* ln1_g, const float* ln1_b, const float* wq,
+                           const float* bq, const float* wk, const float* bk, const float* wv,
+                           const float* bv, const float* wo, const float* bo,
+                           const float* ln2_g, const float* ln2_b, const float* w1,
+                           const float* b1, const float* w2, const float* b2, int d_model,
+                           int ffn_dim, int path, void* dst_layer, void* stream);
+
+/*
+ * Workspace bytes a block/stack call needs for `batch` windows of `t` positions: the LN
+ * output / attention output [batch*t, d] and the QKV / FFN hidden activations
+ * [batch*t, max(3d, ffn)], in the path's operand type.  0 if the arguments are invalid.
+ */
+size_t whisper_enc_workspace_bytes(int batch, int t, int d_model, int heads, int ffn_dim,
+                                   int path);
+
+/*
+ * One pre-LN encoder block (inferencelayer WhisperEncoderGpu::forward, block loop;
+ * turbospark-runtime encode_layer; oxinfer WhisperModel::encode, layer loop):
+ *   y = x1 + FFN(LN2(x1)),  x1 = x + Attn(LN1(x)).
+ * x, y: [batch, t, d_model] fp32, 16-byte aligned; y == x (in place) is allowed, partial
+ * overlap is not.  layer: a blob from whisper_enc_pack_layer with the same d_model, ffn_dim and
+ * path.  heads must give head_dim d_model/heads == 64 (else WENC_ERR_UNSUPPORTED).  Attention
+ * never crosses windows.  workspace: device, 256-byte aligned, >= workspace_bytes().
+ */
+int whisper_enc_block_forward(const float* x, float* y, const void* layer, int batch, int t,
+                              int d_model, int heads, int ffn_dim, int path, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * n_layers blocks in order, then the final LayerNorm y = LN(y; ln_post_g, ln_post_b) when
+ * ln_post_g is non-NULL (inferencelayer forward, ln_post, optional: "absent when the host
+ * model replaced it with Identity"; oxinfer encode, enc_ln).  layers: n_layers blobs packed
+ * back to back, blob i at (char*)layers + i * whisper_enc_layer_bytes(...).  n_layers >= 0
+ * (0 applies only the final LayerNorm, or copies x to y).  ln_post_b must be non-NULL when
+ * ln_post_g is.  Other arguments as for whisper_enc_block_forward.
+ */
+int whisper_enc_stack_forward(const float* x, float* y, const void* layers, int n_layers,
+                              const float* ln_post_g, const float* ln_post_b, int batch, int t,
+                              int d_model, int heads, int ffn_dim, int path, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* ---- Step-level entry points: one step of the block each, for tests and profiling. ---- */
+
+/*
+ * y[rows, d] = (x - mean) / sqrt(var + 1e-5) * gamma + beta per row, two-pass biased variance
+ * (inferencelayer LN_SRC).  x fp32; y in out_dtype (WENC_DTYPE_*); d % 64 == 0, 64 <= d <= 4096.
+ * y == x is allowed only for WENC_DTYPE_F32.
+ */
+int whisper_enc_layernorm(const float* x, const float* gamma, const float* beta, void* y,
+                          int rows, int d, int out_dtype, void* stream);
+
+/*
+ * One projection c = epilogue(a w^T + bias): a [m, k] and w [n, k] in the path's operand type
+ * (fp32 on WENC_PATH_FP32), bias [n] fp32.  WENC_EPI_BIAS / WENC_EPI_BIAS_GELU write c [m, n]
+ * in the operand type; WENC_EPI_BIAS_RESIDUAL writes fp32 c = residual + a w^T + bias with
+ * residual [m, n] fp32 (c == residual allowed).  n % 64 == 0, k % 64 == 0.
+ */
+int whisper_enc_linear(const void* a, const void* w, const float* bias, const float* residual,
+                       void* c, int m, int n, int k, int path, int epilogue, void* stream);
+
+/*
+ * Bidirectional attention with head_dim 64 for `batch` windows of t rows (inferencelayer
+ * VANILLA_ATTN): row i of window b is at ptr + (b*t + i) * ld; head h occupies columns
+ * 64h .. 64h+63.  q, k, v use row stride ld_qkv, o uses ld_o (elements, multiples of 8, at least
+ * 64*heads); all in the path's operand type.  o = softmax(q k^T / 8) v per (window, head).
+ */
+int whisper_enc_attention(const void* q, const void* k, const void* v, void* o, int batch, int t,
+                          int heads, int ld_qkv, int ld_o, int path, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WHISPER_ENC_H */

@@ -1,0 +1,162 @@
+"""ctypes binding of ``libwhisper_enc.so``: the C ABI of ``include/whisper_enc.h`` under the same
+names, with argument marshalling only (every step of the forward pass runs in the HIP kernels).
+
+Pointer arguments accept a ``torch.Tensor`` (its ``data_ptr()``), a plain integer address or
+``None``.  ``stream`` defaults to PyTorch's current stream on the current device.  A non-zero
+status raises :class:`WencError`.
+
+The library is loaded after ``import torch`` so that it binds to the HIP runtime PyTorch has
+already loaded (both carry the soname ``libamdhip64.so.7``); a stream handle from PyTorch is then
+valid inside the library.  There is no fallback: if the library is missing, loading raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libwhisper_enc.so")
+
+WENC_OK = 0
+WENC_ERR_ARG = 1
+WENC_ERR_UNSUPPORTED = 2
+WENC_ERR_WORKSPACE = 3
+WENC_ERR_HIP = 4
+
+WENC_PATH_BF16 = 0
+WENC_PATH_FP32 = 1
+WENC_PATH_FP16 = 2
+PATHS = {"bf16": WENC_PATH_BF16, "fp32": WENC_PATH_FP32, "fp16": WENC_PATH_FP16}
+
+WENC_DTYPE_F32 = 0
+WENC_DTYPE_BF16 = 1
+WENC_DTYPE_F16 = 2
+
+WENC_EPI_BIAS = 0
+WENC_EPI_BIAS_GELU = 1
+WENC_EPI_BIAS_RESIDUAL = 2
+
+HEAD_DIM = 64
+
+EXPORTS = (
+    "whisper_enc_strerror", "whisper_enc_layer_bytes", "whisper_enc_pack_layer",
+    "whisper_enc_workspace_bytes", "whisper_enc_block_forward", "whisper_enc_stack_forward",
+    "whisper_enc_layernorm", "whisper_enc_linear", "whisper_enc_attention",
+)
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+class WencError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: status {code} ({strerror(code)})")
+
+
+def load() -> ctypes.CDLL:
+    """Load the library once (after torch's HIP runtime); raise if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    import torch  # noqa: F401  (binds the process to torch's libamdhip64 first)
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m speech_transformer_encoder_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "whisper_enc_strerror": (ctypes.c_char_p, [I]),
+        "whisper_enc_layer_bytes": (Z, [I, I, I]),
+        "whisper_enc_pack_layer": (I, [P] * 16 + [I, I, I, P, P]),
+        "whisper_enc_workspace_bytes": (Z, [I, I, I, I, I, I]),
+        "whisper_enc_block_forward": (I, [P, P, P, I, I, I, I, I, I, P, Z, P]),
+        "whisper_enc_stack_forward": (I, [P, P, P, I, P, P, I, I, I, I, I, I, P, Z, P]),
+        "whisper_enc_layernorm": (I, [P, P, P, P, I, I, I, P]),
+        "whisper_enc_linear": (I, [P, P, P, P, P, I, I, I, I, I, P]),
+        "whisper_enc_attention": (I, [P, P, P, P, I, I, I, I, I, I, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(code: int, where: str) -> None:
+    if code != WENC_OK:
+        raise WencError(code, where)
+
+
+def strerror(code: int) -> str:
+    return load().whisper_enc_strerror(code).decode()
+
+
+def whisper_enc_layer_bytes(d_model: int, ffn_dim: int, path: int) -> int:
+    return load().whisper_enc_layer_bytes(d_model, ffn_dim, path)
+
+
+def whisper_enc_workspace_bytes(batch: int, t: int, d_model: int, heads: int, ffn_dim: int,
+                                path: int) -> int:
+    return load().whisper_enc_workspace_bytes(batch, t, d_model, heads, ffn_dim, path)
+
+
+def whisper_enc_pack_layer(ln1_g, ln1_b, wq, bq, wk, bk, wv, bv, wo, bo, ln2_g, ln2_b, w1, b1,
+                           w2, b2, d_model, ffn_dim, path, dst_layer, stream=None) -> None:
+    ptrs = [_ptr(a) for a in (ln1_g, ln1_b, wq, bq, wk, bk, wv, bv, wo, bo, ln2_g, ln2_b, w1, b1,
+                              w2, b2)]
+    _check(load().whisper_enc_pack_layer(*ptrs, d_model, ffn_dim, path, _ptr(dst_layer),
+                                         _stream(stream)), "whisper_enc_pack_layer")
+
+
+def whisper_enc_block_forward(x, y, layer, batch, t, d_model, heads, ffn_dim, path, workspace,
+                              workspace_bytes, stream=None) -> None:
+    _check(load().whisper_enc_block_forward(_ptr(x), _ptr(y), _ptr(layer), batch, t, d_model,
+                                            heads, ffn_dim, path, _ptr(workspace),
+                                            workspace_bytes, _stream(stream)),
+           "whisper_enc_block_forward")
+
+
+def whisper_enc_stack_forward(x, y, layers, n_layers, ln_post_g, ln_post_b, batch, t, d_model,
+                              heads, ffn_dim, path, workspace, workspace_bytes,
+                              stream=None) -> None:
+    _check(load().whisper_enc_stack_forward(_ptr(x), _ptr(y), _ptr(layers), n_layers,
+                                            _ptr(ln_post_g), _ptr(ln_post_b), batch, t, d_model,
+                                            heads, ffn_dim, path, _ptr(workspace),
+                                            workspace_bytes, _stream(stream)),
+           "whisper_enc_stack_forward")
+
+
+def whisper_enc_layernorm(x, gamma, beta, y, rows, d, out_dtype, stream=None) -> None:
+    _check(load().whisper_enc_layernorm(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), rows, d,
+                                        out_dtype, _stream(stream)), "whisper_enc_layernorm")
+
+
+def whisper_enc_linear(a, w, bias, residual, c, m, n, k, path, epilogue, stream=None) -> None:
+    _check(load().whisper_enc_linear(_ptr(a), _ptr(w), _ptr(bias), _ptr(residual), _ptr(c), m, n,
+                                     k, path, epilogue, _stream(stream)), "whisper_enc_linear")
+
+
+def whisper_enc_attention(q, k, v, o, batch, t, heads, ld_qkv, ld_o, path, stream=None) -> None:
+    _check(load().whisper_enc_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(o), batch, t, heads,
+                                        ld_qkv, ld_o, path, _stream(stream)),
+           "whisper_enc_attention")

@@ -1,0 +1,310 @@
+// C ABI of the encoder-block library: argument validation, packed-layer and workspace layout,
+// and the launch sequence of one block (inferencelayer whisper_gpu.rs,
+// WhisperEncoderGpu::forward: LN, QKV, attention, out + add, LN, fc1 + GELU, fc2 + add, and
+// the optional ln_post).  Everything is checked before the first launch so that a rejected
+// call enqueues nothing and never touches HIP.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/whisper_enc.h"
+#include "wenc_internal.h"
+
+using namespace wenc;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int path_dtype(int path) {
+  switch (path) {
+    case WENC_PATH_BF16: return DT_BF16;
+    case WENC_PATH_FP16: return DT_F16;
+    case WENC_PATH_FP32: return DT_F32;
+  }
+  return -1;
+}
+
+size_t elem_bytes(int path) { return path == WENC_PATH_FP32 ? 4 : 2; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct LayerLayout {
+  size_t ln1_g, ln1_b, bqkv, bo, ln2_g, ln2_b, b1, b2;  // fp32 sections
+  size_t wqkv, wo, w1, w2;                              // operand-type sections
+  size_t total;
+};
+
+LayerLayout layer_layout(int d, int f, int path) {
+  LayerLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += round_up(bytes);
+    return o;
+  };
+  const size_t es = elem_bytes(path);
+  L.ln1_g = take(4 * (size_t)d);
+  L.ln1_b = take(4 * (size_t)d);
+  L.bqkv = take(4 * 3 * (size_t)d);
+  L.bo = take(4 * (size_t)d);
+  L.ln2_g = take(4 * (size_t)d);
+  L.ln2_b = take(4 * (size_t)d);
+  L.b1 = take(4 * (size_t)f);
+  L.b2 = take(4 * (size_t)d);
+  L.wqkv = take(es * 3 * (size_t)d * d);
+  L.wo = take(es * (size_t)d * d);
+  L.w1 = take(es * (size_t)f * d);
+  L.w2 = take(es * (size_t)d * f);
+  L.total = off;
+  return L;
+}
+
+bool valid_dims(int d, int f) {
+  return d >= 64 && d <= WENC_MAX_D_MODEL && d % 64 == 0 && f >= 64 && f <= WENC_MAX_FFN_DIM &&
+         f % 64 == 0;
+}
+
+// Shape check shared by workspace/block/stack: returns WENC_OK, ARG or UNSUPPORTED.
+int check_shape(int batch, int t, int d, int heads, int f, int path) {
+  if (path_dtype(path) < 0) return WENC_ERR_ARG;
+  if (batch < 0 || t < 0 || heads <= 0) return WENC_ERR_ARG;
+  if ((long long)batch * t > WENC_MAX_ROWS) return WENC_ERR_ARG;
+  if (!valid_dims(d, f)) return WENC_ERR_ARG;
+  if (d % heads != 0) return WENC_ERR_ARG;
+  if (d / heads != WENC_HEAD_DIM) return WENC_ERR_UNSUPPORTED;
+  return WENC_OK;
+}
+
+struct Workspace {
+  void* a;  // [M, d]: LN outputs and the attention output
+  void* b;  // [M, max(3d, f)]: QKV, then the FFN hidden activations
+};
+
+size_t workspace_size(size_t rows, int d, int f, int path) {
+  const size_t es = elem_bytes(path);
+  const size_t wb = (size_t)(3 * d > f ? 3 * d : f);
+  return round_up(rows * d * es) + round_up(rows * wb * es);
+}
+
+Workspace carve(void* ws, size_t rows, int d, int path) {
+  Workspace w;
+  w.a = ws;
+  w.b = static_cast<char*>(ws) + round_up(rows * d * elem_bytes(path));
+  return w;
+}
+
+#define WENC_TRY(expr)                       \
+  do {                                       \
+    if ((expr) != hipSuccess) return WENC_ERR_HIP; \
+  } while (0)
+
+// Enqueue one block; all arguments already validated.
+int run_block(const float* x, float* y, const char* blob, int rows, int t, int batch, int d,
+              int heads, int f, int path, const Workspace& ws, hipStream_t st) {
+  const LayerLayout L = layer_layout(d, f, path);
+  const int dt = path_dtype(path);
+  const size_t es = elem_bytes(path);
+  auto fp = [&](size_t off) { return reinterpret_cast<const float*>(blob + off); };
+  const void* wqkv = blob + L.wqkv;
+  const void* wo = blob + L.wo;
+  const void* w1 = blob + L.w1;
+  const void* w2 = blob + L.w2;
+  char* qkv = static_cast<char*>(ws.b);
+
+  WENC_TRY(launch_layernorm(x, fp(L.ln1_g), fp(L.ln1_b), ws.a, rows, d, dt, st));
+  WENC_TRY(launch_linear(ws.a, d, wqkv, fp(L.bqkv), nullptr, qkv, 3 * d, rows, 3 * d, d, dt,
+                         EPI_BIAS, st));
+  WENC_TRY(launch_attention(qkv, qkv + es * d, qkv + es * 2 * d, 3 * d, ws.a, d, batch, t, heads,
+                            0.125f, dt, st));
+  WENC_TRY(launch_linear(ws.a, d, wo, fp(L.bo), x, y, d, rows, d, d, dt, EPI_BIAS_RESIDUAL, st));
+  WENC_TRY(launch_layernorm(y, fp(L.ln2_g), fp(L.ln2_b), ws.a, rows, d, dt, st));
+  WENC_TRY(launch_linear(ws.a, d, w1, fp(L.b1), nullptr, ws.b, f, rows, f, d, dt, EPI_BIAS_GELU,
+                         st));
+  WENC_TRY(launch_linear(ws.b, f, w2, fp(L.b2), y, y, d, rows, d, f, dt, EPI_BIAS_RESIDUAL, st));
+  return WENC_OK;
+}
+
+bool overlaps_partially(const void* a, const void* b, size_t bytes) {
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  if (pa == pb) return false;
+  return pa < pb + bytes && pb < pa + bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* whisper_enc_strerror(int code) {
+  switch (code) {
+    case WENC_OK: return "ok";
+    case WENC_ERR_ARG: return "invalid argument (null or misaligned pointer, bad size or enum)";
+    case WENC_ERR_UNSUPPORTED: return "unsupported shape (head_dim must be 64)";
+    case WENC_ERR_WORKSPACE: return "workspace too small";
+    case WENC_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status code";
+}
+
+size_t whisper_enc_layer_bytes(int d_model, int ffn_dim, int path) {
+  if (path_dtype(path) < 0 || !valid_dims(d_model, ffn_dim)) return 0;
+  return layer_layout(d_model, ffn_dim, path).total;
+}
+
+int whisper_enc_pack_layer(const float* ln1_g, const float* ln1_b, const float* wq,
+                           const float* bq, const float* wk, const float* bk, const float* wv,
+                           const float* bv, const float* wo, const float* bo,
+                           const float* ln2_g, const float* ln2_b, const float* w1,
+                           const float* b1, const float* w2, const float* b2, int d_model,
+                           int ffn_dim, int path, void* dst_layer, void* stream) {
+  if (path_dtype(path) < 0 || !valid_dims(d_model, ffn_dim)) return WENC_ERR_ARG;
+  const float* req[] = {ln1_g, ln1_b, wq, bq, wk, wv, bv, wo, bo, ln2_g, ln2_b, w1, b1, w2, b2};
+  for (const float* p : req)
+    if (!p) return WENC_ERR_ARG;
+  if (!dst_layer || !aligned(dst_layer, kAlign)) return WENC_ERR_ARG;
+
+  const int d = d_model, f = ffn_dim, dt = path_dtype(path);
+  const size_t dd = (size_t)d * d;
+  const LayerLayout L = layer_layout(d, f, path);
+  const size_t es = elem_bytes(path);
+  char* blob = static_cast<char*>(dst_layer);
+  auto fo = [&](size_t off) { return reinterpret_cast<float*>(blob + off); };
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  WENC_TRY(launch_copy_or_zero(ln1_g, fo(L.ln1_g), d, st));
+  WENC_TRY(launch_copy_or_zero(ln1_b, fo(L.ln1_b), d, st));
+  WENC_TRY(launch_copy_or_zero(bq, fo(L.bqkv), d, st));
+  WENC_TRY(launch_copy_or_zero(bk, fo(L.bqkv) + d, d, st));
+  WENC_TRY(launch_copy_or_zero(bv, fo(L.bqkv) + 2 * d, d, st));
+  WENC_TRY(launch_copy_or_zero(bo, fo(L.bo), d, st));
+  WENC_TRY(launch_copy_or_zero(ln2_g, fo(L.ln2_g), d, st));
+  WENC_TRY(launch_copy_or_zero(ln2_b, fo(L.ln2_b), d, st));
+  WENC_TRY(launch_copy_or_zero(b1, fo(L.b1), f, st));
+  WENC_TRY(launch_copy_or_zero(b2, fo(L.b2), d, st));
+  WENC_TRY(launch_convert(wq, blob + L.wqkv, dd, dt, st));
+  WENC_TRY(launch_convert(wk, blob + L.wqkv + es * dd, dd, dt, st));
+  WENC_TRY(launch_convert(wv, blob + L.wqkv + es * 2 * dd, dd, dt, st));
+  WENC_TRY(launch_convert(wo, blob + L.wo, dd, dt, st));
+  WENC_TRY(launch_convert(w1, blob + L.w1, (size_t)f * d, dt, st));
+  WENC_TRY(launch_convert(w2, blob + L.w2, (size_t)d * f, dt, st));
+  return WENC_OK;
+}
+
+size_t whisper_enc_workspace_bytes(int batch, int t, int d_model, int heads, int ffn_dim,
+                                   int path) {
+  if (check_shape(batch, t, d_model, heads, ffn_dim, path) != WENC_OK) return 0;
+  return workspace_size((size_t)batch * t, d_model, ffn_dim, path);
+}
+
+int whisper_enc_stack_forward(const float* x, float* y, const void* layers, int n_layers,
+                              const float* ln_post_g, const float* ln_post_b, int batch, int t,
+                              int d_model, int heads, int ffn_dim, int path, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  int rc = check_shape(batch, t, d_model, heads, ffn_dim, path);
+  if (rc != WENC_OK) return rc;
+  if (n_layers < 0) return WENC_ERR_ARG;
+  if ((ln_post_g == nullptr) != (ln_post_b == nullptr)) return WENC_ERR_ARG;
+  const size_t rows = (size_t)batch * t;
+  if (rows == 0) return WENC_OK;
+  const size_t xbytes = rows * d_model * sizeof(float);
+  if (!x || !y || !aligned(x, 16) || !aligned(y, 16)) return WENC_ERR_ARG;
+  if (overlaps_partially(x, y, xbytes)) return WENC_ERR_ARG;
+  if (ln_post_g && (!aligned(ln_post_g, 16) || !aligned(ln_post_b, 16))) return WENC_ERR_ARG;
+  if (n_layers > 0) {
+    if (!layers || !aligned(layers, kAlign)) return WENC_ERR_ARG;
+    if (!workspace || !aligned(workspace, kAlign)) return WENC_ERR_ARG;
+    if (workspace_bytes < workspace_size(rows, d_model, ffn_dim, path)) return WENC_ERR_WORKSPACE;
+  }
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t lb = layer_layout(d_model, ffn_dim, path).total;
+  const Workspace ws = carve(workspace, rows, d_model, path);
+  const float* src = x;
+  for (int l = 0; l < n_layers; ++l) {
+    rc = run_block(src, y, static_cast<const char*>(layers) + (size_t)l * lb, (int)rows, t, batch,
+                   d_model, heads, ffn_dim, path, ws, st);
+    if (rc != WENC_OK) return rc;
+    src = y;
+  }
+  if (ln_post_g) {
+    WENC_TRY(launch_layernorm(src, ln_post_g, ln_post_b, y, (int)rows, d_model, DT_F32, st));
+  } else if (src != y) {
+    WENC_TRY(hipMemcpyAsync(y, src, xbytes, hipMemcpyDeviceToDevice, st));
+  }
+  return WENC_OK;
+}
+
+int whisper_enc_block_forward(const float* x, float* y, const void* layer, int batch, int t,
+                              int d_model, int heads, int ffn_dim, int path, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  int rc = check_shape(batch, t, d_model, heads, ffn_dim, path);
+  if (rc != WENC_OK) return rc;
+  if ((size_t)batch * t == 0) return WENC_OK;
+  if (!layer) return WENC_ERR_ARG;
+  return whisper_enc_stack_forward(x, y, layer, 1, nullptr, nullptr, batch, t, d_model, heads,
+                                   ffn_dim, path, workspace, workspace_bytes, stream);
+}
+
+int whisper_enc_layernorm(const float* x, const float* gamma, const float* beta, void* y,
+                          int rows, int d, int out_dtype, void* stream) {
+  if (rows < 0 || rows > WENC_MAX_ROWS) return WENC_ERR_ARG;
+  if (d < 64 || d > WENC_MAX_D_MODEL || d % 64 != 0) return WENC_ERR_ARG;
+  if (out_dtype != WENC_DTYPE_F32 && out_dtype != WENC_DTYPE_BF16 && out_dtype != WENC_DTYPE_F16)
+    return WENC_ERR_ARG;
+  if (rows == 0) return WENC_OK;
+  if (!x || !gamma || !beta || !y) return WENC_ERR_ARG;
+  if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(beta, 16) || !aligned(y, 16))
+    return WENC_ERR_ARG;
+  if (out_dtype != WENC_DTYPE_F32 &&
+      overlaps_partially(x, y, (size_t)rows * d * sizeof(float)))
+    return WENC_ERR_ARG;
+  if (out_dtype != WENC_DTYPE_F32 && x == (const void*)y) return WENC_ERR_ARG;
+  const int dt = out_dtype == WENC_DTYPE_F32 ? DT_F32 : out_dtype == WENC_DTYPE_BF16 ? DT_BF16 : DT_F16;
+  WENC_TRY(launch_layernorm(x, gamma, beta, y, rows, d, dt, static_cast<hipStream_t>(stream)));
+  return WENC_OK;
+}
+
+int whisper_enc_linear(const void* a, const void* w, const float* bias, const float* residual,
+                       void* c, int m, int n, int k, int path, int epilogue, void* stream) {
+  const int dt = path_dtype(path);
+  if (dt < 0) return WENC_ERR_ARG;
+  if (epilogue != WENC_EPI_BIAS && epilogue != WENC_EPI_BIAS_GELU &&
+      epilogue != WENC_EPI_BIAS_RESIDUAL)
+    return WENC_ERR_ARG;
+  if (m < 0 || m > WENC_MAX_ROWS || n < 64 || k < 64 || n % 64 || k % 64 || n > WENC_MAX_FFN_DIM ||
+      k > WENC_MAX_FFN_DIM)
+    return WENC_ERR_ARG;
+  if (m == 0) return WENC_OK;
+  if (!a || !w || !bias || !c) return WENC_ERR_ARG;
+  if (epilogue == WENC_EPI_BIAS_RESIDUAL && !residual) return WENC_ERR_ARG;
+  if (!aligned(a, 16) || !aligned(w, 16) || !aligned(bias, 16) || !aligned(c, 16) ||
+      (residual && !aligned(residual, 16)))
+    return WENC_ERR_ARG;
+  if (epilogue == WENC_EPI_BIAS_RESIDUAL &&
+      overlaps_partially(residual, c, (size_t)m * n * sizeof(float)))
+    return WENC_ERR_ARG;
+  const int epi = epilogue == WENC_EPI_BIAS ? EPI_BIAS
+                  : epilogue == WENC_EPI_BIAS_GELU ? EPI_BIAS_GELU : EPI_BIAS_RESIDUAL;
+  WENC_TRY(launch_linear(a, k, w, bias, residual, c, n, m, n, k, dt, epi,
+                         static_cast<hipStream_t>(stream)));
+  return WENC_OK;
+}
+
+int whisper_enc_attention(const void* q, const void* k, const void* v, void* o, int batch, int t,
+                          int heads, int ld_qkv, int ld_o, int path, void* stream) {
+  const int dt = path_dtype(path);
+  if (dt < 0) return WENC_ERR_ARG;
+  if (batch < 0 || t < 0 || heads <= 0 || (long long)batch * t > WENC_MAX_ROWS) return WENC_ERR_ARG;
+  if (heads * WENC_HEAD_DIM > WENC_MAX_FFN_DIM) return WENC_ERR_ARG;
+  if (ld_qkv < heads * WENC_HEAD_DIM || ld_o < heads * WENC_HEAD_DIM || ld_qkv % 8 || ld_o % 8)
+    return WENC_ERR_ARG;
+  if ((size_t)batch * t == 0) return WENC_OK;
+  if (!q || !k || !v || !o) return WENC_ERR_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return WENC_ERR_ARG;
+  WENC_TRY(launch_attention(q, k, v, ld_qkv, o, ld_o, batch, t, heads, 0.125f, dt,
+                            static_cast<hipStream_t>(stream)));
+  return WENC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,123 @@
+// LayerNorm over rows of an fp32 matrix, one wavefront per row.
+//
+// Whisper's pre-LN block normalises each position before attention and before the FFN, and a
+// stack ends in one more LayerNorm (inferencelayer whisper_gpu.rs, LN_SRC and
+// WhisperEncoderGpu::forward; oxinfer whisper/model.rs, encode).  Two passes as there: the row
+// mean, then the biased variance of the centred values, inv = 1/sqrt(var + 1e-5), and the affine.
+//
+// The pages' shader runs one 256-thread workgroup per row with shared-memory tree reductions.
+// Here a 64-lane wavefront owns a row: it loads the whole row into registers with 16-byte
+// loads (d <= 4096), reduces with cross-lane shuffles, and writes the normalised row in the
+// GEMM operand type (bf16 / fp16) or fp32.  Four rows per 256-thread workgroup.  The pass is
+// HBM-bound: 4 bytes read and 2 (or 4) bytes written per element.
+#include "wenc_device.h"
+#include "wenc_internal.h"
+
+namespace wenc {
+
+template <int NV, typename OutT>
+struct LnStore;
+
+template <int NV>
+struct LnStore<NV, float> {
+  static __device__ __forceinline__ void put(void* y, size_t row, int d, int c, float4 v) {
+    *reinterpret_cast<float4*>(static_cast<float*>(y) + row * d + c) = v;
+  }
+};
+template <int NV>
+struct LnStore<NV, bf16_t> {
+  static __device__ __forceinline__ void put(void* y, size_t row, int d, int c, float4 v) {
+    u32x2 w = {pack2<bf16_t>(v.x, v.y), pack2<bf16_t>(v.z, v.w)};
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(y) + row * d + c) = w;
+  }
+};
+template <int NV>
+struct LnStore<NV, f16_t> {
+  static __device__ __forceinline__ void put(void* y, size_t row, int d, int c, float4 v) {
+    u32x2 w = {pack2<f16_t>(v.x, v.y), pack2<f16_t>(v.z, v.w)};
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(y) + row * d + c) = w;
+  }
+};
+
+// NV = float4 vectors per lane (d <= 256 * NV).
+template <int NV, typename OutT>
+__global__ __launch_bounds__(256) void layernorm_rows(const float* __restrict__ x,
+                                                      const float* __restrict__ gamma,
+                                                      const float* __restrict__ beta,
+                                                      void* y, int rows, int d, float eps) {
+  const int lane = threadIdx.x & 63;
+  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (size_t)rows) return;
+  const float* xr = x + row * d;
+  float4 v[NV];
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int c = (lane + 64 * j) * 4;
+    if (c < d) {
+      v[j] = *reinterpret_cast<const float4*>(xr + c);
+      s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+    } else {
+      v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  const float inv_d = 1.0f / (float)d;
+  const float mean = wave_sum(s) * inv_d;
+  float q = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int c = (lane + 64 * j) * 4;
+    if (c < d) {
+      v[j].x -= mean; v[j].y -= mean; v[j].z -= mean; v[j].w -= mean;
+      q += (v[j].x * v[j].x + v[j].y * v[j].y) + (v[j].z * v[j].z + v[j].w * v[j].w);
+    }
+  }
+  const float var = wave_sum(q) * inv_d;
+  const float inv = 1.0f / sqrtf(var + eps);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int c = (lane + 64 * j) * 4;
+    if (c < d) {
+      const float4 g = *reinterpret_cast<const float4*>(gamma + c);
+      const float4 b = *reinterpret_cast<const float4*>(beta + c);
+      float4 o;
+      o.x = v[j].x * inv * g.x + b.x;
+      o.y = v[j].y * inv * g.y + b.y;
+      o.z = v[j].z * inv * g.z + b.z;
+      o.w = v[j].w * inv * g.w + b.w;
+      LnStore<NV, OutT>::put(y, row, d, c, o);
+    }
+  }
+}
+
+template <typename OutT>
+static hipError_t launch_ln_t(const float* x, const float* g, const float* b, void* y, int rows,
+                              int d, hipStream_t st) {
+  dim3 grid((rows + 3) / 4), block(256);
+  const float eps = 1e-5f;
+  const int nv = (d + 255) / 256;
+  switch (nv) {
+#define WENC_LN_CASE(N) \
+  case N: layernorm_rows<N, OutT><<<grid, block, 0, st>>>(x, g, b, y, rows, d, eps); break;
+    WENC_LN_CASE(1) WENC_LN_CASE(2) WENC_LN_CASE(3) WENC_LN_CASE(4) WENC_LN_CASE(5)
+    WENC_LN_CASE(6) WENC_LN_CASE(7) WENC_LN_CASE(8) WENC_LN_CASE(9) WENC_LN_CASE(10)
+    WENC_LN_CASE(11) WENC_LN_CASE(12) WENC_LN_CASE(13) WENC_LN_CASE(14) WENC_LN_CASE(15)
+    WENC_LN_CASE(16)
+#undef WENC_LN_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* y, int rows,
+                            int d, int out_dtype, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  switch (out_dtype) {
+    case DT_F32: return launch_ln_t<float>(x, g, b, y, rows, d, st);
+    case DT_BF16: return launch_ln_t<bf16_t>(x, g, b, y, rows, d, st);
+    case DT_F16: return launch_ln_t<f16_t>(x, g, b, y, rows, d, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace wenc

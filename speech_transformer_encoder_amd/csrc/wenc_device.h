@@ -1,0 +1,95 @@
+// Device-side helpers shared by the gfx950 kernels: operand vector types, fp32 -> 16-bit
+// rounding, MFMA wrappers and wavefront reductions.  CDNA4 only (64-lane wavefronts).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wenc {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 16-bit storage tags.  Both are held as raw uint16_t bit patterns in memory.
+struct bf16_t {};
+struct f16_t {};
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  _Float16 h = (_Float16)f;  // v_cvt_f16_f32: round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+template <typename T> struct Cvt;
+template <> struct Cvt<bf16_t> {
+  static __device__ __forceinline__ uint32_t bits(float f) { return f32_to_bf16_bits(f); }
+  static __device__ __forceinline__ float to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+};
+template <> struct Cvt<f16_t> {
+  static __device__ __forceinline__ uint32_t bits(float f) { return f32_to_f16_bits(f); }
+  static __device__ __forceinline__ float to_f32(uint32_t b) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+  }
+};
+
+// Two fp32 -> one packed 32-bit word (lo in bits 0..15).
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return Cvt<T>::bits(lo) | (Cvt<T>::bits(hi) << 16);
+}
+
+// D(32x32) += A(32x16) * B(16x32), 16-bit operands held as 4 packed dwords per lane.
+// Lane l supplies A[row l%32][k 8*(l/32) .. +7] and B[k 8*(l/32) .. +7][col l%32];
+// D lane l holds column l%32, rows 8*j + 4*(l/32) + i at register 4*j + i.
+template <typename T>
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c);
+template <>
+__device__ __forceinline__ f32x16 mfma32x32x16<bf16_t>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mfma32x32x16<f16_t>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// D(32x32) += A(32x2) * B(2x32) in fp32.  Lane l supplies A[row l%32][k l/32] and
+// B[k l/32][col l%32]; D has the same layout as the 16-bit form.
+__device__ __forceinline__ f32x16 mfma32x32x2_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Combine a value with the one held by lane l^32 (the other half of the wavefront).
+// v_permlane32_swap exchanges lanes 32..63 of its first operand with lanes 0..31 of its
+// second; with the same value in both, every lane ends up with {own, partner} across the two
+// results, so a symmetric operation of the pair needs no lane-dependent select.
+__device__ __forceinline__ float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace wenc

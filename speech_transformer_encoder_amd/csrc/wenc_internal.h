@@ -1,0 +1,38 @@
+// Host-side launchers of the gfx950 kernels.  Each returns the launch's hipError_t; none of
+// them allocates, synchronises or validates shapes (the C ABI in api.hip does that first).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wenc {
+
+enum DType { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+enum Epilogue { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2 };
+
+// y[rows, d] = LayerNorm(x[rows, d]) * gamma + beta, stored as out_dtype.  d % 4 == 0, d <= 4096.
+hipError_t launch_layernorm(const float* x, const float* gamma, const float* beta, void* y,
+                            int rows, int d, int out_dtype, hipStream_t st);
+
+// c[m, n] = epilogue(a[m, k] . w[n, k]^T + bias[n]) with 16-bit (dtype) or fp32 operands.
+//   EPI_BIAS          -> c in the operand dtype (fp32 for DT_F32)
+//   EPI_BIAS_GELU     -> c = gelu_erf(.) in the operand dtype
+//   EPI_BIAS_RESIDUAL -> c fp32 = residual + (.)   (c may alias residual)
+// lda / ldc are row strides in elements.  k % 64 == 0, n % 64 == 0.
+hipError_t launch_linear(const void* a, int lda, const void* w, const float* bias,
+                         const float* residual, void* c, int ldc, int m, int n, int k, int dtype,
+                         int epilogue, hipStream_t st);
+
+// Bidirectional attention per (window, head), head_dim 64.  q/k/v/o rows of the window b at
+// ptr + (b * t + i) * ld, head h at column offset 64 * h.  scale multiplies q.k.
+hipError_t launch_attention(const void* q, const void* k, const void* v, int ld_qkv, void* o,
+                            int ld_o, int batch, int t, int heads, float scale, int dtype,
+                            hipStream_t st);
+
+// dst[i] = round(src[i]) in dtype (or a copy for DT_F32); n elements.
+hipError_t launch_convert(const float* src, void* dst, size_t n, int dtype, hipStream_t st);
+// dst[i] = src ? src[i] : 0 for i < n (fp32).
+hipError_t launch_copy_or_zero(const float* src, float* dst, size_t n, hipStream_t st);
+
+}  // namespace wenc

@@ -1,0 +1,132 @@
+"""The C ABI without a GPU: the library loads, exports what the header declares, and rejects bad
+arguments before it touches HIP (so every call below returns without a device)."""
+
+import os
+import re
+
+import pytest
+
+from speech_transformer_encoder_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "whisper_enc.h")
+
+FAKE = 1 << 20  # aligned, non-null "device" address: validation must fail before any use
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libwhisper_enc.so is not built (run __graft_entry__.build())")
+    return B.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(whisper_enc_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_sizes():
+    assert B.whisper_enc_layer_bytes(384, 1536, B.WENC_PATH_BF16) > 0
+    bf = B.whisper_enc_layer_bytes(1280, 5120, B.WENC_PATH_BF16)
+    f32 = B.whisper_enc_layer_bytes(1280, 5120, B.WENC_PATH_FP32)
+    # matrices dominate: 12 d^2 elements of 2 or 4 bytes
+    assert bf >= 12 * 1280 * 1280 * 2 and f32 >= 12 * 1280 * 1280 * 4
+    assert bf % 256 == 0 and f32 % 256 == 0
+    assert B.whisper_enc_layer_bytes(100, 5120, 0) == 0
+    assert B.whisper_enc_layer_bytes(1280, 5120, 7) == 0
+    ws = B.whisper_enc_workspace_bytes(16, 1500, 1280, 20, 5120, B.WENC_PATH_BF16)
+    assert ws >= 16 * 1500 * (1280 + 5120) * 2
+    assert B.whisper_enc_workspace_bytes(1, 1500, 1280, 16, 5120, 0) == 0  # head_dim 80
+
+
+def test_strerror(lib):
+    for code in range(5):
+        assert B.strerror(code)
+    assert "unknown" in B.strerror(99)
+
+
+def _block(lib, **kw):
+    a = dict(x=FAKE, y=FAKE, layer=FAKE, batch=1, t=1500, d=384, heads=6, f=1536, path=0,
+             ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.whisper_enc_block_forward(a["x"], a["y"], a["layer"], a["batch"], a["t"], a["d"],
+                                         a["heads"], a["f"], a["path"], a["ws"], a["wsb"],
+                                         a["stream"])
+
+
+def test_block_validation(lib):
+    assert _block(lib, heads=4) == B.WENC_ERR_UNSUPPORTED      # head_dim 96
+    assert _block(lib, heads=5) == B.WENC_ERR_ARG              # d % heads != 0
+    assert _block(lib, d=100, heads=1) == B.WENC_ERR_ARG
+    assert _block(lib, f=100) == B.WENC_ERR_ARG
+    assert _block(lib, path=3) == B.WENC_ERR_ARG
+    assert _block(lib, batch=-1) == B.WENC_ERR_ARG
+    assert _block(lib, x=None) == B.WENC_ERR_ARG
+    assert _block(lib, layer=None) == B.WENC_ERR_ARG
+    assert _block(lib, ws=None) == B.WENC_ERR_ARG
+    assert _block(lib, x=FAKE + 4) == B.WENC_ERR_ARG           # misaligned
+    assert _block(lib, layer=FAKE + 16) == B.WENC_ERR_ARG      # blob must be 256-aligned
+    assert _block(lib, y=FAKE + 16) == B.WENC_ERR_ARG          # partial overlap with x
+    assert _block(lib, wsb=1000) == B.WENC_ERR_WORKSPACE
+    assert _block(lib, batch=1 << 20, t=1500) == B.WENC_ERR_ARG  # too many rows
+    # empty input: nothing to do, pointers unused
+    assert _block(lib, batch=0, x=None, y=None, layer=None, ws=None) == B.WENC_OK
+    assert _block(lib, t=0, x=None, y=None, layer=None, ws=None) == B.WENC_OK
+
+
+def test_stack_validation(lib):
+    f = lib.whisper_enc_stack_forward
+    args = [FAKE, FAKE + (1 << 24), FAKE, 4, None, None, 1, 1500, 512, 8, 2048, 0, FAKE, 1 << 40,
+            None]
+    ok = list(args)
+    bad = list(args); bad[3] = -1
+    assert f(*bad) == B.WENC_ERR_ARG
+    bad = list(args); bad[4] = FAKE                            # gamma without beta
+    assert f(*bad) == B.WENC_ERR_ARG
+    bad = list(args); bad[13] = 10
+    assert f(*bad) == B.WENC_ERR_WORKSPACE
+    bad = list(args); bad[9] = 16
+    assert f(*bad) == B.WENC_ERR_UNSUPPORTED
+    assert ok  # the valid call itself needs a GPU
+
+
+def test_step_validation(lib):
+    assert lib.whisper_enc_layernorm(FAKE, FAKE, FAKE, FAKE, 10, 100, 0, None) == B.WENC_ERR_ARG
+    assert lib.whisper_enc_layernorm(FAKE, FAKE, FAKE, FAKE, 10, 384, 5, None) == B.WENC_ERR_ARG
+    assert lib.whisper_enc_layernorm(FAKE, FAKE, FAKE, FAKE, 10, 384, 1, None) == B.WENC_ERR_ARG
+    assert lib.whisper_enc_layernorm(None, None, None, None, 0, 384, 1, None) == B.WENC_OK
+    lin = lib.whisper_enc_linear
+    assert lin(FAKE, FAKE, FAKE, None, FAKE, 10, 100, 64, 0, 0, None) == B.WENC_ERR_ARG
+    assert lin(FAKE, FAKE, FAKE, None, FAKE, 10, 128, 64, 0, 2, None) == B.WENC_ERR_ARG
+    assert lin(FAKE, FAKE, None, None, FAKE, 10, 128, 64, 0, 0, None) == B.WENC_ERR_ARG
+    assert lin(FAKE, FAKE, FAKE, None, FAKE, 10, 128, 64, 0, 9, None) == B.WENC_ERR_ARG
+    att = lib.whisper_enc_attention
+    assert att(FAKE, FAKE, FAKE, FAKE, 1, 100, 2, 64, 128, 0, None) == B.WENC_ERR_ARG
+    assert att(FAKE, FAKE, FAKE, FAKE, 1, 100, 2, 130, 128, 0, None) == B.WENC_ERR_ARG
+    assert att(None, None, None, None, 0, 100, 2, 128, 128, 0, None) == B.WENC_OK
+    pk = lib.whisper_enc_pack_layer
+    ptrs = [FAKE] * 16
+    assert pk(*ptrs, 384, 1536, 0, FAKE + 8, None) == B.WENC_ERR_ARG
+    ptrs2 = list(ptrs); ptrs2[2] = None
+    assert pk(*ptrs2, 384, 1536, 0, FAKE, None) == B.WENC_ERR_ARG
+    assert pk(*ptrs, 384, 1000, 0, FAKE, None) == B.WENC_ERR_ARG
+
+
+def test_package_has_no_cpu_fallback():
+    """The product package never imports the oracle."""
+    pkg = os.path.join(ROOT, "speech_transformer_encoder_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "import oracle" not in text and "from oracle" not in text, fn

@@ -18,35 +18,35 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 struct bf16_t {};
 struct f16_t {};
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN kept quiet).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
-  _Float16 h = (_Float16)f;  // v_cvt_f16_f32: round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, h);
-}
-
+// fp32 -> 16-bit conversions, round to nearest even.  gfx950 converts to bf16 in hardware
+// (v_cvt_pk_bf16_f32), and to fp16 with v_cvt_f16_f32.
 template <typename T> struct Cvt;
 template <> struct Cvt<bf16_t> {
-  static __device__ __forceinline__ uint32_t bits(float f) { return f32_to_bf16_bits(f); }
-  static __device__ __forceinline__ float to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+  static __device__ __forceinline__ uint32_t bits(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    bf16x2 r = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, r);
+  }
 };
 template <> struct Cvt<f16_t> {
-  static __device__ __forceinline__ uint32_t bits(float f) { return f32_to_f16_bits(f); }
-  static __device__ __forceinline__ float to_f32(uint32_t b) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+  static __device__ __forceinline__ uint32_t bits(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    f16x2 r = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, r);
   }
 };
 
 // Two fp32 -> one packed 32-bit word (lo in bits 0..15).
 template <typename T>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return Cvt<T>::bits(lo) | (Cvt<T>::bits(hi) << 16);
+  return Cvt<T>::pack(lo, hi);
 }
 
 // D(32x32) += A(32x16) * B(16x32), 16-bit operands held as 4 packed dwords per lane.

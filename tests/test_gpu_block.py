@@ -116,6 +116,22 @@ def test_windows_are_independent():
     np.testing.assert_array_equal(full[2:3], alone)
 
 
+@pytest.mark.parametrize("path", [B.WENC_PATH_BF16, B.WENC_PATH_FP16])
+def test_pack_rounds_to_nearest_even(path):
+    """Packing fp32 weights rounds them exactly as PyTorch's RNE conversion does: the block on
+    fp32 weights equals, bit for bit, the block on weights pre-rounded to the operand type."""
+    import torch
+    from tests.gpu_util import torch_dtype
+    cfg = synth.CONFIGS["tiny_block"].with_(t=128)
+    w = synth.make_workload(cfg)
+    a = run_gpu(w, path)
+    for n in ("wq", "wk", "wv", "wo", "w1", "w2"):
+        t = torch.from_numpy(w.layers[0][n]).to(torch_dtype(path)).to(torch.float32)
+        w.layers[0][n] = t.numpy()
+    b = run_gpu(w, path)
+    np.testing.assert_array_equal(a, b)
+
+
 def test_zero_weights_closed_form():
     cfg = synth.CONFIGS["tiny_block"].with_(t=100)
     w = synth.make_workload(cfg)

@@ -64,7 +64,7 @@ def test_layernorm_in_place_fp32():
 @pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("epi", [B.WENC_EPI_BIAS, B.WENC_EPI_BIAS_GELU, B.WENC_EPI_BIAS_RESIDUAL])
 @pytest.mark.parametrize("m,n,k", [(1, 64, 64), (200, 384, 384), (257, 192, 512), (1500, 1152, 384),
-                                   (129, 1280, 5120)])
+                                   (129, 1280, 5120), (6000, 4160, 128), (24000, 1280, 64)])
 def test_linear(path, epi, m, n, k):
     import torch
     r = _rng(m, n, k, epi)

@@ -35,10 +35,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="large_v3_batch16_block")
-    ap.add_argument("--path", default="bf16", choices=["bf16", "fp16", "fp32"])
+    ap.add_argument("--path", default="fp16", choices=["bf16", "fp16", "fp32"])
+    ap.add_argument("--compare-paths", default="bf16",
+                    help="comma-separated other paths timed the same way (reported, not value)")
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-windows", type=int, default=3)
+    ap.add_argument("--cpu-sample-windows", type=int, default=16)
     ap.add_argument("--cpu-sample-layers", type=int, default=2)
     return ap.parse_args()
 
@@ -174,23 +176,29 @@ def main():
     cfg = synth.CONFIGS[args.config]
     path = B.PATHS[args.path]
     w = synth.make_workload(cfg)
-    enc = build_from_workload(w, path)
     x = to_device_input(w.x)
     y = torch.empty_like(x)
-    enc.workspace(cfg.batch, cfg.t)
-    for _ in range(args.warmup):
-        enc.forward(x, y)
-    torch.cuda.synchronize()
     st = torch.cuda.current_stream()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    s.record(st)
-    for _ in range(args.steps):
-        enc.forward(x, y)
-    e.record(st)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = s.elapsed_time(e) / args.steps
+
+    def time_forward(enc):
+        enc.workspace(cfg.batch, cfg.t)
+        for _ in range(args.warmup):
+            enc.forward(x, y)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        s.record(st)
+        for _ in range(args.steps):
+            enc.forward(x, y)
+        e.record(st)
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / args.steps, time.perf_counter() - t0
+
+    ms, wall = time_forward(build_from_workload(w, path))
+    others = {}
+    for pn in [p for p in args.compare_paths.split(",") if p and p != args.path]:
+        oms, _ = time_forward(build_from_workload(w, B.PATHS[pn]))
+        others[pn] = {"value": round(cfg.batch * cfg.t / (oms * 1e-3), 1), "ms_per_step": round(oms, 4)}
     frames = cfg.batch * cfg.t
     flops = cfg.flops()
 
@@ -240,6 +248,7 @@ def main():
         "kernels": kern,
         "wall_s_timed": round(wall, 4),
         "cpu_baseline": cpu,
+        "other_paths": others,
     }
     print(json.dumps(out), flush=True)
 

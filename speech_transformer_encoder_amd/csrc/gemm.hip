@@ -10,159 +10,49 @@
 // design of the same contraction.
 //
 // Both operands are K-contiguous (x rows, W rows), so the tile is computed as
-// D[n][m] = W[n][:] . X[m][:]: W feeds the MFMA's A operand and X its B operand, and each lane
-// of the 32x32 accumulator then owns four consecutive output columns n for one row m, which
-// the epilogue reads and writes as one 8- or 16-byte vector.
+// D[n][m] = W[n][:] . X[m][:]: W feeds the MFMA's A operand and X its B operand.
 //
-// Tile: 128 (n) x 128 (m) x 64 (k) per 256-thread workgroup, four wavefronts in a 2 x 2 grid,
-// each owning 64 x 64 outputs as 2 x 2 blocks of v_mfma_f32_32x32x16 (16-bit operands) or
-// v_mfma_f32_32x32x2_f32 (fp32 operands, 32-wide k tile).  Operand tiles are staged through
-// LDS, double buffered with one barrier per k tile; the next tile's global loads are issued
-// before the current tile's MFMAs.  Rows are padded by 16 bytes so that the 16-byte fragment
-// reads of 8 consecutive lanes hit 32 distinct banks.
+// 16-bit operands (bf16 or fp16).  One 512-thread workgroup (8 wavefronts, two per SIMD) owns a
+// 256 (n) x 256 (m) output tile; wavefront w owns 64 (n) x 128 (m) of it as 2 x 4 blocks of
+// v_mfma_f32_32x32x16 with 128 fp32 accumulators per lane.  k advances in tiles of 64:
+//   * operand tiles go global -> LDS with buffer_load_dwordx4 ... lds (no VGPR staging), into one
+//     of two 64 KB stages; buffer range checks return zeros for rows past M or N;
+//   * an LDS row is 128 bytes (64 k values) held as eight 16-byte chunks, chunk c of row r at
+//     slot c ^ ((r >> 1) & 7): each 16-lane phase of a fragment read then covers the 64 banks once;
+//   * the fragments of the next 16-k step are read while the MFMAs of the current one run;
+//   * one barrier per k tile; the loads of tile kt + 2 are issued right after it.
+// The epilogue stages each wavefront's 32 x 64 block through LDS so that global stores (and the
+// residual loads) are whole 128- or 256-byte row segments.  Workgroups are renumbered so that
+// each XCD (eight, dispatched round-robin) runs a contiguous range of tiles grouped 8 m-tiles
+// deep, so tiles running together share operand rows in that XCD's L2.
+#include <type_traits>
+
 #include "wenc_device.h"
 #include "wenc_internal.h"
 
 namespace wenc {
 
-constexpr int GB_N = 128;  // W rows (output columns) per tile
-constexpr int GB_M = 128;  // X rows per tile
-constexpr int GB_K = 64;   // 16-bit elements of k per tile
-constexpr int GLDS = GB_K + 8;  // LDS row stride in 16-bit elements (144 bytes)
-
+// erf-GELU, gelu(z) = z/2 (1 + erf(z / sqrt 2)), with the device library's erff (fp32 path).
 __device__ __forceinline__ float gelu_erf(float z) {
   return 0.5f * z * (1.0f + erff(z * 0.7071067811865476f));
 }
 
-template <typename T, int EPI>
-__device__ __forceinline__ void store4(void* c, const float* residual, size_t off, float4 v) {
-  if constexpr (EPI == EPI_BIAS_RESIDUAL) {
-    const float4 r = *reinterpret_cast<const float4*>(residual + off);
-    float4 o = make_float4(r.x + v.x, r.y + v.y, r.z + v.z, r.w + v.w);
-    *reinterpret_cast<float4*>(static_cast<float*>(c) + off) = o;
-  } else {
-    if constexpr (EPI == EPI_BIAS_GELU) {
-      v.x = gelu_erf(v.x); v.y = gelu_erf(v.y); v.z = gelu_erf(v.z); v.w = gelu_erf(v.w);
-    }
-    u32x2 w = {pack2<T>(v.x, v.y), pack2<T>(v.z, v.w)};
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(c) + off) = w;
-  }
+// erf-GELU for the 16-bit paths, whose output is rounded to 8 or 11 significant bits: the
+// complementary error function from Abramowitz & Stegun, Handbook of Mathematical Functions,
+// formula 7.1.26 (Hastings' rational approximation, absolute error <= 1.5e-7):
+//   erfc(a) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-a^2),  t = 1 / (1 + p a),  a >= 0,
+// and gelu(z) = max(z, 0) - |z|/2 erfc(|z| / sqrt 2), which holds for both signs of z.
+__device__ __forceinline__ float gelu_erf_as(float z) {
+  const float a = fabsf(z) * 0.7071067811865476f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, a, 1.0f));
+  float p = fmaf(t, 1.061405429f, -1.453152027f);
+  p = fmaf(t, p, 1.421413741f);
+  p = fmaf(t, p, -0.284496736f);
+  p = fmaf(t, p, 0.254829592f);
+  p *= t;
+  const float e = __builtin_amdgcn_exp2f(-(a * a) * 1.4426950408889634f);
+  return fmaf(-0.5f * fabsf(z), p * e, fmaxf(z, 0.0f));
 }
-
-template <typename T, int EPI>
-__global__ __launch_bounds__(256) void gemm16_kernel(const uint16_t* __restrict__ X, int lda,
-                                                     const uint16_t* __restrict__ W,
-                                                     const float* __restrict__ bias,
-                                                     const float* residual, void* C, int ldc,
-                                                     int M, int N, int K) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][(GB_N + GB_M) * GLDS];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wn = wave >> 1, wm = wave & 1;
-  const int n0 = blockIdx.x * GB_N;
-  const int m0 = blockIdx.y * GB_M;
-
-  // Global -> register staging: 4 chunks of 16 bytes for each operand per thread.
-  u32x4 rw[4], rx[4];
-  auto gload = [&](int kt) {
-    const int kbase = kt * GB_K;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 3, col = (c & 7) * 8;
-      const int n = n0 + row, m = m0 + row;
-      rw[i] = (n < N) ? *reinterpret_cast<const u32x4*>(W + (size_t)n * K + kbase + col)
-                      : u32x4{0, 0, 0, 0};
-      rx[i] = (m < M) ? *reinterpret_cast<const u32x4*>(X + (size_t)m * lda + kbase + col)
-                      : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto lstore = [&](int buf) {
-    uint16_t* ws = lds[buf];
-    uint16_t* xs = lds[buf] + GB_N * GLDS;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 3, col = (c & 7) * 8;
-      *reinterpret_cast<u32x4*>(ws + row * GLDS + col) = rw[i];
-      *reinterpret_cast<u32x4*>(xs + row * GLDS + col) = rx[i];
-    }
-  };
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-
-  const int nk = K / GB_K;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  const int frow = lane & 31;
-  const int fcol = (lane >> 5) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint16_t* ws = lds[buf] + (wn * 64 + frow) * GLDS + fcol;
-    const uint16_t* xs = lds[buf] + GB_N * GLDS + (wm * 64 + frow) * GLDS + fcol;
-#pragma unroll
-    for (int s = 0; s < GB_K / 16; ++s) {
-      u32x4 fa[2], fb[2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        fa[b] = *reinterpret_cast<const u32x4*>(ws + b * 32 * GLDS + s * 16);
-        fb[b] = *reinterpret_cast<const u32x4*>(xs + b * 32 * GLDS + s * 16);
-      }
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = mfma32x32x16<T>(fa[a], fb[b], acc[a][b]);
-    }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue: lane owns column m, rows n = base + 8j + 4*(lane/32) + i (i = 0..3).
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int m = m0 + wm * 64 + b * 32 + (lane & 31);
-    if (m >= M) continue;
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wn * 64 + a * 32 + j * 8 + (lane >> 5) * 4;
-        if (n >= N) continue;
-        const float4 bb = *reinterpret_cast<const float4*>(bias + n);
-        float4 v = make_float4(acc[a][b][4 * j + 0] + bb.x, acc[a][b][4 * j + 1] + bb.y,
-                               acc[a][b][4 * j + 2] + bb.z, acc[a][b][4 * j + 3] + bb.w);
-        store4<T, EPI>(C, residual, (size_t)m * ldc + n, v);
-      }
-    }
-  }
-}
-
-// Large-problem variant: 256 (n) x 256 (m) x 64 (k) tiles, four wavefronts each owning a
-// 128 x 128 block of outputs (4 x 4 MFMA blocks, 256 fp32 accumulators per lane).  At this
-// wave tile each 32x32x16 MFMA needs 64 bytes of fragments from LDS, a quarter of what a
-// 64 x 64 wave tile needs, which keeps LDS bandwidth well below the MFMA rate.  LDS rows are
-// 128 bytes with the eight 16-byte chunks of row r stored at slot (chunk ^ (r & 7)): every
-// 8-lane phase of a 16-byte fragment read or write then covers all banks without padding.
-// Workgroups are renumbered so that each XCD (eight of them, dispatched round-robin) gets a
-// contiguous range of tiles, grouped 8 m-tiles deep, so concurrently running tiles share
-// operand rows in that XCD's L2.
-constexpr int BG_N = 256;
-constexpr int BG_M = 256;
-constexpr int BG_K = 64;
-constexpr int BG_GROUP_M = 8;
-
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BG_K + ((chunk ^ (row & 7)) << 3); }
 
 // Bijective renumbering of a 1-D grid so consecutive virtual ids run on the same XCD.
 __device__ __forceinline__ int xcd_virtual_id(int id, int nb) {
@@ -171,114 +61,208 @@ __device__ __forceinline__ int xcd_virtual_id(int id, int nb) {
   return (xcd < r) ? xcd * (q + 1) + pos : r * (q + 1) + (xcd - r) * q + pos;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int G_N = 256, G_M = 256, G_K = 64;  // workgroup tile
+constexpr int G_WN = 4, G_WM = 2;              // wavefront grid: n x m
+constexpr int G_TN = G_N / G_WN, G_TM = G_M / G_WM;  // 64 x 128 per wavefront
+constexpr int G_NA = G_TN / 32, G_NB = G_TM / 32;     // 2 x 4 MFMA blocks
+constexpr int G_WAVES = G_WN * G_WM;
+constexpr int G_THREADS = 64 * G_WAVES;
+constexpr int G_LPO = 32 / G_WAVES;  // 1 KB loads per operand per wavefront and k tile
+constexpr int G_STAGE = (G_N + G_M) * G_K;  // 16-bit elements per stage
+
 template <typename T, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm16_big_kernel(const uint16_t* __restrict__ X,
-                                                            int lda,
-                                                            const uint16_t* __restrict__ W,
-                                                            const float* __restrict__ bias,
-                                                            const float* residual, void* C,
-                                                            int ldc, int M, int N, int K) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t glds[];  // [2][(BG_N + BG_M) * BG_K]
+__global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __restrict__ X,
+                                                             int lda,
+                                                             const uint16_t* __restrict__ W,
+                                                             const float* __restrict__ bias,
+                                                             const float* residual, void* C,
+                                                             int ldc, int M, int N, int K) {
+  __shared__ __attribute__((aligned(1024))) uint16_t s0[G_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t s1[G_STAGE];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wn = wave >> 1, wm = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave / G_WM, wm = wave % G_WM;
+  const int g = lane >> 5, frow = lane & 31;
 
-  const int tiles_m = (M + BG_M - 1) / BG_M;
-  const int tiles_n = (N + BG_N - 1) / BG_N;
+  const int tiles_m = (M + G_M - 1) / G_M, tiles_n = (N + G_N - 1) / G_N;
   const int v = xcd_virtual_id(blockIdx.x, gridDim.x);
-  const int group = BG_GROUP_M * tiles_n;
-  const int first_m = (v / group) * BG_GROUP_M;
-  const int gm = min(tiles_m - first_m, BG_GROUP_M);
-  const int tm = first_m + (v % group) % gm;
-  const int tn = (v % group) / gm;
-  const int n0 = tn * BG_N, m0 = tm * BG_M;
+  const int group = 8 * tiles_n;
+  const int first_m = (v / group) * 8;
+  const int gm = min(tiles_m - first_m, 8);
+  const int tm = first_m + (v % group) % gm, tn = (v % group) / gm;
+  const int n0 = tn * G_N, m0 = tm * G_M;
 
-  // Global -> register staging: 8 chunks of 16 bytes of each operand per thread and k tile.
-  u32x4 rw[8], rx[8];
-  auto gload = [&](int kt) {
-    const int kbase = kt * BG_K;
+  // Buffer resources cover exactly the tile's valid rows: loads past them return zeros.
+  const int wrows = min(N - n0, G_N), xrows = min(M - m0, G_M);
+  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + (size_t)n0 * K), (short)0, wrows * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(X + (size_t)m0 * lda), (short)0, xrows * lda * 2, 0x00020000);
+
+  // Load instruction i of wavefront w fills the 1 KB LDS block (i * 8 + w): rows 8 * block ..
+  // + 7, lane l writing row (l >> 3), slot (l & 7), which holds chunk slot ^ ((row >> 1) & 7).
+  const int lrow = 8 * wave + (lane >> 3);
+  const int lchunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
+  const int voW = lrow * K * 2 + lchunk * 16, voX = lrow * lda * 2 + lchunk * 16;
+  const int stepW = 64 * K * 2, stepX = 64 * lda * 2;
+  auto load_tile = [&](int kt, uint16_t* st) {
+    const int so = kt * (G_K * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 3, col = (c & 7) * 8;
-      const int n = n0 + row, m = m0 + row;
-      rw[i] = (n < N) ? *reinterpret_cast<const u32x4*>(W + (size_t)n * K + kbase + col)
-                      : u32x4{0, 0, 0, 0};
-      rx[i] = (m < M) ? *reinterpret_cast<const u32x4*>(X + (size_t)m * lda + kbase + col)
-                      : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto lstore = [&](int buf) {
-    uint16_t* ws = glds + buf * (BG_N + BG_M) * BG_K;
-    uint16_t* xs = ws + BG_N * BG_K;
+    for (int i = 0; i < G_LPO; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_void*)(st + (i * G_WAVES + wave) * 512),
+                                               16, voW + i * stepW, so, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 3, ch = c & 7;
-      *reinterpret_cast<u32x4*>(ws + swz(row, ch)) = rw[i];
-      *reinterpret_cast<u32x4*>(xs + swz(row, ch)) = rx[i];
-    }
+    for (int i = 0; i < G_LPO; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rX, (lds_void*)(st + G_N * G_K + (i * G_WAVES + wave) * 512), 16, voX + i * stepX, so,
+          0, 0);
   };
 
-  f32x16 acc[4][4];
+  // Fragment of step s (16 k): lane l reads row (l & 31) of a 32-row block, chunk 2s + (l >> 5).
+  const int rowA = (wn * G_TN + frow) * 128;
+  const int rowB = (G_N + wm * G_TM + frow) * 128;
+  int xo[4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int s = 0; s < 4; ++s) xo[s] = ((2 * s + g) ^ ((lane >> 1) & 7)) << 4;
+  auto read_frags = [&](const uint16_t* st, int s, u32x4 (&fa)[G_NA], u32x4 (&fb)[G_NB]) {
+    const char* base = reinterpret_cast<const char*>(st);
+    // in the order the MFMAs consume them
+    fa[0] = *reinterpret_cast<const u32x4*>(base + rowA + xo[s]);
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < G_NB; ++b)
+      fb[b] = *reinterpret_cast<const u32x4*>(base + rowB + b * 4096 + xo[s]);
+#pragma unroll
+    for (int a = 1; a < G_NA; ++a)
+      fa[a] = *reinterpret_cast<const u32x4*>(base + rowA + a * 4096 + xo[s]);
+  };
+
+  f32x16 acc[G_NA][G_NB];
+#pragma unroll
+  for (int a = 0; a < G_NA; ++a)
+#pragma unroll
+    for (int b = 0; b < G_NB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-
-  const int nk = K / BG_K;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  const int frow = lane & 31;
-  const int g = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint16_t* ws = glds + buf * (BG_N + BG_M) * BG_K;
-    const uint16_t* xs = ws + BG_N * BG_K;
+  auto mm = [&](const u32x4 (&fa)[G_NA], const u32x4 (&fb)[G_NB]) {
 #pragma unroll
-    for (int s = 0; s < BG_K / 16; ++s) {
-      u32x4 fa[4], fb[4];
+    for (int a = 0; a < G_NA; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int rn = wn * 128 + b * 32 + frow;
-        const int rm = wm * 128 + b * 32 + frow;
-        fa[b] = *reinterpret_cast<const u32x4*>(ws + swz(rn, 2 * s + g));
-        fb[b] = *reinterpret_cast<const u32x4*>(xs + swz(rm, 2 * s + g));
-      }
+      for (int b = 0; b < G_NB; ++b) acc[a][b] = mfma32x32x16<T>(fa[a], fb[b], acc[a][b]);
+  };
+  // Interleave the next step's fragment reads with the current step's MFMAs.
+  auto sched = [&]() {
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = mfma32x32x16<T>(fa[a], fb[b], acc[a][b]);
+    for (int q = 0; q < G_NA + G_NB; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
-  }
+    __builtin_amdgcn_sched_group_barrier(0x008, G_NA * G_NB - G_NA - G_NB, 0);
+  };
 
+  const int nk = K / G_K;
+  u32x4 fa0[G_NA], fb0[G_NB], fa1[G_NA], fb1[G_NB];
+  load_tile(0, s0);
+  if (nk > 1) {
+    load_tile(1, s1);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * G_LPO));  // vmcnt(2 * G_LPO): tile 0 has landed
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  }
+  __syncthreads();
+  read_frags(s0, 0, fa0, fb0);
+
+  // One k tile.  `loads` / `next` are compile-time flags so that the loop body has no branch
+  // (the scheduling barriers only act inside one basic block).
+  auto body = [&](int kt, auto loads, auto next) {
+    uint16_t* cur = (kt & 1) ? s1 : s0;
+    uint16_t* nxt = (kt & 1) ? s0 : s1;
+    read_frags(cur, 1, fa1, fb1); mm(fa0, fb0); sched();
+    read_frags(cur, 2, fa0, fb0); mm(fa1, fb1); sched();
+    read_frags(cur, 3, fa1, fb1); mm(fa0, fb0); sched();
+    if constexpr (decltype(next)::value) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // this wavefront's loads of tile kt + 1 have landed
+      __syncthreads();                     // ... everyone's, and tile kt is no longer read
+      if constexpr (decltype(loads)::value) load_tile(kt + 2, cur);
+      read_frags(nxt, 0, fa0, fb0);
+    }
+    mm(fa1, fb1);
+    if constexpr (decltype(next)::value) sched();
+  };
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) body(kt, std::true_type{}, std::true_type{});
+  if (kt + 1 < nk) {
+    body(kt, std::false_type{}, std::true_type{});
+    ++kt;
+  }
+  body(kt, std::false_type{}, std::false_type{});
+
+  // Epilogue, one 32-row block of the wavefront at a time: (acc + bias) as fp32 into the
+  // wavefront's 8 KB of LDS (row r, 16-byte chunk c at slot c ^ (r & 15)), then read back by rows.
+  float* ep = reinterpret_cast<float*>(s0) + wave * (32 * 64);
+  const int nw = n0 + wn * G_TN;  // first output column of the wavefront
+  const bool cols_ok = nw < N;    // N % 64 == 0: the wavefront's 64 columns are all in or out
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int m = m0 + wm * 128 + b * 32 + frow;
-    if (m >= M) continue;
+  for (int b = 0; b < G_NB; ++b) {
+    __syncthreads();
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    for (int a = 0; a < G_NA; ++a)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wn * 128 + a * 32 + j * 8 + g * 4;
-        if (n >= N) continue;
-        const float4 bb = *reinterpret_cast<const float4*>(bias + n);
-        float4 v4 = make_float4(acc[a][b][4 * j + 0] + bb.x, acc[a][b][4 * j + 1] + bb.y,
-                                acc[a][b][4 * j + 2] + bb.z, acc[a][b][4 * j + 3] + bb.w);
-        store4<T, EPI>(C, residual, (size_t)m * ldc + n, v4);
+        const int c = a * 8 + 2 * j + g;  // columns 4c .. 4c + 3 of the wavefront
+        const float4 bb = cols_ok ? *reinterpret_cast<const float4*>(bias + nw + 4 * c)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4*>(ep + frow * 64 + ((c ^ (frow & 15)) << 2)) =
+            make_float4(acc[a][b][4 * j] + bb.x, acc[a][b][4 * j + 1] + bb.y,
+                        acc[a][b][4 * j + 2] + bb.z, acc[a][b][4 * j + 3] + bb.w);
+      }
+    __syncthreads();
+    if (!cols_ok) continue;
+    const int mb = m0 + wm * G_TM + b * 32;
+    if constexpr (EPI == EPI_BIAS_RESIDUAL) {
+      // fp32 rows of 64 columns: 16 lanes per row, 4 rows per instruction.  All residual loads
+      // are issued before the first store.
+      float4 res[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int m = mb + (lane >> 4) + 4 * q;
+        res[q] = m < M ? *reinterpret_cast<const float4*>(residual + (size_t)m * ldc + nw +
+                                                          4 * (lane & 15))
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int r = (lane >> 4) + 4 * q, c = lane & 15;
+        const int m = mb + r;
+        const float4 v4 = *reinterpret_cast<const float4*>(ep + r * 64 + ((c ^ (r & 15)) << 2));
+        if (m < M)
+          *reinterpret_cast<float4*>(static_cast<float*>(C) + (size_t)m * ldc + nw + 4 * c) =
+              make_float4(res[q].x + v4.x, res[q].y + v4.y, res[q].z + v4.z, res[q].w + v4.w);
+      }
+    } else {
+      // 16-bit rows of 64 columns (128 bytes): 8 lanes per row, 8 rows per instruction.
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = (lane >> 3) + 8 * q, c0 = 2 * (lane & 7);
+        const int m = mb + r;
+        float4 v0 = *reinterpret_cast<const float4*>(ep + r * 64 + ((c0 ^ (r & 15)) << 2));
+        float4 v1 = *reinterpret_cast<const float4*>(ep + r * 64 + (((c0 + 1) ^ (r & 15)) << 2));
+        if constexpr (EPI == EPI_BIAS_GELU) {
+          v0 = make_float4(gelu_erf_as(v0.x), gelu_erf_as(v0.y), gelu_erf_as(v0.z), gelu_erf_as(v0.w));
+          v1 = make_float4(gelu_erf_as(v1.x), gelu_erf_as(v1.y), gelu_erf_as(v1.z), gelu_erf_as(v1.w));
+        }
+        const u32x4 w4 = {pack2<T>(v0.x, v0.y), pack2<T>(v0.z, v0.w), pack2<T>(v1.x, v1.y),
+                          pack2<T>(v1.z, v1.w)};
+        if (m < M)
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(C) + (size_t)m * ldc + nw + 4 * c0) = w4;
       }
     }
   }
 }
+
+constexpr int GB_N = 128;  // W rows (output columns) per tile
+constexpr int GB_M = 128;  // X rows per tile
 
 // fp32-operand fallback: same tiling with a 32-wide k tile of fp32 (128 bytes per row) and
 // v_mfma_f32_32x32x2_f32.  Two consecutive k of a lane feed two MFMAs, so each fragment read
@@ -395,39 +379,19 @@ __global__ __launch_bounds__(256) void gemm32_kernel(const float* __restrict__ X
   }
 }
 
-constexpr size_t BG_LDS_BYTES = 2 * (BG_N + BG_M) * BG_K * sizeof(uint16_t);
-
 template <typename T, int EPI>
 static void launch16_epi(const uint16_t* X, int lda, const uint16_t* W, const float* bias,
                          const float* residual, void* c, int ldc, int m, int n, int k,
                          hipStream_t st) {
-  const long big_tiles = (long)((m + BG_M - 1) / BG_M) * ((n + BG_N - 1) / BG_N);
-  if (big_tiles >= 384) {
-    gemm16_big_kernel<T, EPI><<<dim3((unsigned)big_tiles), dim3(256), BG_LDS_BYTES, st>>>(
-        X, lda, W, bias, residual, c, ldc, m, n, k);
-  } else {
-    dim3 grid((n + GB_N - 1) / GB_N, (m + GB_M - 1) / GB_M), block(256);
-    gemm16_kernel<T, EPI><<<grid, block, 0, st>>>(X, lda, W, bias, residual, c, ldc, m, n, k);
-  }
+  const int tiles = ((m + G_M - 1) / G_M) * ((n + G_N - 1) / G_N);
+  gemm16_kernel<T, EPI><<<dim3((unsigned)tiles), dim3(G_THREADS), 0, st>>>(X, lda, W, bias,
+                                                                          residual, c, ldc, m, n, k);
 }
 
 template <typename T>
 static hipError_t launch16(const void* a, int lda, const void* w, const float* bias,
                            const float* residual, void* c, int ldc, int m, int n, int k, int epi,
                            hipStream_t st) {
-  // Dynamic LDS beyond 64 KiB needs an explicit opt-in, once per kernel instantiation.
-  static const hipError_t attr = [] {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm16_big_kernel<T, EPI_BIAS>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)BG_LDS_BYTES);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)gemm16_big_kernel<T, EPI_BIAS_GELU>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)BG_LDS_BYTES);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)gemm16_big_kernel<T, EPI_BIAS_RESIDUAL>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)BG_LDS_BYTES);
-    return e;
-  }();
-  if (attr != hipSuccess) return attr;
   auto X = static_cast<const uint16_t*>(a);
   auto W = static_cast<const uint16_t*>(w);
   switch (epi) {

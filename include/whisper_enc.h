@@ -43,7 +43,8 @@ extern "C" {
 /* Status codes. */
 #define WENC_OK 0
 #define WENC_ERR_ARG 1         /* NULL pointer, misaligned pointer, bad size or enum value   */
-#define WENC_ERR_UNSUPPORTED 2 /* valid model shape the kernels do not implement (hd != 64) */
+#define WENC_ERR_UNSUPPORTED 2 /* valid shape the kernels do not implement: hd != 64, or one  */
+                               /* window's QKV rows (t * 3 d_model elements) >= 2 GiB        */
 #define WENC_ERR_WORKSPACE 3   /* workspace_bytes below whisper_enc_workspace_bytes()       */
 #define WENC_ERR_HIP 4         /* HIP reported an error for a launch                         */
 
@@ -158,6 +159,7 @@ int whisper_enc_linear(const void* a, const void* w, const float* bias, const fl
  * VANILLA_ATTN): row i of window b is at ptr + (b*t + i) * ld; head h occupies columns
  * 64h .. 64h+63.  q, k, v use row stride ld_qkv, o uses ld_o (elements, multiples of 8, at least
  * 64*heads); all in the path's operand type.  o = softmax(q k^T / 8) v per (window, head).
+ * t * ld_qkv elements of one window must span less than 2 GiB (else WENC_ERR_UNSUPPORTED).
  */
 int whisper_enc_attention(const void* q, const void* k, const void* v, void* o, int batch, int t,
                           int heads, int ld_qkv, int ld_o, int path, void* stream);

@@ -74,6 +74,9 @@ int check_shape(int batch, int t, int d, int heads, int f, int path) {
   if (!valid_dims(d, f)) return WENC_ERR_ARG;
   if (d % heads != 0) return WENC_ERR_ARG;
   if (d / heads != WENC_HEAD_DIM) return WENC_ERR_UNSUPPORTED;
+  // One window's QKV rows must span less than 2 GiB: the attention kernel addresses them with
+  // 32-bit buffer offsets.
+  if ((size_t)t * 3 * d * elem_bytes(path) > (size_t)INT32_MAX) return WENC_ERR_UNSUPPORTED;
   return WENC_OK;
 }
 
@@ -299,6 +302,7 @@ int whisper_enc_attention(const void* q, const void* k, const void* v, void* o, 
   if (heads * WENC_HEAD_DIM > WENC_MAX_FFN_DIM) return WENC_ERR_ARG;
   if (ld_qkv < heads * WENC_HEAD_DIM || ld_o < heads * WENC_HEAD_DIM || ld_qkv % 8 || ld_o % 8)
     return WENC_ERR_ARG;
+  if ((size_t)t * ld_qkv * elem_bytes(path) > (size_t)INT32_MAX) return WENC_ERR_UNSUPPORTED;
   if ((size_t)batch * t == 0) return WENC_OK;
   if (!q || !k || !v || !o) return WENC_ERR_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return WENC_ERR_ARG;

@@ -3,23 +3,33 @@
 // For each window and head: s_ij = (q_i . k_j) * hd^-0.5 over every key j of the window (no mask,
 // no positional term), softmax over j, o_i = sum_j p_ij v_j (inferencelayer whisper_gpu.rs,
 // VANILLA_ATTN; turbospark-runtime whisper/metal.rs, encode_layer).  As in the pages' online
-// form, keys are visited tile by tile with a running max m and running denominator l: each tile
-// rescales the previous state by exp(m_old - m_new).  The t x t scores never reach memory.
+// form, keys are visited tile by tile with a running max m and running denominator l, and the
+// accumulated state is rescaled by exp(m_old - m_new) when m moves.  The t x t scores never reach
+// memory.
 //
 // gfx950 mapping.  One 256-thread workgroup per (128 query rows, head, window); wavefront w owns
-// 32 query rows.  Keys go in tiles of 64, double-buffered in LDS.  The scores are computed
-// transposed, S^T = K . Q^T, with v_mfma_f32_32x32x16: lane l then holds 32 scores of one query
-// (l % 32), so the row max and sum are 31 in-register operations plus one exchange with lane
-// l ^ 32 (v_permlane32_swap), and the running (m, l) of a query live in one lane's registers.
-// The probabilities stay in registers and feed O^T = V^T . P^T directly as the MFMA's B
-// operand: the 8 keys a lane contributes per MFMA step are exactly the 8 score registers it
-// already holds, provided V^T is laid out with the same key order.  The V tile is therefore
-// transposed into LDS as [dim][key] with keys permuted inside each group of 16
-// (0-3, 8-11, 4-7, 12-15), which makes every A-operand fragment one 16-byte LDS read.
-// Scores are scaled by hd^-0.5 * log2(e) so the exponentials are v_exp_f32 (exp2).
+// 32 queries.  Keys go in tiles of 64 through three LDS stages, each a K tile and a V tile of
+// 64 rows x 128 bytes, loaded global -> LDS directly (buffer_load_dwordx4 ... lds, range-checked
+// so that keys past t read as zeros) two tiles ahead of their use.  Chunk c (16 bytes) of row r
+// sits at slot c ^ f(r), f chosen per tile so that the 16-lane phases of its reads hit distinct
+// banks.  The scores are computed transposed, S^T = K . Q^T, with v_mfma_f32_32x32x16: lane l
+// then holds 32 scores of one query (l % 32), so the row max is in-register plus one exchange
+// with lane l ^ 32 (v_permlane32_swap), and (m, l) of a query live in one lane's registers.  The
+// probabilities stay in registers and feed O^T = V^T . P^T as the MFMA's B operand; the V^T
+// fragments come straight from the row-major V tile with ds_read_b64_tr_b16 (within each group
+// of 16 lanes, lane i receives element i & 3 of the 8-byte rows addressed by lanes 4s + (i >> 2),
+// s = 0..3), so V is never transposed in memory.  The row sums are taken from the rounded
+// probabilities the MFMA consumes (v_dot2 against (1, 1)), so the numerator and denominator see
+// the same values.
 //
-// The fp32 variant keeps the same structure with v_mfma_f32_32x32x2_f32; with one k per lane
-// it reads V in its natural [key][dim] layout.
+// Scores are scaled by hd^-0.5 * log2(e) so the exponentials are v_exp_f32 (exp2).  The running
+// max used for the exponent is only raised when a tile's max exceeds it by more than 8 (log2
+// units): the probabilities are then bounded by 2^8, the same in both the numerator and the
+// denominator, and the O rescale runs only on the few tiles that raise it (a wave-uniform branch)
+// instead of on every tile.  The result is the same softmax up to rounding.
+//
+// The fp32 variant keeps the score layout with v_mfma_f32_32x32x2_f32; with one k per lane it
+// reads V in its natural [key][dim] layout.
 #include "wenc_device.h"
 #include "wenc_internal.h"
 
@@ -27,106 +37,138 @@ namespace wenc {
 
 constexpr int AQ = 128;   // query rows per workgroup
 constexpr int AK = 64;    // keys per tile
-constexpr int ALDS = 72;  // LDS row stride (16-bit elements) for K [key][dim] and V^T [dim][key]
+constexpr int ASTAGES = 3;  // LDS stages (tiles in flight)
+constexpr int ATILE = AK * 64;  // 16-bit elements of one K or V tile
+constexpr float RESCALE_SLACK = 8.0f;  // log2 units the running max may lag a tile's max
 
-__device__ __forceinline__ int vt_pos(int r) {  // key r (0..15) -> position inside its 16-group
-  return (r & 3) | (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 2);
-}
+typedef __attribute__((address_space(3))) void lds_void_a;
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+template <typename T> struct RowSum;
+template <> struct RowSum<f16_t> {
+  static __device__ __forceinline__ float add(uint32_t p2, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p2), one, acc, false);
+  }
+};
+template <> struct RowSum<bf16_t> {
+  static __device__ __forceinline__ float add(uint32_t p2, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p2), one, acc, false);
+  }
+};
 
 template <typename T>
-__global__ __launch_bounds__(256) void attn16_kernel(const uint16_t* __restrict__ Q,
-                                                     const uint16_t* __restrict__ Kp,
-                                                     const uint16_t* __restrict__ Vp, int ld,
-                                                     uint16_t* __restrict__ O, int ldo, int t,
-                                                     float c) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][AK * ALDS];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[2][64 * ALDS];
+__global__ __launch_bounds__(256, 2) void attn16_kernel(const uint16_t* __restrict__ Q,
+                                                        const uint16_t* __restrict__ Kp,
+                                                        const uint16_t* __restrict__ Vp, int ld,
+                                                        uint16_t* __restrict__ O, int ldo, int t,
+                                                        float c) {
+  // Stages as separate arrays: the compiler then sees that the loads into one stage never alias
+  // the fragment reads of another and does not wait for them.
+  __shared__ __attribute__((aligned(1024))) uint16_t st0[2 * ATILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st1[2 * ATILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st2[2 * ATILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int g = lane >> 5;
+  const int frow = lane & 31;
   const int wave = tid >> 6;
   const int h = blockIdx.y;
   const size_t win = (size_t)blockIdx.z * t;  // first row of this window
   const int col0 = h * 64;
 
   // Query fragments: B operand of S^T, lane holds q = lane%32, dims 16s + 8g .. +7.
-  const int qi = blockIdx.x * AQ + wave * 32 + (lane & 31);
+  const int qi = blockIdx.x * AQ + wave * 32 + frow;
   u32x4 qf[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
     qf[s] = (qi < t) ? *reinterpret_cast<const u32x4*>(Q + (win + qi) * ld + col0 + s * 16 + g * 8)
                      : u32x4{0, 0, 0, 0};
 
-  // Tile loaders.  K: 2 chunks of 16 bytes per thread.  V: keys (2kp, 2kp+1), dims 8dc..8dc+7.
-  u32x4 rk[2], rv[2];
-  const int kp = tid >> 3, dc = tid & 7;
-  auto gload = [&](int j0) {
+  // K and V: the window's rows of this head; rows at or past t read as zeros.  The whole offset
+  // (key row included) is in the range-checked VGPR offset.
+  const int nrec = (t - 1) * ld * 2 + 128;
+  const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Kp + win * ld + col0), (short)0, nrec, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Vp + win * ld + col0), (short)0, nrec, 0x00020000);
+  // Load instruction i of wavefront w fills rows 8 (2w + i) .. + 7 of a tile: lane l writes row
+  // r = 16w + 8i + (l >> 3), slot (l & 7), which holds chunk (l & 7) ^ f(r).
+  //   K: f(r) = (r >> 1) & 7  (32 x 16-byte fragment reads)
+  //   V: f(r) = ((r >> 1) & 1) << 2  (8-byte transposing reads of 4 rows x 4 chunks)
+  int kvo[2], vvo[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int cidx = tid + 256 * i;
-      const int key = j0 + (cidx >> 3);
-      rk[i] = (key < t) ? *reinterpret_cast<const u32x4*>(Kp + (win + key) * ld + col0 + (cidx & 7) * 8)
-                        : u32x4{0, 0, 0, 0};
-    }
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * wave + 8 * i + (lane >> 3);
+    kvo[i] = r * ld * 2 + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+    vvo[i] = r * ld * 2 + (((lane & 7) ^ (((r >> 1) & 1) << 2)) << 4);
+  }
+  auto load_tile = [&](int j0, uint16_t* st) {
+    const int ro = j0 * ld * 2;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int key = j0 + 2 * kp + i;
-      rv[i] = (key < t) ? *reinterpret_cast<const u32x4*>(Vp + (win + key) * ld + col0 + dc * 8)
-                        : u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_void_a*)(st + (2 * wave + i) * 512), 16,
+                                               kvo[i] + ro, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rV, (lds_void_a*)(st + ATILE + (2 * wave + i) * 512), 16, vvo[i] + ro, 0, 0, 0);
   };
-  auto lstore = [&](int buf) {
+
+  // K fragment of dims 16s + 8g .. + 7 for key row (mb * 32 + frow).
+  const int xk = (lane >> 1) & 7;
+  // V^T fragment source address for (kstep, db, jj): this lane's 8-byte row piece is key
+  // 16 kstep + 8 jj + 4 g + s, dims db * 32 + 16 (q & 1) + 4 u  (q = lane >> 4, s, u from lane).
+  const int vq = (lane >> 4) & 1, vs = (lane >> 2) & 3, vu = lane & 3;
+  int vro[2][2];  // byte offset inside the V tile for kstep 0, [jj][db]
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int cidx = tid + 256 * i;
-      *reinterpret_cast<u32x4*>(&ks[buf][(cidx >> 3) * ALDS + (cidx & 7) * 8]) = rk[i];
-    }
-    const int kk = 2 * kp;
-    const int pos = (kk & ~15) + vt_pos(kk & 15);
+  for (int jj = 0; jj < 2; ++jj) {
+    const int key = 8 * jj + 4 * g + vs;  // + 16 kstep: does not change ((key >> 1) & 1)
+    const int fbit = (key >> 1) & 1;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      // dims 8dc + 2e and 8dc + 2e + 1: pair the two keys' values of each dim.
-      const uint32_t a = rv[0][e], b = rv[1][e];
-      const uint32_t lo = (a & 0xffffu) | (b << 16);
-      const uint32_t hi = (a >> 16) | (b & 0xffff0000u);
-      *reinterpret_cast<uint32_t*>(&vt[buf][(dc * 8 + 2 * e) * ALDS + pos]) = lo;
-      *reinterpret_cast<uint32_t*>(&vt[buf][(dc * 8 + 2 * e + 1) * ALDS + pos]) = hi;
+    for (int db = 0; db < 2; ++db) {
+      // chunk 2 vq + (vu >> 1) + 4 db, at slot chunk ^ (fbit << 2)
+      const int slot = 2 * vq + (vu >> 1) + 4 * (db ^ fbit);
+      vro[jj][db] = key * 128 + slot * 16 + (vu & 1) * 8;
     }
-  };
+  }
 
   f32x16 oacc[2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[a][r] = 0.f;
-  float m_run = -INFINITY;  // running max of s * c
+  float m_run = -INFINITY;  // max used in the exponents (scaled units), per query
   float l_part = 0.f;       // this lane's share of the running denominator
 
   const int ntiles = (t + AK - 1) / AK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  load_tile(0, st0);
+  if (ntiles > 1) load_tile(AK, st1);
 
-  const int frow = lane & 31;
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
+  // One key tile from stage `cur`; the tile two ahead is loaded into stage `ahead`.
+  auto tile = [&](int it, const uint16_t* cur, uint16_t* ahead) {
     const int j0 = it * AK;
-    if (it + 1 < ntiles) gload(j0 + AK);
+    // Tile it has landed (this wavefront's loads: only tile it + 1 may still be in flight),
+    // and every wavefront is done with tile it - 1, whose stage is `ahead`.
+    if (it + 1 < ntiles)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 4);  // vmcnt(4)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (it + 2 < ntiles) load_tile(j0 + 2 * AK, ahead);
 
     // S^T = K . Q^T for 64 keys x 32 queries.
     f32x16 sacc[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[mb][r] = 0.f;
+    const char* kbase = reinterpret_cast<const char*>(cur);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const u32x4 ka =
-            *reinterpret_cast<const u32x4*>(&ks[buf][(mb * 32 + frow) * ALDS + s * 16 + g * 8]);
-        sacc[mb] = mfma32x32x16<T>(ka, qf[s], sacc[mb]);
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(kbase + (mb * 32 + frow) * 128 +
+                                                         (((2 * s + g) ^ xk) << 4));
+        sacc[mb] = mfma32x32x16<T>(ka, qf[s], s == 0 ? f32x16{} : sacc[mb]);
       }
     }
     if (j0 + AK > t) {  // last tile: keys past the window get no weight
@@ -142,45 +184,57 @@ __global__ __launch_bounds__(256) void attn16_kernel(const uint16_t* __restrict_
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
-    mx = halves_max(mx);
-    const float m_new = fmaxf(m_run, mx * c);
-    const float corr = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
+      for (int r = (mb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
+    mx = halves_max(mx) * c;
+    // Raise the exponent's max only when this tile would push probabilities past 2^8.
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_SLACK)) {
+      const float m_new = mx > m_run + RESCALE_SLACK ? mx : m_run;
+      const float corr = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_part *= corr;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(sacc[mb][r], c, -m_new));
-        sacc[mb][r] = p;
-        psum += p;
-      }
-    l_part = l_part * corr + psum;
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[a][r] *= corr;
-
-    // O^T += V^T . P^T, 4 steps of 16 keys.
+        for (int r = 0; r < 16; ++r) oacc[a][r] *= corr;
+    }
+    u32x4 pb[4];
 #pragma unroll
     for (int kstep = 0; kstep < 4; ++kstep) {
       const int mb = kstep >> 1, js = kstep & 1;
-      u32x4 pb;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        pb[e] = pack2<T>(sacc[mb][8 * js + 2 * e], sacc[mb][8 * js + 2 * e + 1]);
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        const u32x4 va =
-            *reinterpret_cast<const u32x4*>(&vt[buf][(db * 32 + frow) * ALDS + kstep * 16 + g * 8]);
-        oacc[db] = mfma32x32x16<T>(va, pb, oacc[db]);
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = fast_exp2(fmaf(sacc[mb][8 * js + 2 * e], c, -m_run));
+        const float p1 = fast_exp2(fmaf(sacc[mb][8 * js + 2 * e + 1], c, -m_run));
+        pb[kstep][e] = pack2<T>(p0, p1);
+        l_part = RowSum<T>::add(pb[kstep][e], l_part);
       }
     }
 
-    if (it + 1 < ntiles) lstore(buf ^ 1);
-    __syncthreads();
+    // O^T += V^T . P^T, 4 steps of 16 keys; V^T fragments by transposing reads.
+    const uint16_t* vtile = cur + ATILE;
+#pragma unroll
+    for (int kstep = 0; kstep < 4; ++kstep) {
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const int off = kstep * 16 * 128;  // 16 keys per step
+        const short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4_t*)(vtile + (vro[0][db] + off) / 2));
+        const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4_t*)(vtile + (vro[1][db] + off) / 2));
+        const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+        const u32x4 va = {w0[0], w0[1], w1[0], w1[1]};
+        oacc[db] = mfma32x32x16<T>(va, pb[kstep], oacc[db]);
+      }
+    }
+  };
+  int it = 0;
+  for (; it + 3 <= ntiles; it += 3) {
+    tile(it, st0, st2);
+    tile(it + 1, st1, st0);
+    tile(it + 2, st2, st1);
   }
+  if (it < ntiles) tile(it, st0, st2);
+  if (it + 1 < ntiles) tile(it + 1, st1, st0);
 
   const float inv = 1.0f / halves_sum(l_part);
   if (qi < t) {

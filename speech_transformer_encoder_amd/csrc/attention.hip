@@ -7,26 +7,27 @@
 // accumulated state is rescaled by exp(m_old - m_new) when m moves.  The t x t scores never reach
 // memory.
 //
-// gfx950 mapping.  One 256-thread workgroup per (128 query rows, head, window); wavefront w owns
+// gfx950 mapping.  One 512-thread workgroup per (256 query rows, head, window); wavefront w owns
 // 32 queries.  Keys go in tiles of 64 through three LDS stages, each a K tile and a V tile of
 // 64 rows x 128 bytes, loaded global -> LDS directly (buffer_load_dwordx4 ... lds, range-checked
 // so that keys past t read as zeros) two tiles ahead of their use.  Chunk c (16 bytes) of row r
 // sits at slot c ^ f(r), f chosen per tile so that the 16-lane phases of its reads hit distinct
 // banks.  The scores are computed transposed, S^T = K . Q^T, with v_mfma_f32_32x32x16: lane l
-// then holds 32 scores of one query (l % 32), so the row max is in-register plus one exchange
-// with lane l ^ 32 (v_permlane32_swap), and (m, l) of a query live in one lane's registers.  The
-// probabilities stay in registers and feed O^T = V^T . P^T as the MFMA's B operand; the V^T
-// fragments come straight from the row-major V tile with ds_read_b64_tr_b16 (within each group
-// of 16 lanes, lane i receives element i & 3 of the 8-byte rows addressed by lanes 4s + (i >> 2),
-// s = 0..3), so V is never transposed in memory.  The row sums are taken from the rounded
-// probabilities the MFMA consumes (v_dot2 against (1, 1)), so the numerator and denominator see
-// the same values.
+// then holds 32 scores of one query (l % 32), and (m, l) of a query live in one lane's
+// registers.  The probabilities stay in registers and feed O^T = V^T . P^T as the MFMA's B
+// operand; the V^T fragments come straight from the row-major V tile with ds_read_b64_tr_b16
+// (within each group of 16 lanes, lane i receives element i & 3 of the 8-byte rows addressed by
+// lanes 4s + (i >> 2), s = 0..3), so V is never transposed in memory.  The row sums are taken
+// from the rounded probabilities the MFMA consumes (v_dot2 against (1, 1)), so the numerator and
+// denominator see the same values.
 //
-// Scores are scaled by hd^-0.5 * log2(e) so the exponentials are v_exp_f32 (exp2).  The running
-// max used for the exponent is only raised when a tile's max exceeds it by more than 8 (log2
-// units): the probabilities are then bounded by 2^8, the same in both the numerator and the
-// denominator, and the O rescale runs only on the few tiles that raise it (a wave-uniform branch)
-// instead of on every tile.  The result is the same softmax up to rounding.
+// Scores are scaled by hd^-0.5 * log2(e) so the exponentials are v_exp_f32 (exp2).  A tile is
+// first exponentiated against the running max m as it stands: when every probability of a lane
+// stays below 2^15 (checked through the lane's sum of them, which bounds each term), m is kept
+// and no per-tile max is needed.  Otherwise (the first tile, or a score more than ~10 log2 units
+// above m) the tile's true max is taken, m is raised, the running state is rescaled by
+// exp2(m_old - m_new) and the tile is exponentiated again.  Both cases compute the same softmax up
+// to rounding; the rescale and the max run only on the few tiles that need them.
 //
 // The fp32 variant keeps the score layout with v_mfma_f32_32x32x2_f32; with one k per lane it
 // reads V in its natural [key][dim] layout.
@@ -35,11 +36,10 @@
 
 namespace wenc {
 
-constexpr int AQ = 128;   // query rows per workgroup
+constexpr int AQ = 256;   // query rows per workgroup (8 wavefronts)
 constexpr int AK = 64;    // keys per tile
-constexpr int ASTAGES = 3;  // LDS stages (tiles in flight)
 constexpr int ATILE = AK * 64;  // 16-bit elements of one K or V tile
-constexpr float RESCALE_SLACK = 8.0f;  // log2 units the running max may lag a tile's max
+constexpr float P_BOUND = 32768.0f;  // largest probability kept without raising the max (2^15)
 
 typedef __attribute__((address_space(3))) void lds_void_a;
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -58,14 +58,32 @@ template <> struct RowSum<bf16_t> {
   }
 };
 
+// Global -> LDS copy of 16 bytes per lane (lane i to lds_base + 16 i) from a range-checked buffer.
+// Written as inline assembly so that the compiler does not treat the copies in flight as
+// possible writers of every LDS read that follows (it would wait for all of them); the kernel
+// waits for them itself with s_waitcnt vmcnt before the barrier that publishes a tile.
+__device__ __forceinline__ void lds_copy16(u32x4 rsrc, uint32_t lds_base, int voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 template <typename T>
-__global__ __launch_bounds__(256, 2) void attn16_kernel(const uint16_t* __restrict__ Q,
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void attn16_kernel(const uint16_t* __restrict__ Q,
                                                         const uint16_t* __restrict__ Kp,
                                                         const uint16_t* __restrict__ Vp, int ld,
                                                         uint16_t* __restrict__ O, int ldo, int t,
                                                         float c) {
-  // Stages as separate arrays: the compiler then sees that the loads into one stage never alias
-  // the fragment reads of another and does not wait for them.
   __shared__ __attribute__((aligned(1024))) uint16_t st0[2 * ATILE];
   __shared__ __attribute__((aligned(1024))) uint16_t st1[2 * ATILE];
   __shared__ __attribute__((aligned(1024))) uint16_t st2[2 * ATILE];
@@ -74,7 +92,7 @@ __global__ __launch_bounds__(256, 2) void attn16_kernel(const uint16_t* __restri
   const int lane = tid & 63;
   const int g = lane >> 5;
   const int frow = lane & 31;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.y;
   const size_t win = (size_t)blockIdx.z * t;  // first row of this window
   const int col0 = h * 64;
@@ -86,39 +104,33 @@ __global__ __launch_bounds__(256, 2) void attn16_kernel(const uint16_t* __restri
   for (int s = 0; s < 4; ++s)
     qf[s] = (qi < t) ? *reinterpret_cast<const u32x4*>(Q + (win + qi) * ld + col0 + s * 16 + g * 8)
                      : u32x4{0, 0, 0, 0};
+  // Wait for the query fragments here, once, and hand them to the loop as plain register values
+  // (otherwise the wait for them lands inside the key loop and stalls on the tile copies).
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+#pragma unroll
+  for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(qf[s]));
 
   // K and V: the window's rows of this head; rows at or past t read as zeros.  The whole offset
-  // (key row included) is in the range-checked VGPR offset.
-  const int nrec = (t - 1) * ld * 2 + 128;
-  const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(Kp + win * ld + col0), (short)0, nrec, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(Vp + win * ld + col0), (short)0, nrec, 0x00020000);
-  // Load instruction i of wavefront w fills rows 8 (2w + i) .. + 7 of a tile: lane l writes row
-  // r = 16w + 8i + (l >> 3), slot (l & 7), which holds chunk (l & 7) ^ f(r).
-  //   K: f(r) = (r >> 1) & 7  (32 x 16-byte fragment reads)
-  //   V: f(r) = ((r >> 1) & 1) << 2  (8-byte transposing reads of 4 rows x 4 chunks)
-  int kvo[2], vvo[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 16 * wave + 8 * i + (lane >> 3);
-    kvo[i] = r * ld * 2 + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
-    vvo[i] = r * ld * 2 + (((lane & 7) ^ (((r >> 1) & 1) << 2)) << 4);
-  }
-  auto load_tile = [&](int j0, uint16_t* st) {
+  // (key row included) is in the range-checked VGPR offset.  Wavefront w copies rows
+  // 8w .. 8w + 7 of each tile: lane l row r = 8w + (l >> 3), slot (l & 7), which holds chunk
+  // (l & 7) ^ f(r):
+  //   K: f(r) = (r >> 1) & 7           (32-row x 16-byte fragment reads)
+  //   V: f(r) = ((r >> 1) & 1) << 2    (8-byte transposing reads of 4 rows x 4 chunks)
+  const uint32_t nrec = (uint32_t)((t - 1) * ld * 2 + 128);
+  const u32x4 rK = buffer_rsrc(Kp + win * ld + col0, nrec);
+  const u32x4 rV = buffer_rsrc(Vp + win * ld + col0, nrec);
+  const int lr = 8 * wave + (lane >> 3);
+  const int kvo = lr * ld * 2 + (((lane & 7) ^ ((lr >> 1) & 7)) << 4);
+  const int vvo = lr * ld * 2 + (((lane & 7) ^ (((lr >> 1) & 1) << 2)) << 4);
+  const uint32_t blk = (uint32_t)wave * 1024u;
+  auto load_tile = [&](int j0, const uint16_t* st) {
     const int ro = j0 * ld * 2;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_void_a*)(st + (2 * wave + i) * 512), 16,
-                                               kvo[i] + ro, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rV, (lds_void_a*)(st + ATILE + (2 * wave + i) * 512), 16, vvo[i] + ro, 0, 0, 0);
+    const uint32_t base = lds_addr(st) + blk;
+    lds_copy16(rK, base, kvo + ro);
+    lds_copy16(rV, base + ATILE * 2, vvo + ro);
   };
 
-  // K fragment of dims 16s + 8g .. + 7 for key row (mb * 32 + frow).
-  const int xk = (lane >> 1) & 7;
+  const int xk = (lane >> 1) & 7;  // K fragment-read swizzle of row (lane & 31)
   // V^T fragment source address for (kstep, db, jj): this lane's 8-byte row piece is key
   // 16 kstep + 8 jj + 4 g + s, dims db * 32 + 16 (q & 1) + 4 u  (q = lane >> 4, s, u from lane).
   const int vq = (lane >> 4) & 1, vs = (lane >> 2) & 3, vu = lane & 3;
@@ -148,12 +160,12 @@ __global__ __launch_bounds__(256, 2) void attn16_kernel(const uint16_t* __restri
   if (ntiles > 1) load_tile(AK, st1);
 
   // One key tile from stage `cur`; the tile two ahead is loaded into stage `ahead`.
-  auto tile = [&](int it, const uint16_t* cur, uint16_t* ahead) {
+  auto tile = [&](int it, const uint16_t* cur, const uint16_t* ahead) {
     const int j0 = it * AK;
-    // Tile it has landed (this wavefront's loads: only tile it + 1 may still be in flight),
+    // Tile it has landed (this wavefront's copies: only tile it + 1 may still be in flight),
     // and every wavefront is done with tile it - 1, whose stage is `ahead`.
     if (it + 1 < ntiles)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | 4);  // vmcnt(4)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 2);  // vmcnt(2)
     else
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
@@ -180,15 +192,35 @@ __global__ __launch_bounds__(256, 2) void attn16_kernel(const uint16_t* __restri
           if (key >= t) sacc[mb][r] = -INFINITY;
         }
     }
-    float mx = sacc[0][0];
+    // Probabilities against the current max, packed for the MFMA; tsum = this lane's sum.
+    u32x4 pb[4];
+    float tsum;
+    auto exponentiate = [&]() {
+      tsum = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int kstep = 0; kstep < 4; ++kstep) {
+        const int mb = kstep >> 1, js = kstep & 1;
 #pragma unroll
-      for (int r = (mb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
-    mx = halves_max(mx) * c;
-    // Raise the exponent's max only when this tile would push probabilities past 2^8.
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_SLACK)) {
-      const float m_new = mx > m_run + RESCALE_SLACK ? mx : m_run;
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(fmaf(sacc[mb][8 * js + 2 * e], c, -m_run));
+          const float p1 = fast_exp2(fmaf(sacc[mb][8 * js + 2 * e + 1], c, -m_run));
+          pb[kstep][e] = pack2<T>(p0, p1);
+          tsum = RowSum<T>::add(pb[kstep][e], tsum);
+        }
+      }
+    };
+    exponentiate();
+    if (__builtin_amdgcn_ballot_w64(!(tsum <= P_BOUND))) {
+      // Raise the max to the tile's (only for the queries whose probabilities ran past the
+      // bound), rescale the running state and exponentiate again.
+      float mx = sacc[0][0];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = (mb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
+      mx = halves_max(mx) * c;
+      const bool raise = !(halves_max(tsum) <= P_BOUND);
+      const float m_new = raise ? fmaxf(m_run, mx) : m_run;
       const float corr = fast_exp2(m_run - m_new);
       m_run = m_new;
       l_part *= corr;
@@ -196,19 +228,9 @@ __global__ __launch_bounds__(256, 2) void attn16_kernel(const uint16_t* __restri
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[a][r] *= corr;
+      exponentiate();
     }
-    u32x4 pb[4];
-#pragma unroll
-    for (int kstep = 0; kstep < 4; ++kstep) {
-      const int mb = kstep >> 1, js = kstep & 1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = fast_exp2(fmaf(sacc[mb][8 * js + 2 * e], c, -m_run));
-        const float p1 = fast_exp2(fmaf(sacc[mb][8 * js + 2 * e + 1], c, -m_run));
-        pb[kstep][e] = pack2<T>(p0, p1);
-        l_part = RowSum<T>::add(pb[kstep][e], l_part);
-      }
-    }
+    l_part += tsum;
 
     // O^T += V^T . P^T, 4 steps of 16 keys; V^T fragments by transposing reads.
     const uint16_t* vtile = cur + ATILE;
@@ -251,6 +273,7 @@ __global__ __launch_bounds__(256, 2) void attn16_kernel(const uint16_t* __restri
   }
 }
 
+constexpr int AQ32 = 128;  // query rows per workgroup of the fp32 kernel
 constexpr int AFLDS = 66;  // fp32 LDS row stride
 
 __global__ __launch_bounds__(256) void attn32_kernel(const float* __restrict__ Q,
@@ -270,7 +293,7 @@ __global__ __launch_bounds__(256) void attn32_kernel(const float* __restrict__ Q
   const int col0 = h * 64;
 
   // B operand of S^T: lane holds q = lane%32 and dims 4s + 2g, 4s + 2g + 1 for s = 0..15.
-  const int qi = blockIdx.x * AQ + wave * 32 + (lane & 31);
+  const int qi = blockIdx.x * AQ32 + wave * 32 + (lane & 31);
   float2 qf[16];
 #pragma unroll
   for (int s = 0; s < 16; ++s)
@@ -406,15 +429,16 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int ld_
                             hipStream_t st) {
   if (batch == 0 || t == 0) return hipSuccess;
   const float c = scale * 1.4426950408889634f;  // fold log2(e): exp(x) = exp2(x * log2 e)
-  dim3 grid((t + AQ - 1) / AQ, heads, batch), block(256);
+  dim3 grid16((t + AQ - 1) / AQ, heads, batch), block16(512);
+  dim3 grid((t + AQ32 - 1) / AQ32, heads, batch), block(256);
   switch (dtype) {
     case DT_BF16:
-      attn16_kernel<bf16_t><<<grid, block, 0, st>>>(
+      attn16_kernel<bf16_t><<<grid16, block16, 0, st>>>(
           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
           static_cast<const uint16_t*>(v), ld_qkv, static_cast<uint16_t*>(o), ld_o, t, c);
       break;
     case DT_F16:
-      attn16_kernel<f16_t><<<grid, block, 0, st>>>(
+      attn16_kernel<f16_t><<<grid16, block16, 0, st>>>(
           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
           static_cast<const uint16_t*>(v), ld_qkv, static_cast<uint16_t*>(o), ld_o, t, c);
       break;

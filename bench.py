@@ -42,6 +42,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-windows", type=int, default=16)
     ap.add_argument("--cpu-sample-layers", type=int, default=2)
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="launch each block kernel once plus a calibration copy (for rocprofv3 --pmc)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/hbm_traffic.json from two rocprofv3 counter CSVs")
+    ap.add_argument("--pmc-command", default="", help="command line recorded with --ingest-pmc")
     return ap.parse_args()
 
 
@@ -68,8 +73,22 @@ def time_events(fn, reps, stream):
     return s.elapsed_time(e) / reps  # ms
 
 
-def kernel_breakdown(cfg, path_name, reps):
-    """Each kernel of one block at the workload's shapes, timed alone on the current stream."""
+KERNEL_SOURCES = {
+    "ln": ["layernorm.hip", "wenc_device.h"],
+    "gemm_qkv": ["gemm.hip", "wenc_device.h"],
+    "attention": ["attention.hip", "wenc_device.h"],
+    "gemm_out_residual": ["gemm.hip", "wenc_device.h"],
+    "gemm_fc1_gelu": ["gemm.hip", "wenc_device.h"],
+    "gemm_fc2_residual": ["gemm.hip", "wenc_device.h"],
+}
+KERNEL_ORDER = list(KERNEL_SOURCES)
+COPY_BYTES = 1 << 30  # plain device copy used to scale the HBM byte counters
+
+
+def make_kernels(cfg, path_name):
+    """Each kernel of one block at the workload's shapes, as (launch, bound, work) on fresh
+    device buffers: LN1, the QKV projection, attention, out-projection + residual, fc1 + GELU,
+    fc2 + residual.  Work is algorithmic flops (MFMA-bound) or bytes (HBM-bound) per launch."""
     import torch
     from speech_transformer_encoder_amd import binding as B
     path = B.PATHS[path_name]
@@ -92,9 +111,8 @@ def kernel_breakdown(cfg, path_name, reps):
     ones, zeros = torch.ones(d, device=dev), torch.zeros(d, device=dev)
     b3, bf = torch.zeros(3 * d, device=dev), torch.zeros(f, device=dev)
     ln_dt = {"bf16": B.WENC_DTYPE_BF16, "fp16": B.WENC_DTYPE_F16, "fp32": B.WENC_DTYPE_F32}[path_name]
-    st = torch.cuda.current_stream()
     qp = qkv.data_ptr()
-    kernels = {
+    return {
         "ln": (lambda: B.whisper_enc_layernorm(x, ones, zeros, a, M, d, ln_dt),
                "hbm", M * d * (4 + es) + 2 * d * 4),
         "gemm_qkv": (lambda: B.whisper_enc_linear(a, wqkv, b3, None, qkv_out, M, 3 * d, d, path,
@@ -111,9 +129,15 @@ def kernel_breakdown(cfg, path_name, reps):
                                                            B.WENC_EPI_BIAS_RESIDUAL), "mfma",
                               2.0 * M * d * f),
     }
+
+
+def kernel_breakdown(cfg, path_name, reps):
+    """Each kernel of one block at the workload's shapes, timed alone on the current stream."""
+    import torch
+    st = torch.cuda.current_stream()
     per_block = {"ln": 2}  # LN1 and LN2
     out = {}
-    for name, (fn, bound, work) in kernels.items():
+    for name, (fn, bound, work) in make_kernels(cfg, path_name).items():
         ms = time_events(fn, reps, st)
         if bound == "hbm":
             ach = work / (ms * 1e-3) / 1e9
@@ -127,6 +151,63 @@ def kernel_breakdown(cfg, path_name, reps):
                      "peak": peak, "frac": round(ach / peak, 4), "work": work,
                      "launches_per_block": per_block.get(name, 1)}
     return out
+
+
+def pmc_run(cfg, path_name):
+    """For `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE`: two passes of one launch of each
+    block kernel (in KERNEL_ORDER), each followed by a plain device copy of COPY_BYTES that
+    scales the counters (the last pass is the one read)."""
+    import torch
+    kern = make_kernels(cfg, path_name)
+    src = torch.zeros(COPY_BYTES // 4, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        for name in KERNEL_ORDER:
+            kern[name][0]()
+            torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    print("pmc run done: " + ", ".join(KERNEL_ORDER) + f", copy of {COPY_BYTES} bytes", flush=True)
+
+
+def _counter_rows(path):
+    import csv
+    with open(path) as fh:
+        rows = list(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return rows
+
+
+def _last_pass(rows, counter):
+    """(per-kernel KiB in KERNEL_ORDER, copy KiB) of the last pmc pass in a counter CSV."""
+    rows = [r for r in rows if r["Counter_Name"] == counter]
+    copy_idx = max(i for i, r in enumerate(rows) if "opy" in r["Kernel_Name"]
+                   and "wenc" not in r["Kernel_Name"])
+    ours = [r for r in rows[:copy_idx] if "wenc::" in r["Kernel_Name"]][-len(KERNEL_ORDER):]
+    return [float(r["Counter_Value"]) for r in ours], float(rows[copy_idx]["Counter_Value"]), \
+        [r["Kernel_Name"] for r in ours]
+
+
+def ingest_pmc(cfg, path_name, fetch_csv, write_csv, command):
+    """Scale the FETCH_SIZE / WRITE_SIZE readings (KiB per dispatch) by the copy's known bytes and
+    store bytes per launch per kernel, with the hash of the sources they were taken on."""
+    fetch, fcopy, names = _last_pass(_counter_rows(fetch_csv), "FETCH_SIZE")
+    write, wcopy, _ = _last_pass(_counter_rows(write_csv), "WRITE_SIZE")
+    f_fetch = COPY_BYTES / (fcopy * 1024.0)
+    f_write = COPY_BYTES / (wcopy * 1024.0)
+    out = {"command": command, "copy_bytes": COPY_BYTES,
+           "copy_fetch_kib": fcopy, "copy_write_kib": wcopy,
+           "scale_fetch": f_fetch, "scale_write": f_write, "kernels": {}}
+    for i, name in enumerate(KERNEL_ORDER):
+        srcs = KERNEL_SOURCES[name]
+        out["kernels"][name] = {
+            "kernel_name": names[i], "fetch_kib": fetch[i], "write_kib": write[i],
+            "bytes_per_launch": round(fetch[i] * 1024 * f_fetch + write[i] * 1024 * f_write),
+            "config": cfg.name, "path": path_name, "sources": srcs,
+            "source_hash": source_hash(srcs)}
+    with open(COUNTERS, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def cpu_baseline(cfg, windows, layers):
@@ -171,9 +252,15 @@ def main():
     from speech_transformer_encoder_amd import synth
     from speech_transformer_encoder_amd.encoder import build_from_workload, to_device_input
 
+    cfg = synth.CONFIGS[args.config]
+    if args.ingest_pmc:
+        ingest_pmc(cfg, args.path, args.ingest_pmc[0], args.ingest_pmc[1], args.pmc_command)
+        return
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     B.load()
-    cfg = synth.CONFIGS[args.config]
+    if args.pmc_run:
+        pmc_run(cfg, args.path)
+        return
     path = B.PATHS[args.path]
     w = synth.make_workload(cfg)
     x = to_device_input(w.x)

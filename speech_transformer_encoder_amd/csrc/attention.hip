@@ -62,12 +62,17 @@ template <> struct RowSum<bf16_t> {
 // Written as inline assembly so that the compiler does not treat the copies in flight as
 // possible writers of every LDS read that follows (it would wait for all of them); the kernel
 // waits for them itself with s_waitcnt vmcnt before the barrier that publishes a tile.
+// M0 is listed as clobbered for the reader; the compiler treats M0 as reserved (and says so in a
+// warning, silenced here) and nothing else in these kernels reads it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_copy16(u32x4 rsrc, uint32_t lds_base, int voffset) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(lds_base), "v"(voffset), "s"(rsrc)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
@@ -83,7 +88,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
                                                         const uint16_t* __restrict__ Kp,
                                                         const uint16_t* __restrict__ Vp, int ld,
                                                         uint16_t* __restrict__ O, int ldo, int t,
-                                                        float c) {
+                                                        int heads, float c) {
   __shared__ __attribute__((aligned(1024))) uint16_t st0[2 * ATILE];
   __shared__ __attribute__((aligned(1024))) uint16_t st1[2 * ATILE];
   __shared__ __attribute__((aligned(1024))) uint16_t st2[2 * ATILE];
@@ -93,12 +98,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int g = lane >> 5;
   const int frow = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = blockIdx.y;
-  const size_t win = (size_t)blockIdx.z * t;  // first row of this window
+  // 1-D grid over (query block, head, window), renumbered so that the query blocks of one
+  // (window, head) run on the same XCD and read its K and V through one L2.
+  const int nqb = (t + AQ - 1) / AQ;
+  const int v = xcd_virtual_id(blockIdx.x, gridDim.x);
+  const int qb = v % nqb;
+  const int h = (v / nqb) % heads;
+  const size_t win = (size_t)(v / (nqb * heads)) * t;  // first row of this window
   const int col0 = h * 64;
 
   // Query fragments: B operand of S^T, lane holds q = lane%32, dims 16s + 8g .. +7.
-  const int qi = blockIdx.x * AQ + wave * 32 + frow;
+  const int qi = qb * AQ + wave * 32 + frow;
   u32x4 qf[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
@@ -429,18 +439,19 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int ld_
                             hipStream_t st) {
   if (batch == 0 || t == 0) return hipSuccess;
   const float c = scale * 1.4426950408889634f;  // fold log2(e): exp(x) = exp2(x * log2 e)
-  dim3 grid16((t + AQ - 1) / AQ, heads, batch), block16(512);
+  const long nblk16 = (long)((t + AQ - 1) / AQ) * heads * batch;
+  dim3 grid16((unsigned)nblk16), block16(512);
   dim3 grid((t + AQ32 - 1) / AQ32, heads, batch), block(256);
   switch (dtype) {
     case DT_BF16:
       attn16_kernel<bf16_t><<<grid16, block16, 0, st>>>(
           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-          static_cast<const uint16_t*>(v), ld_qkv, static_cast<uint16_t*>(o), ld_o, t, c);
+          static_cast<const uint16_t*>(v), ld_qkv, static_cast<uint16_t*>(o), ld_o, t, heads, c);
       break;
     case DT_F16:
       attn16_kernel<f16_t><<<grid16, block16, 0, st>>>(
           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-          static_cast<const uint16_t*>(v), ld_qkv, static_cast<uint16_t*>(o), ld_o, t, c);
+          static_cast<const uint16_t*>(v), ld_qkv, static_cast<uint16_t*>(o), ld_o, t, heads, c);
       break;
     case DT_F32:
       attn32_kernel<<<grid, block, 0, st>>>(static_cast<const float*>(q),

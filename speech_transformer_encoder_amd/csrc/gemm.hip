@@ -54,13 +54,6 @@ __device__ __forceinline__ float gelu_erf_as(float z) {
   return fmaf(-0.5f * fabsf(z), p * e, fmaxf(z, 0.0f));
 }
 
-// Bijective renumbering of a 1-D grid so consecutive virtual ids run on the same XCD.
-__device__ __forceinline__ int xcd_virtual_id(int id, int nb) {
-  const int q = nb >> 3, r = nb & 7;
-  const int xcd = id & 7, pos = id >> 3;
-  return (xcd < r) ? xcd * (q + 1) + pos : r * (q + 1) + (xcd - r) * q + pos;
-}
-
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int G_N = 256, G_M = 256, G_K = 64;  // workgroup tile

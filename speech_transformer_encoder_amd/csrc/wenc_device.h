@@ -92,4 +92,13 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Workgroups of a 1-D grid are dispatched round-robin over the eight XCDs (id % 8).  This
+// bijective renumbering gives each XCD a contiguous range of virtual ids, so workgroups that
+// share operands can be placed on one XCD and share its L2.
+__device__ __forceinline__ int xcd_virtual_id(int id, int nb) {
+  const int q = nb >> 3, r = nb & 7;
+  const int xcd = id & 7, pos = id >> 3;
+  return (xcd < r) ? xcd * (q + 1) + pos : r * (q + 1) + (xcd - r) * q + pos;
+}
+
 }  // namespace wenc

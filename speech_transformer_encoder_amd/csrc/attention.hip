@@ -206,7 +206,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     u32x4 pb[4];
     float tsum;
     auto exponentiate = [&]() {
-      tsum = 0.f;
+      float ts[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial sums (shorter chains)
 #pragma unroll
       for (int kstep = 0; kstep < 4; ++kstep) {
         const int mb = kstep >> 1, js = kstep & 1;
@@ -215,9 +215,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
           const float p0 = fast_exp2(fmaf(sacc[mb][8 * js + 2 * e], c, -m_run));
           const float p1 = fast_exp2(fmaf(sacc[mb][8 * js + 2 * e + 1], c, -m_run));
           pb[kstep][e] = pack2<T>(p0, p1);
-          tsum = RowSum<T>::add(pb[kstep][e], tsum);
+          ts[e] = RowSum<T>::add(pb[kstep][e], ts[e]);
         }
       }
+      tsum = (ts[0] + ts[1]) + (ts[2] + ts[3]);
     };
     exponentiate();
     if (__builtin_amdgcn_ballot_w64(!(tsum <= P_BOUND))) {

@@ -58,31 +58,6 @@ template <> struct RowSum<bf16_t> {
   }
 };
 
-// Global -> LDS copy of 16 bytes per lane (lane i to lds_base + 16 i) from a range-checked buffer.
-// Written as inline assembly so that the compiler does not treat the copies in flight as
-// possible writers of every LDS read that follows (it would wait for all of them); the kernel
-// waits for them itself with s_waitcnt vmcnt before the barrier that publishes a tile.
-// M0 is listed as clobbered for the reader; the compiler treats M0 as reserved (and says so in a
-// warning, silenced here) and nothing else in these kernels reads it.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_copy16(u32x4 rsrc, uint32_t lds_base, int voffset) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds_base), "v"(voffset), "s"(rsrc)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-
 template <typename T>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void attn16_kernel(const uint16_t* __restrict__ Q,
                                                         const uint16_t* __restrict__ Kp,

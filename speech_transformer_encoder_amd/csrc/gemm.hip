@@ -254,6 +254,191 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
   }
 }
 
+// Smaller-problem variant (fewer 256 x 256 tiles than CUs, e.g. the 1500-row GEMMs of a single
+// window): 128 (n) x 256 (m) tiles with a 32-wide k tile for a 256-thread workgroup (four
+// wavefronts, 64 x 128 outputs each), two workgroups per CU so that one's barriers and epilogue
+// overlap the other's MFMAs, three LDS stages of 64-byte rows (chunk c of row r at slot
+// c ^ ((r >> 2) & 3), conflict-free for the 16-lane fragment phases).  The tile copies are
+// inline assembly (lds_copy16), so the kernel's own s_waitcnt vmcnt is the only wait on them.
+constexpr int H_N = 128, H_M = 256, H_K = 32;
+constexpr int H_WN = 2, H_WM = 2;
+constexpr int H_TN = H_N / H_WN, H_TM = H_M / H_WM;  // 64 x 128 per wavefront
+constexpr int H_NA = H_TN / 32, H_NB = H_TM / 32;     // 2 x 4
+constexpr int H_WAVES = H_WN * H_WM;
+constexpr int H_THREADS = 64 * H_WAVES;
+constexpr int H_ROWS = H_N + H_M;                      // 64-byte rows per stage
+constexpr int H_STAGE = H_ROWS * H_K;                  // 16-bit elements per stage
+constexpr int H_LW = H_N / 16 / H_WAVES, H_LX = H_M / 16 / H_WAVES;  // 1 KB copies per wave: 2, 4
+
+template <typename T, int EPI>
+__global__ __launch_bounds__(H_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm16_small_kernel(
+    const uint16_t* __restrict__ X, int lda, const uint16_t* __restrict__ W,
+    const float* __restrict__ bias, const float* residual, void* C, int ldc, int M, int N, int K) {
+  // One array for the three stages: the copies are inline assembly, invisible to the compiler's
+  // wait insertion, so separate arrays buy nothing; the epilogue reuses the whole 72 KB.
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[3 * H_STAGE];
+  uint16_t* const s0 = lds;
+  uint16_t* const s1 = lds + H_STAGE;
+  uint16_t* const s2 = lds + 2 * H_STAGE;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave / H_WM, wm = wave % H_WM;
+  const int g = lane >> 5, frow = lane & 31;
+
+  const int tiles_m = (M + H_M - 1) / H_M, tiles_n = (N + H_N - 1) / H_N;
+  const int v = xcd_virtual_id(blockIdx.x, gridDim.x);
+  const int group = 8 * tiles_n;
+  const int first_m = (v / group) * 8;
+  const int gm = min(tiles_m - first_m, 8);
+  const int tm = first_m + (v % group) % gm, tn = (v % group) / gm;
+  const int n0 = tn * H_N, m0 = tm * H_M;
+
+  const int wrows = min(N - n0, H_N), xrows = min(M - m0, H_M);
+  const u32x4 rW = buffer_rsrc(W + (size_t)n0 * K, (uint32_t)(wrows * K * 2));
+  const u32x4 rX = buffer_rsrc(X + (size_t)m0 * lda, (uint32_t)(xrows * lda * 2));
+
+  // Copy i of wavefront w fills 1 KB block (i * 4 + w) of its operand: 16 rows of 64 bytes,
+  // lane l row (l >> 2), slot (l & 3) holding chunk slot ^ ((row >> 2) & 3).
+  const int lrow = 16 * wave + (lane >> 2);
+  const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  const int voW = lrow * K * 2 + lchunk * 16, voX = lrow * lda * 2 + lchunk * 16;
+  auto load_tile = [&](int kt, const uint16_t* st) {
+    const int ko = kt * (H_K * 2);
+    const uint32_t base = lds_addr(st);
+#pragma unroll
+    for (int i = 0; i < H_LW; ++i)
+      lds_copy16(rW, base + (uint32_t)(i * 4 + wave) * 1024u, voW + i * 64 * K * 2 + ko);
+#pragma unroll
+    for (int i = 0; i < H_LX; ++i)
+      lds_copy16(rX, base + H_N * 64 + (uint32_t)(i * 4 + wave) * 1024u, voX + i * 64 * lda * 2 + ko);
+  };
+
+  const int rowA = (wn * H_TN + frow) * 64;
+  const int rowB = (H_N + wm * H_TM + frow) * 64;
+  int xo[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) xo[s] = ((2 * s + g) ^ ((lane >> 2) & 3)) << 4;
+  auto read_frags = [&](const uint16_t* st, int s, u32x4 (&fa)[H_NA], u32x4 (&fb)[H_NB]) {
+    const char* base = reinterpret_cast<const char*>(st);
+    fa[0] = *reinterpret_cast<const u32x4*>(base + rowA + xo[s]);
+#pragma unroll
+    for (int b = 0; b < H_NB; ++b)
+      fb[b] = *reinterpret_cast<const u32x4*>(base + rowB + b * 2048 + xo[s]);
+#pragma unroll
+    for (int a = 1; a < H_NA; ++a)
+      fa[a] = *reinterpret_cast<const u32x4*>(base + rowA + a * 2048 + xo[s]);
+  };
+
+  f32x16 acc[H_NA][H_NB];
+#pragma unroll
+  for (int a = 0; a < H_NA; ++a)
+#pragma unroll
+    for (int b = 0; b < H_NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  auto mm = [&](const u32x4 (&fa)[H_NA], const u32x4 (&fb)[H_NB]) {
+#pragma unroll
+    for (int a = 0; a < H_NA; ++a)
+#pragma unroll
+      for (int b = 0; b < H_NB; ++b) acc[a][b] = mfma32x32x16<T>(fa[a], fb[b], acc[a][b]);
+  };
+  auto sched = [&]() {
+#pragma unroll
+    for (int q = 0; q < H_NA + H_NB; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, H_NA * H_NB - H_NA - H_NB, 0);
+  };
+
+  constexpr int LT = H_LW + H_LX;  // copies per wavefront and tile
+  const int nk = K / H_K;
+  u32x4 fa0[H_NA], fb0[H_NB], fa1[H_NA], fb1[H_NB];
+  load_tile(0, s0);
+  if (nk > 1) load_tile(1, s1);
+  if (nk > 1) __builtin_amdgcn_s_waitcnt(0x0F70 | LT); else __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  read_frags(s0, 0, fa0, fb0);
+
+  // k tile kt from `cur`; tile kt + 2 goes to `ahead` (the stage of tile kt - 1, which every
+  // wavefront finished reading before the barrier of body(kt - 1)).
+  auto body = [&](int kt, const uint16_t* cur, const uint16_t* nxt, const uint16_t* ahead) {
+    const bool loads = kt + 2 < nk, next = kt + 1 < nk;
+    if (loads) load_tile(kt + 2, ahead);
+    read_frags(cur, 1, fa1, fb1); mm(fa0, fb0); sched();
+    if (next) {
+      if (loads) __builtin_amdgcn_s_waitcnt(0x0F70 | LT);
+      else __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();  // tile kt + 1 landed everywhere; tile kt no longer read after this step
+      read_frags(nxt, 0, fa0, fb0);
+    }
+    mm(fa1, fb1);
+  };
+  for (int kt = 0; kt < nk; kt += 3) {
+    body(kt, s0, s1, s2);
+    if (kt + 1 < nk) body(kt + 1, s1, s2, s0);
+    if (kt + 2 < nk) body(kt + 2, s2, s0, s1);
+  }
+
+  // Epilogue as in the 8-wave kernel: 32-row blocks staged through the wavefront's own 8 KB of
+  // LDS (wavefront-private, so only the first reuse of the stage memory needs a barrier).
+  __syncthreads();
+  float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 64);
+  const int nw = n0 + wn * H_TN;
+  const bool cols_ok = nw < N;
+#pragma unroll
+  for (int b = 0; b < H_NB; ++b) {
+#pragma unroll
+    for (int a = 0; a < H_NA; ++a)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = a * 8 + 2 * j + g;
+        const float4 bb = cols_ok ? *reinterpret_cast<const float4*>(bias + nw + 4 * c)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4*>(ep + frow * 64 + ((c ^ (frow & 15)) << 2)) =
+            make_float4(acc[a][b][4 * j] + bb.x, acc[a][b][4 * j + 1] + bb.y,
+                        acc[a][b][4 * j + 2] + bb.z, acc[a][b][4 * j + 3] + bb.w);
+      }
+    if (!cols_ok) continue;
+    const int mb = m0 + wm * H_TM + b * 32;
+    if constexpr (EPI == EPI_BIAS_RESIDUAL) {
+      float4 res[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int m = mb + (lane >> 4) + 4 * q;
+        res[q] = m < M ? *reinterpret_cast<const float4*>(residual + (size_t)m * ldc + nw + 4 * (lane & 15))
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int r = (lane >> 4) + 4 * q, c = lane & 15;
+        const int m = mb + r;
+        const float4 v4 = *reinterpret_cast<const float4*>(ep + r * 64 + ((c ^ (r & 15)) << 2));
+        if (m < M)
+          *reinterpret_cast<float4*>(static_cast<float*>(C) + (size_t)m * ldc + nw + 4 * c) =
+              make_float4(res[q].x + v4.x, res[q].y + v4.y, res[q].z + v4.z, res[q].w + v4.w);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = (lane >> 3) + 8 * q, c0 = 2 * (lane & 7);
+        const int m = mb + r;
+        float4 v0 = *reinterpret_cast<const float4*>(ep + r * 64 + ((c0 ^ (r & 15)) << 2));
+        float4 v1 = *reinterpret_cast<const float4*>(ep + r * 64 + (((c0 + 1) ^ (r & 15)) << 2));
+        if constexpr (EPI == EPI_BIAS_GELU) {
+          v0 = make_float4(gelu_erf_as(v0.x), gelu_erf_as(v0.y), gelu_erf_as(v0.z), gelu_erf_as(v0.w));
+          v1 = make_float4(gelu_erf_as(v1.x), gelu_erf_as(v1.y), gelu_erf_as(v1.z), gelu_erf_as(v1.w));
+        }
+        const u32x4 w4 = {pack2<T>(v0.x, v0.y), pack2<T>(v0.z, v0.w), pack2<T>(v1.x, v1.y), pack2<T>(v1.z, v1.w)};
+        if (m < M)
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(C) + (size_t)m * ldc + nw + 4 * c0) = w4;
+      }
+    }
+  }
+}
+
+
 constexpr int GB_N = 128;  // W rows (output columns) per tile
 constexpr int GB_M = 128;  // X rows per tile
 
@@ -376,9 +561,15 @@ template <typename T, int EPI>
 static void launch16_epi(const uint16_t* X, int lda, const uint16_t* W, const float* bias,
                          const float* residual, void* c, int ldc, int m, int n, int k,
                          hipStream_t st) {
-  const int tiles = ((m + G_M - 1) / G_M) * ((n + G_N - 1) / G_N);
-  gemm16_kernel<T, EPI><<<dim3((unsigned)tiles), dim3(G_THREADS), 0, st>>>(X, lda, W, bias,
-                                                                          residual, c, ldc, m, n, k);
+  const long tiles = (long)((m + G_M - 1) / G_M) * ((n + G_N - 1) / G_N);
+  if (tiles >= 256) {
+    gemm16_kernel<T, EPI><<<dim3((unsigned)tiles), dim3(G_THREADS), 0, st>>>(
+        X, lda, W, bias, residual, c, ldc, m, n, k);
+  } else {
+    const long small = (long)((m + H_M - 1) / H_M) * ((n + H_N - 1) / H_N);
+    gemm16_small_kernel<T, EPI><<<dim3((unsigned)small), dim3(H_THREADS), 0, st>>>(
+        X, lda, W, bias, residual, c, ldc, m, n, k);
+  }
 }
 
 template <typename T>

@@ -101,4 +101,31 @@ __device__ __forceinline__ int xcd_virtual_id(int id, int nb) {
   return (xcd < r) ? xcd * (q + 1) + pos : r * (q + 1) + (xcd - r) * q + pos;
 }
 
+
+// Global -> LDS copy of 16 bytes per lane (lane i to lds_base + 16 i) from a range-checked buffer,
+// as inline assembly so that the compiler does not treat the copies in flight as possible writers
+// of every later LDS read (it would wait for all of them).  M0 is listed as clobbered for the
+// reader; the compiler reserves M0 (and says so in a warning, silenced here) and nothing else in
+// these kernels reads it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(u32x4 rsrc, uint32_t lds_base, int voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Raw buffer resource over `bytes` bytes at `base` (loads past the end return zeros).
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 }  // namespace wenc

@@ -40,18 +40,19 @@ __device__ __forceinline__ float gelu_erf(float z) {
 // erf-GELU for the 16-bit paths, whose output is rounded to 8 or 11 significant bits: the
 // complementary error function from Abramowitz & Stegun, Handbook of Mathematical Functions,
 // formula 7.1.26 (Hastings' rational approximation, absolute error <= 1.5e-7):
-//   erfc(a) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-a^2),  t = 1 / (1 + p a),  a >= 0,
-// and gelu(z) = max(z, 0) - |z|/2 erfc(|z| / sqrt 2), which holds for both signs of z.
+//   erfc(a) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-a^2),  t = 1 / (1 + p a),  a >= 0.
+// With a = |z| / sqrt 2 and w = 1 - erfc(a) = erf(a):  gelu(z) = z/2 (1 + erf(z/sqrt 2))
+// = (z + |z| w) / 2 for both signs of z.  13 VALU operations (two of them transcendental).
 __device__ __forceinline__ float gelu_erf_as(float z) {
-  const float a = fabsf(z) * 0.7071067811865476f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, a, 1.0f));
-  float p = fmaf(t, 1.061405429f, -1.453152027f);
-  p = fmaf(t, p, 1.421413741f);
-  p = fmaf(t, p, -0.284496736f);
-  p = fmaf(t, p, 0.254829592f);
-  p *= t;
-  const float e = __builtin_amdgcn_exp2f(-(a * a) * 1.4426950408889634f);
-  return fmaf(-0.5f * fabsf(z), p * e, fmaxf(z, 0.0f));
+  const float az = fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.7071067811865476f, az, 1.0f));
+  float q = fmaf(t, 1.061405429f, -1.453152027f);
+  q = fmaf(t, q, 1.421413741f);
+  q = fmaf(t, q, -0.284496736f);
+  q = fmaf(t, q, 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(z * (z * (-0.5f * 1.4426950408889634f)));  // exp(-a^2)
+  const float w = fmaf(-(q * t), e, 1.0f);
+  return 0.5f * fmaf(az, w, z);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -192,13 +193,16 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
   body(kt, std::false_type{}, std::false_type{});
 
   // Epilogue, one 32-row block of the wavefront at a time: (acc + bias) as fp32 into the
-  // wavefront's 8 KB of LDS (row r, 16-byte chunk c at slot c ^ (r & 15)), then read back by rows.
+  // wavefront's 8 KB of LDS (row r, 16-byte chunk c at slot c ^ (r & 15)), then read back by rows
+  // (LDS operations of one wavefront complete in order, so the read-back sees the writes).
   float* ep = reinterpret_cast<float*>(s0) + wave * (32 * 64);
   const int nw = n0 + wn * G_TN;  // first output column of the wavefront
   const bool cols_ok = nw < N;    // N % 64 == 0: the wavefront's 64 columns are all in or out
+  // Each wavefront uses only its own 8 KB, so after the one barrier that retires the fragment
+  // reads, the staging needs no further workgroup synchronisation.
+  __syncthreads();
 #pragma unroll
   for (int b = 0; b < G_NB; ++b) {
-    __syncthreads();
 #pragma unroll
     for (int a = 0; a < G_NA; ++a)
 #pragma unroll
@@ -210,7 +214,6 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
             make_float4(acc[a][b][4 * j] + bb.x, acc[a][b][4 * j + 1] + bb.y,
                         acc[a][b][4 * j + 2] + bb.z, acc[a][b][4 * j + 3] + bb.w);
       }
-    __syncthreads();
     if (!cols_ok) continue;
     const int mb = m0 + wm * G_TM + b * 32;
     if constexpr (EPI == EPI_BIAS_RESIDUAL) {

@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/hbm_traffic.json from two rocprofv3 counter CSVs")
     ap.add_argument("--pmc-command", default="", help="command line recorded with --ingest-pmc")
+    ap.add_argument("--no-next-steps", action="store_true",
+                    help="skip timing the adjacent steps (cross-attention K/V precompute)")
     return ap.parse_args()
 
 
@@ -210,6 +212,41 @@ def ingest_pmc(cfg, path_name, fetch_csv, write_csv, command):
     print(json.dumps(out, indent=1))
 
 
+DECODER_LAYERS = {384: 4, 512: 6, 768: 12, 1280: 32}  # Whisper tiny / base / small / large-v3
+
+
+def time_cross_kv(cfg, path_name, reps):
+    """The step after the encoder: cross-attention keys and values of every decoder layer of the
+    matching Whisper size from the workload's encoder output, one C ABI call."""
+    import torch
+    from speech_transformer_encoder_amd import binding as B
+    from speech_transformer_encoder_amd import synth
+    path = B.PATHS[path_name]
+    d, L = cfg.d_model, DECODER_LAYERS.get(cfg.d_model, 4)
+    M = cfg.batch * cfg.t
+    layers = synth.make_cross_layers(cfg.seed, L, d, bf16=cfg.bf16_weights)
+    dev = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
+    blob = torch.empty(B.whisper_enc_cross_kv_bytes(d, L, path), dtype=torch.uint8, device="cuda")
+    B.whisper_enc_pack_cross_kv([dev(q["wk"]) for q in layers], [dev(q["wv"]) for q in layers],
+                                [dev(q["bv"]) for q in layers], L, d, path, blob)
+    ws_bytes = B.whisper_enc_cross_kv_workspace_bytes(cfg.batch, cfg.t, d, path)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    es = 4 if path_name == "fp32" else 2
+    kv = torch.empty(cfg.batch * L * 2 * cfg.t * d * es, dtype=torch.uint8, device="cuda")
+    y = torch.randn(cfg.batch, cfg.t, d, device="cuda")
+    fn = lambda: B.whisper_enc_cross_kv(y, kv, blob, L, cfg.batch, cfg.t, d, cfg.heads, path,  # noqa: E731
+                                        ws, ws.numel())
+    ms = time_events(fn, reps, torch.cuda.current_stream())
+    flops = 2.0 * M * (2 * L * d) * d
+    tf = flops / (ms * 1e-3) / 1e12
+    out = {"decoder_layers": L, "ms": round(ms, 4), "achieved": round(tf, 1), "unit": "TFLOP/s",
+           "peak": PEAK_TFLOPS[path_name], "frac": round(tf / PEAK_TFLOPS[path_name], 4),
+           "work": flops}
+    del kv, blob, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, windows, layers):
     """The oracle as it stands, on a bounded sample of the workload (first windows / layers)."""
     import numpy as np
@@ -313,6 +350,10 @@ def main():
     attn_tf = flops["attention"] / (attn_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[args.path]
 
+    next_steps = {}
+    if not args.no_next_steps:
+        next_steps["cross_kv"] = time_cross_kv(cfg, args.path, args.kernel_reps)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, args.cpu_sample_windows, args.cpu_sample_layers)
@@ -336,6 +377,7 @@ def main():
         "wall_s_timed": round(wall, 4),
         "cpu_baseline": cpu,
         "other_paths": others,
+        "next_steps": next_steps,
     }
     print(json.dumps(out), flush=True)
 

@@ -72,6 +72,7 @@ extern "C" {
 #define WENC_MAX_D_MODEL 4096
 #define WENC_MAX_FFN_DIM 65536
 #define WENC_MAX_ROWS (1 << 24)
+#define WENC_MAX_DEC_LAYERS 64
 
 /* Human-readable text of a status code (static storage; never NULL). */
 const char* whisper_enc_strerror(int code);
@@ -163,6 +164,47 @@ int whisper_enc_linear(const void* a, const void* w, const float* bias, const fl
  */
 int whisper_enc_attention(const void* q, const void* k, const void* v, void* o, int batch, int t,
                           int heads, int ld_qkv, int ld_o, int path, void* stream);
+
+
+/* ---- Cross-attention keys and values for the decoder (the step after the encoder). ---- */
+
+/*
+ * The decoder's cross-attention projects the encoder output once per window through every
+ * decoder layer's K and V weights (turbospark-runtime whisper/metal.rs, build_cross_caches;
+ * oxinfer whisper/model.rs, cross_kv): for decoder layer l,
+ *   K_l = y Wk_l^T   (no bias),   V_l = y Wv_l^T + bv_l,
+ * stored head-major as in oxinfer's Kv ([heads][n][dh], each head's rows contiguous).
+ *
+ * whisper_enc_cross_kv_bytes: size of the packed weights for n_dec_layers (1..64) layers,
+ * 0 if invalid.  Layout: fp32 biases [2L][d] (K rows zero) then W [2L d, d] in the path's
+ * operand type, row block 2l = Wk_l, 2l + 1 = Wv_l.
+ */
+size_t whisper_enc_cross_kv_bytes(int d_model, int n_dec_layers, int path);
+
+/*
+ * Pack the cross K/V weights: wk, wv, bv are HOST arrays of n_dec_layers DEVICE pointers to
+ * fp32 Wk_l [d, d], Wv_l [d, d] (PyTorch [n_out, n_in]) and bv_l [d].  dst: device,
+ * whisper_enc_cross_kv_bytes() bytes, 256-byte aligned.  Matrices are rounded to the path's
+ * operand type (nearest even).  Asynchronous on `stream`; sources must stay valid until done.
+ */
+int whisper_enc_pack_cross_kv(const float* const* wk, const float* const* wv,
+                              const float* const* bv, int n_dec_layers, int d_model, int path,
+                              void* dst, void* stream);
+
+/* Workspace for whisper_enc_cross_kv: the 16-bit copy of y (256 bytes on the fp32 path). */
+size_t whisper_enc_cross_kv_workspace_bytes(int batch, int t, int d_model, int path);
+
+/*
+ * y: [batch, t, d_model] fp32 encoder output (16-byte aligned).  kv: output, element
+ * [b][l][j][h][i][e] = (j == 0 ? K_l : V_l)[b, i, 64 h + e] with b < batch, l < n_dec_layers,
+ * j in {0, 1}, h < heads, i < t, e < 64, in the path's operand type (fp32 on WENC_PATH_FP32);
+ * batch * n_dec_layers * 2 * t * d_model elements.  wkv: from whisper_enc_pack_cross_kv with the
+ * same d_model, n_dec_layers and path.  d_model / heads must be 64.  workspace: device,
+ * 256-byte aligned, >= whisper_enc_cross_kv_workspace_bytes().
+ */
+int whisper_enc_cross_kv(const float* y, void* kv, const void* wkv, int n_dec_layers, int batch,
+                         int t, int d_model, int heads, int path, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -31,6 +31,11 @@ Readings taken where the pages leave a step open:
   * The ``exp`` is the exact one (oxinfer's decoder uses a fast approximation; the encoder
     attention the pages describe uses ``exp``).
 
+The step after the encoder (cross-attention keys and values of the decoder):
+  * ``cross_kv`` - for every decoder layer ``l``, ``K_l = y Wk_l^T`` (no bias) and
+    ``V_l = y Wv_l^T + bv_l`` from the encoder output ``y``, stored head-major
+    (turbospark-runtime ``build_cross_caches``; oxinfer ``cross_kv`` and ``Kv``).
+
 Cross-check formulations (used only by the tests):
   * ``attention_two_pass`` - exact max pass, exponent/sum pass, weighted sum (inferencelayer
     ``DEC_QATTN`` shader; turbospark-runtime ``encode_layer`` score planes + ``softmax_rows``).
@@ -256,3 +261,24 @@ def max_rel_error(got, ref) -> float:
 def mean_abs_error(got, ref) -> float:
     g, o = _f64(got), _f64(ref)
     return float(np.mean(np.abs(g - o))) if o.size else 0.0
+
+
+def cross_kv(y, dec_layers: Sequence[Dict[str, np.ndarray]], heads: int) -> np.ndarray:
+    """Cross-attention keys and values of every decoder layer for the encoder output ``y``.
+
+    turbospark-runtime ``build_cross_caches`` / oxinfer ``cross_kv``: per decoder layer, the keys
+    ``y Wk^T`` (the key projection has no bias) and the values ``y Wv^T + bv``; oxinfer's ``Kv``
+    keeps each head's rows contiguous.  ``y``: ``[batch, t, d]`` (or ``[t, d]``);
+    ``dec_layers``: dicts with ``wk``, ``wv`` ``[d, d]`` and ``bv`` ``[d]``.  Returns
+    ``[batch, L, 2, heads, t, hd]`` (index 0 = K, 1 = V).
+    """
+    y = _f64(y)
+    if y.ndim == 2:
+        y = y[None]
+    b, t, d = y.shape
+    out = np.empty((b, len(dec_layers), 2, heads, t, d // heads))
+    for w in range(b):
+        for l, p in enumerate(dec_layers):
+            out[w, l, 0] = _heads(linear(y[w], p["wk"]), heads)
+            out[w, l, 1] = _heads(linear(y[w], p["wv"], p["bv"]), heads)
+    return out

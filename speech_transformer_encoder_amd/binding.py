@@ -44,6 +44,8 @@ EXPORTS = (
     "whisper_enc_strerror", "whisper_enc_layer_bytes", "whisper_enc_pack_layer",
     "whisper_enc_workspace_bytes", "whisper_enc_block_forward", "whisper_enc_stack_forward",
     "whisper_enc_layernorm", "whisper_enc_linear", "whisper_enc_attention",
+    "whisper_enc_cross_kv_bytes", "whisper_enc_pack_cross_kv",
+    "whisper_enc_cross_kv_workspace_bytes", "whisper_enc_cross_kv",
 )
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -76,6 +78,10 @@ def load() -> ctypes.CDLL:
         "whisper_enc_layernorm": (I, [P, P, P, P, I, I, I, P]),
         "whisper_enc_linear": (I, [P, P, P, P, P, I, I, I, I, I, P]),
         "whisper_enc_attention": (I, [P, P, P, P, I, I, I, I, I, I, P]),
+        "whisper_enc_cross_kv_bytes": (Z, [I, I, I]),
+        "whisper_enc_pack_cross_kv": (I, [P, P, P, I, I, I, P, P]),
+        "whisper_enc_cross_kv_workspace_bytes": (Z, [I, I, I, I]),
+        "whisper_enc_cross_kv": (I, [P, P, P, I, I, I, I, I, I, P, Z, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -160,3 +166,31 @@ def whisper_enc_attention(q, k, v, o, batch, t, heads, ld_qkv, ld_o, path, strea
     _check(load().whisper_enc_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(o), batch, t, heads,
                                         ld_qkv, ld_o, path, _stream(stream)),
            "whisper_enc_attention")
+
+
+def whisper_enc_cross_kv_bytes(d_model: int, n_dec_layers: int, path: int) -> int:
+    return load().whisper_enc_cross_kv_bytes(d_model, n_dec_layers, path)
+
+
+def whisper_enc_cross_kv_workspace_bytes(batch: int, t: int, d_model: int, path: int) -> int:
+    return load().whisper_enc_cross_kv_workspace_bytes(batch, t, d_model, path)
+
+
+def whisper_enc_pack_cross_kv(wk, wv, bv, n_dec_layers, d_model, path, dst, stream=None) -> None:
+    """``wk``, ``wv``, ``bv``: sequences of ``n_dec_layers`` device tensors / addresses."""
+    arr = ctypes.c_void_p * n_dec_layers
+    pk = arr(*[_ptr(x) for x in wk])
+    pv = arr(*[_ptr(x) for x in wv])
+    pb = arr(*[_ptr(x) for x in bv])
+    _check(load().whisper_enc_pack_cross_kv(ctypes.cast(pk, ctypes.c_void_p),
+                                            ctypes.cast(pv, ctypes.c_void_p),
+                                            ctypes.cast(pb, ctypes.c_void_p), n_dec_layers,
+                                            d_model, path, _ptr(dst), _stream(stream)),
+           "whisper_enc_pack_cross_kv")
+
+
+def whisper_enc_cross_kv(y, kv, wkv, n_dec_layers, batch, t, d_model, heads, path, workspace,
+                         workspace_bytes, stream=None) -> None:
+    _check(load().whisper_enc_cross_kv(_ptr(y), _ptr(kv), _ptr(wkv), n_dec_layers, batch, t,
+                                       d_model, heads, path, _ptr(workspace), workspace_bytes,
+                                       _stream(stream)), "whisper_enc_cross_kv")

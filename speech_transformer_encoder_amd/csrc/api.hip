@@ -312,3 +312,97 @@ int whisper_enc_attention(const void* q, const void* k, const void* v, void* o, 
 }
 
 }  // extern "C"
+
+// ---- Cross-attention keys and values of the decoder layers (turbospark-runtime
+// build_cross_caches; oxinfer cross_kv): one projection of the encoder output through the packed
+// [2 L d, d] weights, written head-major. ----
+
+namespace {
+
+struct CrossLayout {
+  size_t bias, w, total;
+};
+
+CrossLayout cross_layout(int d, int n_layers, int path) {
+  CrossLayout L;
+  const size_t rows = 2 * (size_t)n_layers * d;
+  L.bias = 0;
+  L.w = round_up(rows * sizeof(float));
+  L.total = L.w + round_up(rows * d * elem_bytes(path));
+  return L;
+}
+
+bool valid_cross(int d, int n_layers, int path) {
+  return path_dtype(path) >= 0 && d >= 64 && d <= WENC_MAX_D_MODEL && d % 64 == 0 &&
+         n_layers >= 1 && n_layers <= WENC_MAX_DEC_LAYERS;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t whisper_enc_cross_kv_bytes(int d_model, int n_dec_layers, int path) {
+  if (!valid_cross(d_model, n_dec_layers, path)) return 0;
+  return cross_layout(d_model, n_dec_layers, path).total;
+}
+
+int whisper_enc_pack_cross_kv(const float* const* wk, const float* const* wv,
+                              const float* const* bv, int n_dec_layers, int d_model, int path,
+                              void* dst, void* stream) {
+  if (!valid_cross(d_model, n_dec_layers, path)) return WENC_ERR_ARG;
+  if (!wk || !wv || !bv || !dst || !aligned(dst, kAlign)) return WENC_ERR_ARG;
+  for (int l = 0; l < n_dec_layers; ++l)
+    if (!wk[l] || !wv[l] || !bv[l]) return WENC_ERR_ARG;
+  const int d = d_model, dt = path_dtype(path);
+  const size_t dd = (size_t)d * d, es = elem_bytes(path);
+  const CrossLayout L = cross_layout(d, n_dec_layers, path);
+  char* blob = static_cast<char*>(dst);
+  float* bias = reinterpret_cast<float*>(blob + L.bias);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int l = 0; l < n_dec_layers; ++l) {
+    WENC_TRY(launch_copy_or_zero(nullptr, bias + (size_t)(2 * l) * d, d, st));  // K: no bias
+    WENC_TRY(launch_copy_or_zero(bv[l], bias + (size_t)(2 * l + 1) * d, d, st));
+    WENC_TRY(launch_convert(wk[l], blob + L.w + es * (size_t)(2 * l) * dd, dd, dt, st));
+    WENC_TRY(launch_convert(wv[l], blob + L.w + es * (size_t)(2 * l + 1) * dd, dd, dt, st));
+  }
+  return WENC_OK;
+}
+
+size_t whisper_enc_cross_kv_workspace_bytes(int batch, int t, int d_model, int path) {
+  if (path_dtype(path) < 0 || batch < 0 || t < 0 || (long long)batch * t > WENC_MAX_ROWS ||
+      d_model < 64 || d_model > WENC_MAX_D_MODEL || d_model % 64)
+    return 0;
+  if (path == WENC_PATH_FP32) return kAlign;  // the fp32 path reads y directly
+  return round_up((size_t)batch * t * d_model * elem_bytes(path));
+}
+
+int whisper_enc_cross_kv(const float* y, void* kv, const void* wkv, int n_dec_layers, int batch,
+                         int t, int d_model, int heads, int path, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!valid_cross(d_model, n_dec_layers, path)) return WENC_ERR_ARG;
+  if (batch < 0 || t < 0 || heads <= 0 || (long long)batch * t > WENC_MAX_ROWS) return WENC_ERR_ARG;
+  if (d_model % heads != 0) return WENC_ERR_ARG;
+  if (d_model / heads != WENC_HEAD_DIM) return WENC_ERR_UNSUPPORTED;
+  const size_t rows = (size_t)batch * t;
+  if (rows == 0) return WENC_OK;
+  if (!y || !kv || !wkv || !workspace) return WENC_ERR_ARG;
+  if (!aligned(y, 16) || !aligned(kv, 16) || !aligned(wkv, kAlign) || !aligned(workspace, kAlign))
+    return WENC_ERR_ARG;
+  if (workspace_bytes < whisper_enc_cross_kv_workspace_bytes(batch, t, d_model, path))
+    return WENC_ERR_WORKSPACE;
+  const int d = d_model, dt = path_dtype(path);
+  const int n = 2 * n_dec_layers * d;
+  const CrossLayout L = cross_layout(d, n_dec_layers, path);
+  const char* blob = static_cast<const char*>(wkv);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const void* a = y;
+  if (path != WENC_PATH_FP32) {
+    WENC_TRY(launch_convert(y, workspace, rows * d, dt, st));
+    a = workspace;
+  }
+  WENC_TRY(launch_linear(a, d, blob + L.w, reinterpret_cast<const float*>(blob + L.bias), nullptr,
+                         kv, t, (int)rows, n, d, dt, EPI_BIAS_HEADMAJOR, st));
+  return WENC_OK;
+}
+
+}  // extern "C"

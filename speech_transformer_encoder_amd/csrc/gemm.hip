@@ -57,6 +57,13 @@ __device__ __forceinline__ float gelu_erf_as(float z) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Element offset of (row m, column n) in the head-major layout of EPI_BIAS_HEADMAJOR: rows are
+// windows of T positions, columns blocks of 64; block j of window b is a [T][64] slab.
+__device__ __forceinline__ size_t headmajor_offset(int m, int n, int N, int T) {
+  const int b = m / T, i = m - b * T;
+  return ((size_t)((size_t)b * (N >> 6) + (n >> 6)) * T + i) * 64 + (n & 63);
+}
+
 constexpr int G_N = 256, G_M = 256, G_K = 64;  // workgroup tile
 constexpr int G_WN = 4, G_WM = 2;              // wavefront grid: n x m
 constexpr int G_TN = G_N / G_WN, G_TM = G_M / G_WM;  // 64 x 128 per wavefront
@@ -250,8 +257,11 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
         }
         const u32x4 w4 = {pack2<T>(v0.x, v0.y), pack2<T>(v0.z, v0.w), pack2<T>(v1.x, v1.y),
                           pack2<T>(v1.z, v1.w)};
-        if (m < M)
-          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(C) + (size_t)m * ldc + nw + 4 * c0) = w4;
+        if (m < M) {
+          const size_t off = EPI == EPI_BIAS_HEADMAJOR ? headmajor_offset(m, nw + 4 * c0, N, ldc)
+                                                       : (size_t)m * ldc + nw + 4 * c0;
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(C) + off) = w4;
+        }
       }
     }
   }
@@ -434,8 +444,11 @@ __global__ __launch_bounds__(H_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
           v1 = make_float4(gelu_erf_as(v1.x), gelu_erf_as(v1.y), gelu_erf_as(v1.z), gelu_erf_as(v1.w));
         }
         const u32x4 w4 = {pack2<T>(v0.x, v0.y), pack2<T>(v0.z, v0.w), pack2<T>(v1.x, v1.y), pack2<T>(v1.z, v1.w)};
-        if (m < M)
-          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(C) + (size_t)m * ldc + nw + 4 * c0) = w4;
+        if (m < M) {
+          const size_t off = EPI == EPI_BIAS_HEADMAJOR ? headmajor_offset(m, nw + 4 * c0, N, ldc)
+                                                       : (size_t)m * ldc + nw + 4 * c0;
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(C) + off) = w4;
+        }
       }
     }
   }
@@ -547,7 +560,8 @@ __global__ __launch_bounds__(256) void gemm32_kernel(const float* __restrict__ X
         const float4 bb = *reinterpret_cast<const float4*>(bias + n);
         float4 v = make_float4(acc[a][b][4 * j + 0] + bb.x, acc[a][b][4 * j + 1] + bb.y,
                                acc[a][b][4 * j + 2] + bb.z, acc[a][b][4 * j + 3] + bb.w);
-        const size_t off = (size_t)m * ldc + n;
+        const size_t off = EPI == EPI_BIAS_HEADMAJOR ? headmajor_offset(m, n, N, ldc)
+                                                     : (size_t)m * ldc + n;
         if constexpr (EPI == EPI_BIAS_RESIDUAL) {
           const float4 r = *reinterpret_cast<const float4*>(residual + off);
           v = make_float4(r.x + v.x, r.y + v.y, r.z + v.z, r.w + v.w);
@@ -589,6 +603,9 @@ static hipError_t launch16(const void* a, int lda, const void* w, const float* b
     case EPI_BIAS_RESIDUAL:
       launch16_epi<T, EPI_BIAS_RESIDUAL>(X, lda, W, bias, residual, c, ldc, m, n, k, st);
       break;
+    case EPI_BIAS_HEADMAJOR:
+      launch16_epi<T, EPI_BIAS_HEADMAJOR>(X, lda, W, bias, residual, c, ldc, m, n, k, st);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -611,6 +628,10 @@ static hipError_t launch32(const void* a, int lda, const void* w, const float* b
     case EPI_BIAS_RESIDUAL:
       gemm32_kernel<EPI_BIAS_RESIDUAL><<<grid, block, 0, st>>>(X, lda, W, bias, residual, C, ldc, m,
                                                                n, k);
+      break;
+    case EPI_BIAS_HEADMAJOR:
+      gemm32_kernel<EPI_BIAS_HEADMAJOR><<<grid, block, 0, st>>>(X, lda, W, bias, residual, C, ldc,
+                                                                m, n, k);
       break;
     default: return hipErrorInvalidValue;
   }

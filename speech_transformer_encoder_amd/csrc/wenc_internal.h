@@ -9,7 +9,7 @@
 namespace wenc {
 
 enum DType { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
-enum Epilogue { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2 };
+enum Epilogue { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_BIAS_HEADMAJOR = 3 };
 
 // y[rows, d] = LayerNorm(x[rows, d]) * gamma + beta, stored as out_dtype.  d % 4 == 0, d <= 4096.
 hipError_t launch_layernorm(const float* x, const float* gamma, const float* beta, void* y,
@@ -19,6 +19,9 @@ hipError_t launch_layernorm(const float* x, const float* gamma, const float* bet
 //   EPI_BIAS          -> c in the operand dtype (fp32 for DT_F32)
 //   EPI_BIAS_GELU     -> c = gelu_erf(.) in the operand dtype
 //   EPI_BIAS_RESIDUAL -> c fp32 = residual + (.)   (c may alias residual)
+//   EPI_BIAS_HEADMAJOR-> c in the operand dtype, head-major: row m = b * T + i of window b and
+//                        column n = 64 j + e go to c[((b * (n / 64 count) + j) * T + i) * 64 + e],
+//                        with the window length T passed in ldc.
 // lda / ldc are row strides in elements.  k % 64 == 0, n % 64 == 0.
 hipError_t launch_linear(const void* a, int lda, const void* w, const float* bias,
                          const float* residual, void* c, int ldc, int m, int n, int k, int dtype,

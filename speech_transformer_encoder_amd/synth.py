@@ -176,3 +176,24 @@ def random_qkv(seed: int, batch: int, t: int, heads: int, head_dim: int = 64,
             rows = np.random.default_rng([seed, 1000, 1, w]).choice(t, n, replace=False)
             q[w, rows, :] *= np.float32(outlier_scale)
     return q, k, v
+
+
+# Decoder cross-attention weights for the cross K/V step: tensor ids 21 (Wk), 22 (Wv), 23 (bv)
+# of decoder layer l, drawn with ``default_rng([seed, 100 + l, id])`` like the encoder's.
+CROSS_IDS = {"wk": 21, "wv": 22, "bv": 23}
+
+
+def make_cross_layers(seed: int, n_layers: int, d: int, bf16: bool = True):
+    layers = []
+    for l in range(n_layers):
+        p = {}
+        for name, tid in CROSS_IDS.items():
+            shape = (d,) if name == "bv" else (d, d)
+            std = B_STD if name == "bv" else W_STD
+            rng = np.random.default_rng([seed, 100 + l, tid])
+            arr = (rng.standard_normal(shape, dtype=np.float32) * np.float32(std)).astype(np.float32)
+            if bf16 and name != "bv":
+                arr = round_to_bf16(arr)
+            p[name] = arr
+        layers.append(p)
+    return layers

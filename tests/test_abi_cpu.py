@@ -130,3 +130,21 @@ def test_package_has_no_cpu_fallback():
             if fn.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "import oracle" not in text and "from oracle" not in text, fn
+
+
+def test_cross_kv_sizes_and_validation(lib):
+    assert B.whisper_enc_cross_kv_bytes(1280, 32, B.WENC_PATH_FP16) > 2 * 32 * 1280 * 1280 * 2
+    assert B.whisper_enc_cross_kv_bytes(1280, 0, B.WENC_PATH_FP16) == 0
+    assert B.whisper_enc_cross_kv_bytes(100, 2, B.WENC_PATH_FP16) == 0
+    assert B.whisper_enc_cross_kv_bytes(1280, 65, B.WENC_PATH_FP16) == 0
+    assert B.whisper_enc_cross_kv_workspace_bytes(16, 1500, 1280, B.WENC_PATH_FP16) >= 16 * 1500 * 1280 * 2
+    call = lambda *a: lib.whisper_enc_cross_kv(*a)  # noqa: E731
+    # heads that do not give head_dim 64
+    assert call(FAKE, FAKE, FAKE, 2, 1, 10, 1280, 10, B.WENC_PATH_FP16, FAKE, 1 << 30, None) == B.WENC_ERR_UNSUPPORTED
+    # null output, misaligned weights, small workspace, bad layer count
+    assert call(FAKE, None, FAKE, 2, 1, 10, 1280, 20, B.WENC_PATH_FP16, FAKE, 1 << 30, None) == B.WENC_ERR_ARG
+    assert call(FAKE, FAKE, FAKE + 16, 2, 1, 10, 1280, 20, B.WENC_PATH_FP16, FAKE, 1 << 30, None) == B.WENC_ERR_ARG
+    assert call(FAKE, FAKE, FAKE, 2, 1, 10, 1280, 20, B.WENC_PATH_FP16, FAKE, 16, None) == B.WENC_ERR_WORKSPACE
+    assert call(FAKE, FAKE, FAKE, 0, 1, 10, 1280, 20, B.WENC_PATH_FP16, FAKE, 1 << 30, None) == B.WENC_ERR_ARG
+    # zero rows enqueue nothing
+    assert call(None, None, FAKE, 2, 0, 10, 1280, 20, B.WENC_PATH_FP16, None, 0, None) == B.WENC_OK

@@ -370,3 +370,54 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
             return real_block(x, p, heads) - x
         monkeypatch.setattr(orc, "_window_block", blk)
     assert _hf_check() > 1e-6
+
+
+# ---------------------------------------------------------------- cross-attention keys and values
+
+
+def test_cross_kv_matches_hf_decoder_cross_attention_projections():
+    """The oracle's cross K/V equal the key and value projections of the Hugging Face Whisper
+    decoder layer's encoder attention (its k_proj has no bias, v_proj has one), split by head."""
+    from transformers import WhisperConfig
+    from transformers.models.whisper.modeling_whisper import WhisperDecoderLayer
+    d, heads, t, L = 128, 2, 37, 3
+    cfg = WhisperConfig(d_model=d, decoder_attention_heads=heads, decoder_ffn_dim=256,
+                        dropout=0.0, attention_dropout=0.0, activation_dropout=0.0)
+    r = _rng(77)
+    y = r.standard_normal((2, t, d))
+    dec = []
+    ref = np.empty((2, L, 2, heads, t, d // heads))
+    for l in range(L):
+        layer = WhisperDecoderLayer(cfg).double().eval()
+        ea = layer.encoder_attn
+        assert ea.k_proj.bias is None and ea.v_proj.bias is not None
+        p = {"wk": r.standard_normal((d, d)) * 0.1, "wv": r.standard_normal((d, d)) * 0.1,
+             "bv": r.standard_normal(d) * 0.1}
+        with torch.no_grad():
+            ea.k_proj.weight.copy_(torch.tensor(p["wk"]))
+            ea.v_proj.weight.copy_(torch.tensor(p["wv"]))
+            ea.v_proj.bias.copy_(torch.tensor(p["bv"]))
+            yt = torch.tensor(y)
+            k = ea.k_proj(yt).reshape(2, t, heads, d // heads).transpose(1, 2)
+            v = ea.v_proj(yt).reshape(2, t, heads, d // heads).transpose(1, 2)
+        ref[:, l, 0], ref[:, l, 1] = k.numpy(), v.numpy()
+        dec.append(p)
+    np.testing.assert_allclose(oracle.cross_kv(y, dec, heads), ref, atol=1e-12, rtol=0)
+
+
+def test_cross_kv_closed_forms():
+    """Zero weights give K = 0 and V = bv on every row; a head's slab is the head's columns."""
+    d, heads, t = 128, 2, 9
+    r = _rng(78)
+    y = r.standard_normal((t, d))
+    p = {"wk": np.zeros((d, d)), "wv": np.zeros((d, d)), "bv": r.standard_normal(d)}
+    out = oracle.cross_kv(y, [p], heads)
+    assert out.shape == (1, 1, 2, heads, t, 64)
+    assert np.all(out[0, 0, 0] == 0)
+    for h in range(heads):
+        np.testing.assert_array_equal(out[0, 0, 1, h], np.tile(p["bv"][64 * h:64 * h + 64], (t, 1)))
+    # identity key weights: the key slab of head h is y's columns 64h .. 64h + 63
+    p2 = {"wk": np.eye(d), "wv": np.zeros((d, d)), "bv": np.zeros(d)}
+    out2 = oracle.cross_kv(y, [p2], heads)
+    for h in range(heads):
+        np.testing.assert_array_equal(out2[0, 0, 0, h], y[:, 64 * h:64 * h + 64])

@@ -247,6 +247,39 @@ def time_cross_kv(cfg, path_name, reps):
     return out
 
 
+def time_stem(cfg, path_name, reps):
+    """The step before the first block: the conv front end from 2 t mel frames (the matching
+    Whisper size's mel bins) to the workload's t rows, one C ABI call (unfold, conv1 GEMM + GELU,
+    stride-2 unfold + positions, conv2 GEMM + GELU + positions)."""
+    import torch
+    from speech_transformer_encoder_amd import binding as B
+    from speech_transformer_encoder_amd import synth
+    path = B.PATHS[path_name]
+    d, t2 = cfg.d_model, cfg.t
+    t_mel, n_mels = 2 * t2, synth.N_MELS.get(d, 80)
+    p = synth.make_stem(cfg.seed, n_mels, d, bf16=cfg.bf16_weights, n_pos=t2)
+    dev = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
+    blob = torch.empty(B.whisper_enc_stem_bytes(n_mels, d, t2, path), dtype=torch.uint8,
+                       device="cuda")
+    B.whisper_enc_pack_stem(dev(p["conv1_w"]), dev(p["conv1_b"]), dev(p["conv2_w"]),
+                            dev(p["conv2_b"]), dev(p["pos"]), n_mels, d, t2, path, blob)
+    ws_bytes = B.whisper_enc_stem_workspace_bytes(cfg.batch, t_mel, n_mels, d, path)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    mel = torch.randn(cfg.batch, t_mel, n_mels, device="cuda")
+    x = torch.empty(cfg.batch, t2, d, device="cuda")
+    fn = lambda: B.whisper_enc_stem_forward(mel, x, blob, cfg.batch, t_mel, n_mels, d, t2, path,  # noqa: E731
+                                            ws, ws.numel())
+    ms = time_events(fn, reps, torch.cuda.current_stream())
+    flops = 2.0 * cfg.batch * (t_mel * d * 3 * n_mels + t2 * d * 3 * d)
+    tf = flops / (ms * 1e-3) / 1e12
+    out = {"n_mels": n_mels, "mel_frames": t_mel, "ms": round(ms, 4), "achieved": round(tf, 1),
+           "unit": "TFLOP/s", "peak": PEAK_TFLOPS[path_name],
+           "frac": round(tf / PEAK_TFLOPS[path_name], 4), "work": flops}
+    del blob, ws, mel, x
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, windows, layers):
     """The oracle as it stands, on a bounded sample of the workload (first windows / layers)."""
     import numpy as np
@@ -352,6 +385,7 @@ def main():
 
     next_steps = {}
     if not args.no_next_steps:
+        next_steps["stem"] = time_stem(cfg, args.path, args.kernel_reps)
         next_steps["cross_kv"] = time_cross_kv(cfg, args.path, args.kernel_reps)
 
     cpu = None

@@ -66,6 +66,7 @@ extern "C" {
 #define WENC_EPI_BIAS 0          /* c = a w^T + bias                        (path dtype) */
 #define WENC_EPI_BIAS_GELU 1     /* c = gelu_erf(a w^T + bias)              (path dtype) */
 #define WENC_EPI_BIAS_RESIDUAL 2 /* c = residual + a w^T + bias              (fp32)      */
+#define WENC_EPI_BIAS_GELU_RESIDUAL 3 /* c = residual + gelu_erf(a w^T + bias) (fp32)      */
 
 /* Limits checked by every entry point. */
 #define WENC_HEAD_DIM 64
@@ -73,6 +74,7 @@ extern "C" {
 #define WENC_MAX_FFN_DIM 65536
 #define WENC_MAX_ROWS (1 << 24)
 #define WENC_MAX_DEC_LAYERS 64
+#define WENC_MAX_MELS 1024
 
 /* Human-readable text of a status code (static storage; never NULL). */
 const char* whisper_enc_strerror(int code);
@@ -149,8 +151,10 @@ int whisper_enc_layernorm(const float* x, const float* gamma, const float* beta,
 /*
  * One projection c = epilogue(a w^T + bias): a [m, k] and w [n, k] in the path's operand type
  * (fp32 on WENC_PATH_FP32), bias [n] fp32.  WENC_EPI_BIAS / WENC_EPI_BIAS_GELU write c [m, n]
- * in the operand type; WENC_EPI_BIAS_RESIDUAL writes fp32 c = residual + a w^T + bias with
- * residual [m, n] fp32 (c == residual allowed).  n % 64 == 0, k % 64 == 0.
+ * in the operand type; WENC_EPI_BIAS_RESIDUAL writes fp32 c = residual + a w^T + bias and
+ * WENC_EPI_BIAS_GELU_RESIDUAL fp32 c = residual + gelu_erf(a w^T + bias) (the conv front end's
+ * second convolution plus positions), with residual [m, n] fp32 (c == residual allowed).
+ * n % 64 == 0, k % 64 == 0.
  */
 int whisper_enc_linear(const void* a, const void* w, const float* bias, const float* residual,
                        void* c, int m, int n, int k, int path, int epilogue, void* stream);
@@ -165,6 +169,42 @@ int whisper_enc_linear(const void* a, const void* w, const float* bias, const fl
 int whisper_enc_attention(const void* q, const void* k, const void* v, void* o, int batch, int t,
                           int heads, int ld_qkv, int ld_o, int path, void* stream);
 
+
+/* ---- Conv front end (the step before the first block). ---- */
+
+/*
+ * Whisper's convolutional front end over mel frames (oxinfer whisper/model.rs,
+ * WhisperModel::encode and conv_weight; turbospark-runtime whisper/metal.rs, encode_partial):
+ *   h = gelu(conv1(mel)),  kernel 3, stride 1, padding 1      [t_mel, d]
+ *   x = gelu(conv2(h)) + pos,  kernel 3, stride 2, padding 1    [ceil(t_mel / 2), d]
+ * with frames as rows (a 30 s window is 3000 frames -> 1500 positions).
+ *
+ * whisper_enc_stem_bytes: size of the packed front end (conv weights rearranged to [cout][k][cin]
+ * in the path's operand type, biases and n_pos positional rows fp32), 0 if invalid.
+ */
+size_t whisper_enc_stem_bytes(int n_mels, int d_model, int n_pos, int path);
+
+/*
+ * Pack it from device fp32 arrays in PyTorch layout: conv1_w [d, n_mels, 3], conv1_b [d],
+ * conv2_w [d, d, 3], conv2_b [d], pos [n_pos, d].  dst: device, whisper_enc_stem_bytes() bytes,
+ * 256-byte aligned.  Asynchronous on `stream`; sources must stay valid until it completes.
+ */
+int whisper_enc_pack_stem(const float* conv1_w, const float* conv1_b, const float* conv2_w,
+                          const float* conv2_b, const float* pos, int n_mels, int d_model,
+                          int n_pos, int path, void* dst, void* stream);
+
+/* Workspace for whisper_enc_stem_forward: both unfolded inputs and h, in the operand type. */
+size_t whisper_enc_stem_workspace_bytes(int batch, int t_mel, int n_mels, int d_model, int path);
+
+/*
+ * mel: [batch, t_mel, n_mels] fp32 (16-byte aligned); x: [batch, ceil(t_mel / 2), d_model] fp32,
+ * distinct from mel; needs ceil(t_mel / 2) <= n_pos.  stem: from whisper_enc_pack_stem with the
+ * same n_mels, d_model, n_pos and path.  workspace: device, 256-byte aligned,
+ * >= whisper_enc_stem_workspace_bytes().
+ */
+int whisper_enc_stem_forward(const float* mel, float* x, const void* stem, int batch, int t_mel,
+                             int n_mels, int d_model, int n_pos, int path, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* ---- Cross-attention keys and values for the decoder (the step after the encoder). ---- */
 

@@ -31,6 +31,12 @@ Readings taken where the pages leave a step open:
   * The ``exp`` is the exact one (oxinfer's decoder uses a fast approximation; the encoder
     attention the pages describe uses ``exp``).
 
+The step before the encoder block (the convolutional front end):
+  * ``conv_stem`` - ``h = gelu(conv1(mel))`` (kernel 3, stride 1, padding 1), then
+    ``x = gelu(conv2(h)) + pos`` (kernel 3, stride 2, padding 1) over frames, with frames as rows
+    (oxinfer ``WhisperModel::encode``, conv front end; turbospark-runtime ``encode_partial``,
+    ``encode_whisper_conv1d3_gelu`` and ``encode_whisper_transpose_pos``).
+
 The step after the encoder (cross-attention keys and values of the decoder):
   * ``cross_kv`` - for every decoder layer ``l``, ``K_l = y Wk_l^T`` (no bias) and
     ``V_l = y Wv_l^T + bv_l`` from the encoder output ``y``, stored head-major
@@ -282,3 +288,35 @@ def cross_kv(y, dec_layers: Sequence[Dict[str, np.ndarray]], heads: int) -> np.n
             out[w, l, 0] = _heads(linear(y[w], p["wk"]), heads)
             out[w, l, 1] = _heads(linear(y[w], p["wv"], p["bv"]), heads)
     return out
+
+
+def conv1d_k3(x, w, b, stride: int) -> np.ndarray:
+    """1-D convolution over rows with kernel 3 and zero padding 1: ``x`` ``[t, cin]`` (frames as
+    rows), ``w`` ``[cout, cin, 3]`` (PyTorch layout), ``b`` ``[cout]``; output row ``i`` is
+    ``b + sum_j w[:, :, j] x[stride i + j - 1]`` (terms outside ``[0, t)`` are zero), for
+    ``i < floor((t - 1) / stride) + 1``."""
+    x, w = _f64(x), _f64(w)
+    t = x.shape[0]
+    n = (t - 1) // stride + 1
+    xp = np.zeros((t + 2, x.shape[1]))
+    xp[1:t + 1] = x
+    y = np.tile(_f64(b), (n, 1))
+    for j in range(3):
+        y += xp[j:j + stride * (n - 1) + 1:stride] @ w[:, :, j].T
+    return y
+
+
+def conv_stem(mel, conv1_w, conv1_b, conv2_w, conv2_b, pos) -> np.ndarray:
+    """Whisper's convolutional front end on ``mel`` ``[t, n_mels]`` or ``[batch, t, n_mels]``
+    (frames as rows): ``gelu(conv1)`` with stride 1, ``gelu(conv2)`` with stride 2, plus the
+    positional rows ``pos[i]`` (oxinfer ``encode``: conv1 and conv2 as unfolded projections,
+    ``gelu_erf(v) + p``).  Returns ``[ceil(t / 2), d]`` per window."""
+    mel = _f64(mel)
+    if mel.ndim == 2:
+        mel = mel[None]
+    outs = []
+    for m in mel:
+        h = gelu_erf(conv1d_k3(m, conv1_w, conv1_b, 1))
+        x = gelu_erf(conv1d_k3(h, conv2_w, conv2_b, 2))
+        outs.append(x + _f64(pos)[:x.shape[0]])
+    return np.stack(outs)

@@ -37,6 +37,15 @@ WENC_DTYPE_F16 = 2
 WENC_EPI_BIAS = 0
 WENC_EPI_BIAS_GELU = 1
 WENC_EPI_BIAS_RESIDUAL = 2
+WENC_EPI_BIAS_GELU_RESIDUAL = 3
+
+# Limits checked by every entry point.
+WENC_HEAD_DIM = 64
+WENC_MAX_D_MODEL = 4096
+WENC_MAX_FFN_DIM = 65536
+WENC_MAX_ROWS = 1 << 24
+WENC_MAX_DEC_LAYERS = 64
+WENC_MAX_MELS = 1024
 
 HEAD_DIM = 64
 
@@ -46,6 +55,8 @@ EXPORTS = (
     "whisper_enc_layernorm", "whisper_enc_linear", "whisper_enc_attention",
     "whisper_enc_cross_kv_bytes", "whisper_enc_pack_cross_kv",
     "whisper_enc_cross_kv_workspace_bytes", "whisper_enc_cross_kv",
+    "whisper_enc_stem_bytes", "whisper_enc_pack_stem", "whisper_enc_stem_workspace_bytes",
+    "whisper_enc_stem_forward",
 )
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -82,6 +93,10 @@ def load() -> ctypes.CDLL:
         "whisper_enc_pack_cross_kv": (I, [P, P, P, I, I, I, P, P]),
         "whisper_enc_cross_kv_workspace_bytes": (Z, [I, I, I, I]),
         "whisper_enc_cross_kv": (I, [P, P, P, I, I, I, I, I, I, P, Z, P]),
+        "whisper_enc_stem_bytes": (Z, [I, I, I, I]),
+        "whisper_enc_pack_stem": (I, [P, P, P, P, P, I, I, I, I, P, P]),
+        "whisper_enc_stem_workspace_bytes": (Z, [I, I, I, I, I]),
+        "whisper_enc_stem_forward": (I, [P, P, P, I, I, I, I, I, I, P, Z, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -194,3 +209,26 @@ def whisper_enc_cross_kv(y, kv, wkv, n_dec_layers, batch, t, d_model, heads, pat
     _check(load().whisper_enc_cross_kv(_ptr(y), _ptr(kv), _ptr(wkv), n_dec_layers, batch, t,
                                        d_model, heads, path, _ptr(workspace), workspace_bytes,
                                        _stream(stream)), "whisper_enc_cross_kv")
+
+
+def whisper_enc_stem_bytes(n_mels: int, d_model: int, n_pos: int, path: int) -> int:
+    return load().whisper_enc_stem_bytes(n_mels, d_model, n_pos, path)
+
+
+def whisper_enc_stem_workspace_bytes(batch: int, t_mel: int, n_mels: int, d_model: int,
+                                     path: int) -> int:
+    return load().whisper_enc_stem_workspace_bytes(batch, t_mel, n_mels, d_model, path)
+
+
+def whisper_enc_pack_stem(conv1_w, conv1_b, conv2_w, conv2_b, pos, n_mels, d_model, n_pos, path,
+                          dst, stream=None) -> None:
+    _check(load().whisper_enc_pack_stem(_ptr(conv1_w), _ptr(conv1_b), _ptr(conv2_w),
+                                        _ptr(conv2_b), _ptr(pos), n_mels, d_model, n_pos, path,
+                                        _ptr(dst), _stream(stream)), "whisper_enc_pack_stem")
+
+
+def whisper_enc_stem_forward(mel, x, stem, batch, t_mel, n_mels, d_model, n_pos, path, workspace,
+                             workspace_bytes, stream=None) -> None:
+    _check(load().whisper_enc_stem_forward(_ptr(mel), _ptr(x), _ptr(stem), batch, t_mel, n_mels,
+                                           d_model, n_pos, path, _ptr(workspace), workspace_bytes,
+                                           _stream(stream)), "whisper_enc_stem_forward")

@@ -273,22 +273,24 @@ int whisper_enc_linear(const void* a, const void* w, const float* bias, const fl
   const int dt = path_dtype(path);
   if (dt < 0) return WENC_ERR_ARG;
   if (epilogue != WENC_EPI_BIAS && epilogue != WENC_EPI_BIAS_GELU &&
-      epilogue != WENC_EPI_BIAS_RESIDUAL)
+      epilogue != WENC_EPI_BIAS_RESIDUAL && epilogue != WENC_EPI_BIAS_GELU_RESIDUAL)
     return WENC_ERR_ARG;
+  const bool fp32_out = epilogue == WENC_EPI_BIAS_RESIDUAL || epilogue == WENC_EPI_BIAS_GELU_RESIDUAL;
   if (m < 0 || m > WENC_MAX_ROWS || n < 64 || k < 64 || n % 64 || k % 64 || n > WENC_MAX_FFN_DIM ||
       k > WENC_MAX_FFN_DIM)
     return WENC_ERR_ARG;
   if (m == 0) return WENC_OK;
   if (!a || !w || !bias || !c) return WENC_ERR_ARG;
-  if (epilogue == WENC_EPI_BIAS_RESIDUAL && !residual) return WENC_ERR_ARG;
+  if (fp32_out && !residual) return WENC_ERR_ARG;
   if (!aligned(a, 16) || !aligned(w, 16) || !aligned(bias, 16) || !aligned(c, 16) ||
       (residual && !aligned(residual, 16)))
     return WENC_ERR_ARG;
-  if (epilogue == WENC_EPI_BIAS_RESIDUAL &&
-      overlaps_partially(residual, c, (size_t)m * n * sizeof(float)))
+  if (fp32_out && overlaps_partially(residual, c, (size_t)m * n * sizeof(float)))
     return WENC_ERR_ARG;
-  const int epi = epilogue == WENC_EPI_BIAS ? EPI_BIAS
-                  : epilogue == WENC_EPI_BIAS_GELU ? EPI_BIAS_GELU : EPI_BIAS_RESIDUAL;
+  const int epi = epilogue == WENC_EPI_BIAS        ? EPI_BIAS
+                  : epilogue == WENC_EPI_BIAS_GELU ? EPI_BIAS_GELU
+                  : epilogue == WENC_EPI_BIAS_RESIDUAL ? EPI_BIAS_RESIDUAL
+                                                       : EPI_BIAS_GELU_RESIDUAL;
   WENC_TRY(launch_linear(a, k, w, bias, residual, c, n, m, n, k, dt, epi,
                          static_cast<hipStream_t>(stream)));
   return WENC_OK;
@@ -402,6 +404,132 @@ int whisper_enc_cross_kv(const float* y, void* kv, const void* wkv, int n_dec_la
   }
   WENC_TRY(launch_linear(a, d, blob + L.w, reinterpret_cast<const float*>(blob + L.bias), nullptr,
                          kv, t, (int)rows, n, d, dt, EPI_BIAS_HEADMAJOR, st));
+  return WENC_OK;
+}
+
+}  // extern "C"
+
+// ---- Conv front end (oxinfer WhisperModel::encode, conv1 / conv2 / positions; turbospark-runtime
+// encode_partial): unfold, GEMM + GELU, unfold with stride 2, GEMM + GELU + positions. ----
+
+namespace {
+
+int stem_k1(int n_mels) { return (3 * n_mels + 63) / 64 * 64; }
+
+struct StemLayout {
+  size_t b1, b2, pos, w1, w2, total;
+};
+
+StemLayout stem_layout(int n_mels, int d, int n_pos, int path) {
+  StemLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += round_up(bytes);
+    return o;
+  };
+  const size_t es = elem_bytes(path);
+  L.b1 = take(4 * (size_t)d);
+  L.b2 = take(4 * (size_t)d);
+  L.pos = take(4 * (size_t)n_pos * d);
+  L.w1 = take(es * (size_t)d * stem_k1(n_mels));
+  L.w2 = take(es * (size_t)d * 3 * d);
+  L.total = off;
+  return L;
+}
+
+bool valid_stem(int n_mels, int d, int n_pos, int path) {
+  return path_dtype(path) >= 0 && n_mels >= 1 && n_mels <= WENC_MAX_MELS && d >= 64 &&
+         d <= WENC_MAX_D_MODEL && d % 64 == 0 && n_pos >= 1 && n_pos <= WENC_MAX_ROWS;
+}
+
+struct StemWorkspace {
+  void* cols1;  // [B t, k1]
+  void* h;      // [B t, d]
+  void* cols2;  // [B t2, 3 d]
+  size_t total;
+};
+
+StemWorkspace stem_workspace(void* base, size_t batch, int t, int n_mels, int d, int path) {
+  const size_t es = elem_bytes(path);
+  const size_t t2 = (size_t)(t + 1) / 2;
+  StemWorkspace w;
+  char* p = static_cast<char*>(base);
+  const size_t a = round_up(batch * t * stem_k1(n_mels) * es);
+  const size_t b = round_up(batch * t * d * es);
+  const size_t c = round_up(batch * t2 * 3 * d * es);
+  w.cols1 = p;
+  w.h = p ? p + a : nullptr;
+  w.cols2 = p ? p + a + b : nullptr;
+  w.total = a + b + c;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t whisper_enc_stem_bytes(int n_mels, int d_model, int n_pos, int path) {
+  if (!valid_stem(n_mels, d_model, n_pos, path)) return 0;
+  return stem_layout(n_mels, d_model, n_pos, path).total;
+}
+
+int whisper_enc_pack_stem(const float* conv1_w, const float* conv1_b, const float* conv2_w,
+                          const float* conv2_b, const float* pos, int n_mels, int d_model,
+                          int n_pos, int path, void* dst, void* stream) {
+  if (!valid_stem(n_mels, d_model, n_pos, path)) return WENC_ERR_ARG;
+  if (!conv1_w || !conv1_b || !conv2_w || !conv2_b || !pos) return WENC_ERR_ARG;
+  if (!dst || !aligned(dst, kAlign)) return WENC_ERR_ARG;
+  const int d = d_model, dt = path_dtype(path);
+  const StemLayout L = stem_layout(n_mels, d, n_pos, path);
+  char* blob = static_cast<char*>(dst);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  WENC_TRY(launch_copy_or_zero(conv1_b, reinterpret_cast<float*>(blob + L.b1), d, st));
+  WENC_TRY(launch_copy_or_zero(conv2_b, reinterpret_cast<float*>(blob + L.b2), d, st));
+  WENC_TRY(launch_copy_or_zero(pos, reinterpret_cast<float*>(blob + L.pos), (size_t)n_pos * d, st));
+  WENC_TRY(launch_pack_conv(conv1_w, blob + L.w1, d, n_mels, stem_k1(n_mels), dt, st));
+  WENC_TRY(launch_pack_conv(conv2_w, blob + L.w2, d, d, 3 * d, dt, st));
+  return WENC_OK;
+}
+
+size_t whisper_enc_stem_workspace_bytes(int batch, int t_mel, int n_mels, int d_model, int path) {
+  if (!valid_stem(n_mels, d_model, 1, path) || batch < 0 || t_mel < 0 ||
+      (long long)batch * t_mel > WENC_MAX_ROWS)
+    return 0;
+  return stem_workspace(nullptr, (size_t)batch, t_mel, n_mels, d_model, path).total;
+}
+
+int whisper_enc_stem_forward(const float* mel, float* x, const void* stem, int batch, int t_mel,
+                             int n_mels, int d_model, int n_pos, int path, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!valid_stem(n_mels, d_model, n_pos, path)) return WENC_ERR_ARG;
+  if (batch < 0 || t_mel < 0 || (long long)batch * t_mel > WENC_MAX_ROWS) return WENC_ERR_ARG;
+  const int t2 = (t_mel + 1) / 2;
+  if (t2 > n_pos) return WENC_ERR_ARG;
+  if ((size_t)batch * t_mel == 0) return WENC_OK;
+  if (!mel || !x || !stem || !workspace) return WENC_ERR_ARG;
+  if (!aligned(mel, 16) || !aligned(x, 16) || !aligned(stem, kAlign) || !aligned(workspace, kAlign))
+    return WENC_ERR_ARG;
+  {
+    const uintptr_t pm = (uintptr_t)mel, px = (uintptr_t)x;
+    const size_t mel_bytes = (size_t)batch * t_mel * n_mels * sizeof(float);
+    const size_t x_bytes = (size_t)batch * t2 * d_model * sizeof(float);
+    if (pm < px + x_bytes && px < pm + mel_bytes) return WENC_ERR_ARG;  // x must not alias mel
+  }
+  const StemWorkspace w = stem_workspace(workspace, (size_t)batch, t_mel, n_mels, d_model, path);
+  if (workspace_bytes < w.total) return WENC_ERR_WORKSPACE;
+  const int d = d_model, dt = path_dtype(path), k1 = stem_k1(n_mels);
+  const StemLayout L = stem_layout(n_mels, d, n_pos, path);
+  const char* blob = static_cast<const char*>(stem);
+  auto fp = [&](size_t off) { return reinterpret_cast<const float*>(blob + off); };
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int m1 = batch * t_mel, m2 = batch * t2;
+  WENC_TRY(launch_unfold_s1(mel, w.cols1, batch, t_mel, n_mels, k1, dt, st));
+  WENC_TRY(launch_linear(w.cols1, k1, blob + L.w1, fp(L.b1), nullptr, w.h, d, m1, d, k1, dt,
+                         EPI_BIAS_GELU, st));
+  WENC_TRY(launch_unfold_s2(w.h, w.cols2, fp(L.pos), x, batch, t_mel, t2, d, dt, st));
+  WENC_TRY(launch_linear(w.cols2, 3 * d, blob + L.w2, fp(L.b2), x, x, d, m2, d, 3 * d, dt,
+                         EPI_BIAS_GELU_RESIDUAL, st));
   return WENC_OK;
 }
 

@@ -223,7 +223,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
       }
     if (!cols_ok) continue;
     const int mb = m0 + wm * G_TM + b * 32;
-    if constexpr (EPI == EPI_BIAS_RESIDUAL) {
+    if constexpr (EPI == EPI_BIAS_RESIDUAL || EPI == EPI_BIAS_GELU_RESIDUAL) {
       // fp32 rows of 64 columns: 16 lanes per row, 4 rows per instruction.  All residual loads
       // are issued before the first store.
       float4 res[8];
@@ -238,7 +238,9 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
       for (int q = 0; q < 8; ++q) {
         const int r = (lane >> 4) + 4 * q, c = lane & 15;
         const int m = mb + r;
-        const float4 v4 = *reinterpret_cast<const float4*>(ep + r * 64 + ((c ^ (r & 15)) << 2));
+        float4 v4 = *reinterpret_cast<const float4*>(ep + r * 64 + ((c ^ (r & 15)) << 2));
+        if constexpr (EPI == EPI_BIAS_GELU_RESIDUAL)
+          v4 = make_float4(gelu_erf_as(v4.x), gelu_erf_as(v4.y), gelu_erf_as(v4.z), gelu_erf_as(v4.w));
         if (m < M)
           *reinterpret_cast<float4*>(static_cast<float*>(C) + (size_t)m * ldc + nw + 4 * c) =
               make_float4(res[q].x + v4.x, res[q].y + v4.y, res[q].z + v4.z, res[q].w + v4.w);
@@ -415,7 +417,7 @@ __global__ __launch_bounds__(H_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
       }
     if (!cols_ok) continue;
     const int mb = m0 + wm * H_TM + b * 32;
-    if constexpr (EPI == EPI_BIAS_RESIDUAL) {
+    if constexpr (EPI == EPI_BIAS_RESIDUAL || EPI == EPI_BIAS_GELU_RESIDUAL) {
       float4 res[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -427,7 +429,9 @@ __global__ __launch_bounds__(H_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
       for (int q = 0; q < 8; ++q) {
         const int r = (lane >> 4) + 4 * q, c = lane & 15;
         const int m = mb + r;
-        const float4 v4 = *reinterpret_cast<const float4*>(ep + r * 64 + ((c ^ (r & 15)) << 2));
+        float4 v4 = *reinterpret_cast<const float4*>(ep + r * 64 + ((c ^ (r & 15)) << 2));
+        if constexpr (EPI == EPI_BIAS_GELU_RESIDUAL)
+          v4 = make_float4(gelu_erf_as(v4.x), gelu_erf_as(v4.y), gelu_erf_as(v4.z), gelu_erf_as(v4.w));
         if (m < M)
           *reinterpret_cast<float4*>(static_cast<float*>(C) + (size_t)m * ldc + nw + 4 * c) =
               make_float4(res[q].x + v4.x, res[q].y + v4.y, res[q].z + v4.z, res[q].w + v4.w);
@@ -562,7 +566,9 @@ __global__ __launch_bounds__(256) void gemm32_kernel(const float* __restrict__ X
                                acc[a][b][4 * j + 2] + bb.z, acc[a][b][4 * j + 3] + bb.w);
         const size_t off = EPI == EPI_BIAS_HEADMAJOR ? headmajor_offset(m, n, N, ldc)
                                                      : (size_t)m * ldc + n;
-        if constexpr (EPI == EPI_BIAS_RESIDUAL) {
+        if constexpr (EPI == EPI_BIAS_GELU_RESIDUAL)
+          v = make_float4(gelu_erf(v.x), gelu_erf(v.y), gelu_erf(v.z), gelu_erf(v.w));
+        if constexpr (EPI == EPI_BIAS_RESIDUAL || EPI == EPI_BIAS_GELU_RESIDUAL) {
           const float4 r = *reinterpret_cast<const float4*>(residual + off);
           v = make_float4(r.x + v.x, r.y + v.y, r.z + v.z, r.w + v.w);
         } else if constexpr (EPI == EPI_BIAS_GELU) {
@@ -606,6 +612,9 @@ static hipError_t launch16(const void* a, int lda, const void* w, const float* b
     case EPI_BIAS_HEADMAJOR:
       launch16_epi<T, EPI_BIAS_HEADMAJOR>(X, lda, W, bias, residual, c, ldc, m, n, k, st);
       break;
+    case EPI_BIAS_GELU_RESIDUAL:
+      launch16_epi<T, EPI_BIAS_GELU_RESIDUAL>(X, lda, W, bias, residual, c, ldc, m, n, k, st);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -632,6 +641,10 @@ static hipError_t launch32(const void* a, int lda, const void* w, const float* b
     case EPI_BIAS_HEADMAJOR:
       gemm32_kernel<EPI_BIAS_HEADMAJOR><<<grid, block, 0, st>>>(X, lda, W, bias, residual, C, ldc,
                                                                 m, n, k);
+      break;
+    case EPI_BIAS_GELU_RESIDUAL:
+      gemm32_kernel<EPI_BIAS_GELU_RESIDUAL><<<grid, block, 0, st>>>(X, lda, W, bias, residual, C,
+                                                                    ldc, m, n, k);
       break;
     default: return hipErrorInvalidValue;
   }

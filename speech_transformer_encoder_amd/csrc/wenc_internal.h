@@ -9,7 +9,13 @@
 namespace wenc {
 
 enum DType { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
-enum Epilogue { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_BIAS_HEADMAJOR = 3 };
+enum Epilogue {
+  EPI_BIAS = 0,
+  EPI_BIAS_GELU = 1,
+  EPI_BIAS_RESIDUAL = 2,
+  EPI_BIAS_HEADMAJOR = 3,
+  EPI_BIAS_GELU_RESIDUAL = 4
+};
 
 // y[rows, d] = LayerNorm(x[rows, d]) * gamma + beta, stored as out_dtype.  d % 4 == 0, d <= 4096.
 hipError_t launch_layernorm(const float* x, const float* gamma, const float* beta, void* y,
@@ -19,6 +25,7 @@ hipError_t launch_layernorm(const float* x, const float* gamma, const float* bet
 //   EPI_BIAS          -> c in the operand dtype (fp32 for DT_F32)
 //   EPI_BIAS_GELU     -> c = gelu_erf(.) in the operand dtype
 //   EPI_BIAS_RESIDUAL -> c fp32 = residual + (.)   (c may alias residual)
+//   EPI_BIAS_GELU_RESIDUAL -> c fp32 = residual + gelu_erf(.)   (c may alias residual)
 //   EPI_BIAS_HEADMAJOR-> c in the operand dtype, head-major: row m = b * T + i of window b and
 //                        column n = 64 j + e go to c[((b * (n / 64 count) + j) * T + i) * 64 + e],
 //                        with the window length T passed in ldc.
@@ -37,5 +44,16 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int ld_
 hipError_t launch_convert(const float* src, void* dst, size_t n, int dtype, hipStream_t st);
 // dst[i] = src ? src[i] : 0 for i < n (fp32).
 hipError_t launch_copy_or_zero(const float* src, float* dst, size_t n, hipStream_t st);
+
+// Conv front end rearrangements (stem.hip).  dst[o][j * cin + i] = w[o][i][j] (zero past 3 cin,
+// kp columns); unfold_s1: out[b t + i][j c + q] = src[b][i + j - 1][q] (fp32 src, kp columns);
+// unfold_s2: out[b t2 + i][j d + q] = src[b t + 2 i + j - 1][q] (src in dtype) and
+// pos_out[b t2 + i] = pos[i].  Zeros outside each window.
+hipError_t launch_pack_conv(const float* w, void* dst, int cout, int cin, int kp, int dtype,
+                            hipStream_t st);
+hipError_t launch_unfold_s1(const float* src, void* out, int batch, int t, int c, int kp,
+                            int dtype, hipStream_t st);
+hipError_t launch_unfold_s2(const void* src, void* out, const float* pos, float* pos_out,
+                            int batch, int t, int t2, int d, int dtype, hipStream_t st);
 
 }  // namespace wenc

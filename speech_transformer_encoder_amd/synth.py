@@ -197,3 +197,42 @@ def make_cross_layers(seed: int, n_layers: int, d: int, bf16: bool = True):
             p[name] = arr
         layers.append(p)
     return layers
+
+
+# Conv front end inputs.  A 30 s window is 3000 mel frames (two per encoder position).  Whisper's
+# log-mel features are clipped to 8 decades below the window's maximum and mapped by
+# (log10 + 4) / 4, so they lie in about [-1, 1.5]; the synthetic frames are N(0.2, 0.4^2).
+# Conv weights: tensor ids 31 (conv1_w), 32 (conv1_b), 33 (conv2_w), 34 (conv2_b), drawn like
+# the block's (N(0, 0.02^2) weights, N(0, 0.01^2) biases).  Positions: the sinusoidal table of
+# the Whisper encoder (sin of position / 10000^(k / (d/2 - 1)) in the first half of the row, cos
+# in the second).
+N_MELS = {384: 80, 512: 80, 768: 80, 1280: 128}
+STEM_IDS = {"conv1_w": 31, "conv1_b": 32, "conv2_w": 33, "conv2_b": 34}
+
+
+def make_mel(seed: int, batch: int, frames: int, n_mels: int) -> np.ndarray:
+    rng = np.random.default_rng([seed, 200, 0])
+    return (rng.standard_normal((batch, frames, n_mels), dtype=np.float32) * np.float32(0.4)
+            + np.float32(0.2)).astype(np.float32)
+
+
+def sinusoid_positions(n: int, d: int) -> np.ndarray:
+    half = d // 2
+    inc = np.log(10000.0) / (half - 1)
+    inv = np.exp(-inc * np.arange(half))
+    ang = np.arange(n)[:, None] * inv[None, :]
+    return np.concatenate([np.sin(ang), np.cos(ang)], axis=1).astype(np.float32)
+
+
+def make_stem(seed: int, n_mels: int, d: int, bf16: bool = True, n_pos: int = 1500):
+    shapes = {"conv1_w": (d, n_mels, 3), "conv1_b": (d,), "conv2_w": (d, d, 3), "conv2_b": (d,)}
+    p = {}
+    for name, shp in shapes.items():
+        rng = np.random.default_rng([seed, 200, STEM_IDS[name]])
+        std = W_STD if name.endswith("_w") else B_STD
+        arr = (rng.standard_normal(shp, dtype=np.float32) * np.float32(std)).astype(np.float32)
+        if bf16 and name.endswith("_w"):
+            arr = round_to_bf16(arr)
+        p[name] = arr
+    p["pos"] = sinusoid_positions(n_pos, d)
+    return p

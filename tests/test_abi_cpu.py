@@ -30,6 +30,15 @@ def test_header_declares_the_abi():
     assert declared_functions() == sorted(B.EXPORTS)
 
 
+def test_header_constants_match_binding():
+    """Every #define WENC_* integer in the header has the same value in the Python binding."""
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"^#define\s+(WENC_\w+)\s+(-?\d+)\b", text, re.M))
+    assert len(consts) > 10
+    for name, value in consts.items():
+        assert getattr(B, name) == int(value), name
+
+
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
@@ -148,3 +157,33 @@ def test_cross_kv_sizes_and_validation(lib):
     assert call(FAKE, FAKE, FAKE, 0, 1, 10, 1280, 20, B.WENC_PATH_FP16, FAKE, 1 << 30, None) == B.WENC_ERR_ARG
     # zero rows enqueue nothing
     assert call(None, None, FAKE, 2, 0, 10, 1280, 20, B.WENC_PATH_FP16, None, 0, None) == B.WENC_OK
+
+
+def test_stem_sizes_and_validation(lib):
+    # large-v3 front end: 128 mel bins, width 1280, 1500 positions
+    n = B.whisper_enc_stem_bytes(128, 1280, 1500, B.WENC_PATH_FP16)
+    assert n >= (1280 * 384 + 1280 * 3 * 1280) * 2 + 1500 * 1280 * 4
+    assert B.whisper_enc_stem_bytes(0, 1280, 1500, B.WENC_PATH_FP16) == 0
+    assert B.whisper_enc_stem_bytes(128, 100, 1500, B.WENC_PATH_FP16) == 0
+    assert B.whisper_enc_stem_bytes(128, 1280, 0, B.WENC_PATH_FP16) == 0
+    ws = B.whisper_enc_stem_workspace_bytes(16, 3000, 128, 1280, B.WENC_PATH_FP16)
+    assert ws >= 16 * 3000 * (384 + 1280) * 2 + 16 * 1500 * 3 * 1280 * 2
+    call = lambda *a: lib.whisper_enc_stem_forward(*a)  # noqa: E731
+
+    def go(mel=FAKE, x=1 << 40, stem=FAKE, batch=2, t=3000, mels=128, d=1280, npos=1500,
+           path=B.WENC_PATH_FP16, ws=FAKE, wsb=1 << 34):
+        return call(mel, x, stem, batch, t, mels, d, npos, path, ws, wsb, None)
+
+    # more positions needed than packed, width not a multiple of 64, null output
+    assert go(t=3002) == B.WENC_ERR_ARG
+    assert go(d=1000) == B.WENC_ERR_ARG
+    assert go(x=None) == B.WENC_ERR_ARG
+    # misaligned stem, x overlapping mel, small workspace
+    assert go(stem=FAKE + 16) == B.WENC_ERR_ARG
+    assert go(x=FAKE) == B.WENC_ERR_ARG
+    assert go(x=FAKE + 4096) == B.WENC_ERR_ARG
+    assert go(wsb=16) == B.WENC_ERR_WORKSPACE
+    # odd frame counts take ceil(t / 2) positions
+    assert go(t=2999, npos=1500, wsb=16) == B.WENC_ERR_WORKSPACE
+    # no frames enqueue nothing
+    assert go(mel=None, x=None, stem=FAKE, t=0, ws=None, wsb=0) == B.WENC_OK

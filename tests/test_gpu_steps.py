@@ -62,7 +62,8 @@ def test_layernorm_in_place_fp32():
 
 
 @pytest.mark.parametrize("path", PATHS)
-@pytest.mark.parametrize("epi", [B.WENC_EPI_BIAS, B.WENC_EPI_BIAS_GELU, B.WENC_EPI_BIAS_RESIDUAL])
+@pytest.mark.parametrize("epi", [B.WENC_EPI_BIAS, B.WENC_EPI_BIAS_GELU, B.WENC_EPI_BIAS_RESIDUAL,
+                                 B.WENC_EPI_BIAS_GELU_RESIDUAL])
 @pytest.mark.parametrize("m,n,k", [(1, 64, 64), (200, 384, 384), (257, 192, 512), (1500, 1152, 384),
                                    (129, 1280, 5120), (6000, 4160, 128), (24000, 1280, 64)])
 def test_linear(path, epi, m, n, k):
@@ -75,10 +76,13 @@ def test_linear(path, epi, m, n, k):
     wd, wh = as_operand(w, path)
     ref = oracle.linear(ah, wh, bias)
     resid = None
-    if epi == B.WENC_EPI_BIAS_RESIDUAL:
+    fp32_out = epi in (B.WENC_EPI_BIAS_RESIDUAL, B.WENC_EPI_BIAS_GELU_RESIDUAL)
+    if fp32_out:
         res_np = r.standard_normal((m, n)).astype(np.float32) * 4
         resid = dev(res_np)
         c = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        if epi == B.WENC_EPI_BIAS_GELU_RESIDUAL:
+            ref = oracle.gelu_erf(ref)
         ref = ref + res_np
     else:
         c = torch.empty((m, n), dtype=torch_dtype(path), device="cuda")
@@ -88,7 +92,7 @@ def test_linear(path, epi, m, n, k):
     B.whisper_enc_linear(ad, wd, dev(bias), resid, c, m, n, k, path, epi)
     e = errors(host(c), ref)
     report(f"linear p{path} e{epi} {m}x{n}x{k}", e)
-    tol = 2e-5 if epi == B.WENC_EPI_BIAS_RESIDUAL else OUT_TOL[path]
+    tol = 2e-5 if fp32_out else OUT_TOL[path]
     assert e["finite"] and e["max_rel"] <= tol
 
 

@@ -421,3 +421,59 @@ def test_cross_kv_closed_forms():
     out2 = oracle.cross_kv(y, [p2], heads)
     for h in range(heads):
         np.testing.assert_array_equal(out2[0, 0, 0, h], y[:, 64 * h:64 * h + 64])
+
+
+# ---------------------------------------------------------------- conv front end
+
+
+@pytest.mark.parametrize("t,cin,cout,stride", [(3000, 8, 16, 1), (3000, 16, 8, 2), (7, 3, 5, 2),
+                                               (1, 4, 4, 2), (2, 4, 4, 2)])
+def test_conv1d_k3_matches_torch(t, cin, cout, stride):
+    r = _rng(t + cin + stride)
+    x, w, b = r.standard_normal((t, cin)), r.standard_normal((cout, cin, 3)), r.standard_normal(cout)
+    ref = torch.nn.functional.conv1d(torch.tensor(x.T[None]), torch.tensor(w), torch.tensor(b),
+                                     stride=stride, padding=1)[0].numpy().T
+    np.testing.assert_allclose(oracle.conv1d_k3(x, w, b, stride), ref, atol=1e-12, rtol=0)
+
+
+def test_conv1d_k3_brute_force():
+    r = _rng(81)
+    x, w, b = r.standard_normal((5, 2)), r.standard_normal((3, 2, 3)), r.standard_normal(3)
+    for stride in (1, 2):
+        n = (5 - 1) // stride + 1
+        ref = [[b[o] + sum(w[o, c, j] * x[stride * i + j - 1, c]
+                           for c in range(2) for j in range(3) if 0 <= stride * i + j - 1 < 5)
+                for o in range(3)] for i in range(n)]
+        np.testing.assert_allclose(oracle.conv1d_k3(x, w, b, stride), ref, atol=1e-13)
+
+
+def test_conv_stem_matches_hf_whisper_encoder_front_end():
+    """Hugging Face's WhisperEncoder applies conv1 + GELU, conv2 + GELU and adds its positional
+    embedding before the first layer; with no layers and no final norm its output is the stem's."""
+    from transformers import WhisperConfig
+    from transformers.models.whisper.modeling_whisper import WhisperEncoder
+    d, n_mels, frames = 128, 16, 60
+    cfg = WhisperConfig(d_model=d, num_mel_bins=n_mels, encoder_layers=0, encoder_attention_heads=2,
+                        max_source_positions=frames // 2, dropout=0.0)
+    enc = WhisperEncoder(cfg).double().eval()
+    r = _rng(82)
+    p = {"conv1_w": r.standard_normal((d, n_mels, 3)) * 0.1, "conv1_b": r.standard_normal(d) * 0.1,
+         "conv2_w": r.standard_normal((d, d, 3)) * 0.05, "conv2_b": r.standard_normal(d) * 0.1,
+         "pos": r.standard_normal((frames // 2, d))}
+    with torch.no_grad():
+        enc.conv1.weight.copy_(torch.tensor(p["conv1_w"])); enc.conv1.bias.copy_(torch.tensor(p["conv1_b"]))
+        enc.conv2.weight.copy_(torch.tensor(p["conv2_w"])); enc.conv2.bias.copy_(torch.tensor(p["conv2_b"]))
+        enc.embed_positions.weight.copy_(torch.tensor(p["pos"]))
+        enc.layer_norm = torch.nn.Identity()
+        mel = r.standard_normal((2, frames, n_mels))
+        ref = enc(torch.tensor(mel.transpose(0, 2, 1))).last_hidden_state.numpy()
+    got = oracle.conv_stem(mel, p["conv1_w"], p["conv1_b"], p["conv2_w"], p["conv2_b"], p["pos"])
+    np.testing.assert_allclose(got, ref, atol=1e-11, rtol=0)
+
+
+def test_sinusoid_positions_closed_form():
+    pos = synth.sinusoid_positions(1500, 1280)
+    assert pos.shape == (1500, 1280)
+    np.testing.assert_array_equal(pos[0, :640], 0.0)
+    np.testing.assert_array_equal(pos[0, 640:], 1.0)
+    np.testing.assert_allclose(pos[1, 0], math.sin(1.0), rtol=1e-6)

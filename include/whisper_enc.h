@@ -169,6 +169,46 @@ int whisper_enc_linear(const void* a, const void* w, const float* bias, const fl
 int whisper_enc_attention(const void* q, const void* k, const void* v, void* o, int batch, int t,
                           int heads, int ld_qkv, int ld_o, int path, void* stream);
 
+/* ---- Ragged batches: windows of different lengths packed back to back. ---- */
+
+/*
+ * The pages encode one window of t <= max_t rows at a time (inferencelayer
+ * WhisperEncoderGpu::forward checks t against max_t), or pad every window to 30 s
+ * (turbospark-runtime module doc, buffering).  Here `batch` windows of different lengths share
+ * one call without padding: window b is rows cu_seqlens[b] .. cu_seqlens[b + 1] - 1 of a packed
+ * [total_rows, ...] array, and attends only within itself.
+ *
+ * cu_seqlens: DEVICE int32 [batch + 1], read by the kernels on `stream` (not by the host), with
+ * cu_seqlens[0] = 0, non-decreasing, cu_seqlens[batch] = total_rows and every window at most
+ * max_t rows.  The kernels skip a window whose entries break 0 <= cu[b] <= cu[b + 1] <=
+ * total_rows or cu[b + 1] - cu[b] <= max_t, and never address rows outside [0, total_rows); the
+ * output rows of a skipped window, and rows that no window covers, are unspecified.  The host
+ * checks total_rows <= batch * max_t.  Zero-length windows are allowed.
+ *
+ * whisper_enc_varlen_workspace_bytes: workspace for whisper_enc_stack_forward_varlen (the dense
+ * call's, for total_rows rows), 0 if the shape is invalid.
+ */
+size_t whisper_enc_varlen_workspace_bytes(int batch, int total_rows, int max_t, int d_model,
+                                          int heads, int ffn_dim, int path);
+
+/*
+ * whisper_enc_stack_forward over a ragged batch: x, y [total_rows, d_model] fp32; other arguments
+ * as for whisper_enc_stack_forward, with max_t in place of t for the per-window limits.
+ */
+int whisper_enc_stack_forward_varlen(const float* x, float* y, const void* layers, int n_layers,
+                                     const float* ln_post_g, const float* ln_post_b,
+                                     const int* cu_seqlens, int batch, int total_rows, int max_t,
+                                     int d_model, int heads, int ffn_dim, int path,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * whisper_enc_attention over a ragged batch: row i of window b at ptr + (cu_seqlens[b] + i) * ld.
+ * max_t * ld_qkv elements must span less than 2 GiB (else WENC_ERR_UNSUPPORTED).
+ */
+int whisper_enc_attention_varlen(const void* q, const void* k, const void* v, void* o,
+                                 const int* cu_seqlens, int batch, int total_rows, int max_t,
+                                 int heads, int ld_qkv, int ld_o, int path, void* stream);
+
 
 /* ---- Conv front end (the step before the first block). ---- */
 

@@ -31,6 +31,11 @@ Readings taken where the pages leave a step open:
   * The ``exp`` is the exact one (oxinfer's decoder uses a fast approximation; the encoder
     attention the pages describe uses ``exp``).
 
+Ragged batches (windows of different lengths packed back to back, no padding):
+  * ``encoder_stack_varlen`` - each window through the stack on its own; the pages encode one
+    window of t <= max_t rows per call (inferencelayer ``forward``) or pad to 30 s
+    (turbospark-runtime module doc), and a window never attends outside itself.
+
 The step before the encoder block (the convolutional front end):
   * ``conv_stem`` - ``h = gelu(conv1(mel))`` (kernel 3, stride 1, padding 1), then
     ``x = gelu(conv2(h)) + pos`` (kernel 3, stride 2, padding 1) over frames, with frames as rows
@@ -233,6 +238,25 @@ def encoder_stack(x, layers: Sequence[Dict[str, Optional[np.ndarray]]], heads: i
     if ln_post is not None:
         h = layer_norm(h, ln_post[0], ln_post[1])
     return h
+
+
+def encoder_stack_varlen(x_rows, seqlens: Sequence[int],
+                         layers: Sequence[Dict[str, Optional[np.ndarray]]], heads: int,
+                         ln_post=None) -> np.ndarray:
+    """The stack over a ragged batch: ``x_rows`` ``[sum(seqlens), d]`` holds the windows back to
+    back, window ``b`` being the next ``seqlens[b]`` rows.  Each window runs through
+    ``encoder_stack`` on its own (windows never attend across each other), and the outputs are
+    packed the same way."""
+    x = _f64(x_rows)
+    starts = np.concatenate([[0], np.cumsum(np.asarray(seqlens, dtype=np.int64))])
+    if starts[-1] != x.shape[0]:
+        raise ValueError("window lengths do not add up to the number of rows")
+    out = np.empty_like(x)
+    for b in range(len(seqlens)):
+        s0, s1 = int(starts[b]), int(starts[b + 1])
+        if s1 > s0:
+            out[s0:s1] = encoder_stack(x[s0:s1], layers, heads, ln_post)
+    return out
 
 
 def encoder_block_rows(x_window, p: Dict[str, Optional[np.ndarray]], heads: int,

@@ -57,6 +57,8 @@ EXPORTS = (
     "whisper_enc_cross_kv_workspace_bytes", "whisper_enc_cross_kv",
     "whisper_enc_stem_bytes", "whisper_enc_pack_stem", "whisper_enc_stem_workspace_bytes",
     "whisper_enc_stem_forward",
+    "whisper_enc_varlen_workspace_bytes", "whisper_enc_stack_forward_varlen",
+    "whisper_enc_attention_varlen",
 )
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -97,6 +99,9 @@ def load() -> ctypes.CDLL:
         "whisper_enc_pack_stem": (I, [P, P, P, P, P, I, I, I, I, P, P]),
         "whisper_enc_stem_workspace_bytes": (Z, [I, I, I, I, I]),
         "whisper_enc_stem_forward": (I, [P, P, P, I, I, I, I, I, I, P, Z, P]),
+        "whisper_enc_varlen_workspace_bytes": (Z, [I, I, I, I, I, I, I]),
+        "whisper_enc_stack_forward_varlen": (I, [P, P, P, I, P, P, P, I, I, I, I, I, I, I, P, Z, P]),
+        "whisper_enc_attention_varlen": (I, [P, P, P, P, P, I, I, I, I, I, I, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -232,3 +237,27 @@ def whisper_enc_stem_forward(mel, x, stem, batch, t_mel, n_mels, d_model, n_pos,
     _check(load().whisper_enc_stem_forward(_ptr(mel), _ptr(x), _ptr(stem), batch, t_mel, n_mels,
                                            d_model, n_pos, path, _ptr(workspace), workspace_bytes,
                                            _stream(stream)), "whisper_enc_stem_forward")
+
+
+def whisper_enc_varlen_workspace_bytes(batch: int, total_rows: int, max_t: int, d_model: int,
+                                       heads: int, ffn_dim: int, path: int) -> int:
+    return load().whisper_enc_varlen_workspace_bytes(batch, total_rows, max_t, d_model, heads,
+                                                     ffn_dim, path)
+
+
+def whisper_enc_stack_forward_varlen(x, y, layers, n_layers, ln_post_g, ln_post_b, cu_seqlens,
+                                     batch, total_rows, max_t, d_model, heads, ffn_dim, path,
+                                     workspace, workspace_bytes, stream=None) -> None:
+    """cu_seqlens: device int32 tensor [batch + 1] of window offsets."""
+    _check(load().whisper_enc_stack_forward_varlen(
+        _ptr(x), _ptr(y), _ptr(layers), n_layers, _ptr(ln_post_g), _ptr(ln_post_b),
+        _ptr(cu_seqlens), batch, total_rows, max_t, d_model, heads, ffn_dim, path,
+        _ptr(workspace), workspace_bytes, _stream(stream)), "whisper_enc_stack_forward_varlen")
+
+
+def whisper_enc_attention_varlen(q, k, v, o, cu_seqlens, batch, total_rows, max_t, heads, ld_qkv,
+                                 ld_o, path, stream=None) -> None:
+    _check(load().whisper_enc_attention_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                               _ptr(cu_seqlens), batch, total_rows, max_t, heads,
+                                               ld_qkv, ld_o, path, _stream(stream)),
+           "whisper_enc_attention_varlen")

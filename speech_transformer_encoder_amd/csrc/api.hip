@@ -103,9 +103,9 @@ Workspace carve(void* ws, size_t rows, int d, int path) {
     if ((expr) != hipSuccess) return WENC_ERR_HIP; \
   } while (0)
 
-// Enqueue one block; all arguments already validated.
+// Enqueue one block; all arguments already validated.  cu: ragged-batch offsets or nullptr.
 int run_block(const float* x, float* y, const char* blob, int rows, int t, int batch, int d,
-              int heads, int f, int path, const Workspace& ws, hipStream_t st) {
+              int heads, int f, int path, const Workspace& ws, hipStream_t st, const int* cu) {
   const LayerLayout L = layer_layout(d, f, path);
   const int dt = path_dtype(path);
   const size_t es = elem_bytes(path);
@@ -120,7 +120,7 @@ int run_block(const float* x, float* y, const char* blob, int rows, int t, int b
   WENC_TRY(launch_linear(ws.a, d, wqkv, fp(L.bqkv), nullptr, qkv, 3 * d, rows, 3 * d, d, dt,
                          EPI_BIAS, st));
   WENC_TRY(launch_attention(qkv, qkv + es * d, qkv + es * 2 * d, 3 * d, ws.a, d, batch, t, heads,
-                            0.125f, dt, st));
+                            0.125f, dt, st, cu, rows));
   WENC_TRY(launch_linear(ws.a, d, wo, fp(L.bo), x, y, d, rows, d, d, dt, EPI_BIAS_RESIDUAL, st));
   WENC_TRY(launch_layernorm(y, fp(L.ln2_g), fp(L.ln2_b), ws.a, rows, d, dt, st));
   WENC_TRY(launch_linear(ws.a, d, w1, fp(L.b1), nullptr, ws.b, f, rows, f, d, dt, EPI_BIAS_GELU,
@@ -200,15 +200,19 @@ size_t whisper_enc_workspace_bytes(int batch, int t, int d_model, int heads, int
   return workspace_size((size_t)batch * t, d_model, ffn_dim, path);
 }
 
-int whisper_enc_stack_forward(const float* x, float* y, const void* layers, int n_layers,
-                              const float* ln_post_g, const float* ln_post_b, int batch, int t,
-                              int d_model, int heads, int ffn_dim, int path, void* workspace,
-                              size_t workspace_bytes, void* stream) {
-  int rc = check_shape(batch, t, d_model, heads, ffn_dim, path);
-  if (rc != WENC_OK) return rc;
+}  // extern "C"
+
+namespace {
+
+// Stack over `rows` rows: equal windows of t (cu == nullptr) or a ragged batch (t = longest
+// window); shapes already checked.
+int stack_impl(const float* x, float* y, const void* layers, int n_layers, const float* ln_post_g,
+               const float* ln_post_b, const int* cu, int batch, size_t rows, int t, int d_model,
+               int heads, int ffn_dim, int path, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  int rc;
   if (n_layers < 0) return WENC_ERR_ARG;
   if ((ln_post_g == nullptr) != (ln_post_b == nullptr)) return WENC_ERR_ARG;
-  const size_t rows = (size_t)batch * t;
   if (rows == 0) return WENC_OK;
   const size_t xbytes = rows * d_model * sizeof(float);
   if (!x || !y || !aligned(x, 16) || !aligned(y, 16)) return WENC_ERR_ARG;
@@ -226,7 +230,7 @@ int whisper_enc_stack_forward(const float* x, float* y, const void* layers, int 
   const float* src = x;
   for (int l = 0; l < n_layers; ++l) {
     rc = run_block(src, y, static_cast<const char*>(layers) + (size_t)l * lb, (int)rows, t, batch,
-                   d_model, heads, ffn_dim, path, ws, st);
+                   d_model, heads, ffn_dim, path, ws, st, cu);
     if (rc != WENC_OK) return rc;
     src = y;
   }
@@ -236,6 +240,49 @@ int whisper_enc_stack_forward(const float* x, float* y, const void* layers, int 
     WENC_TRY(hipMemcpyAsync(y, src, xbytes, hipMemcpyDeviceToDevice, st));
   }
   return WENC_OK;
+}
+
+// Shape check of a ragged batch: `batch` windows packed into total_rows rows, none longer than
+// max_t (same per-window limits as check_shape with t = max_t).
+int check_varlen(int batch, int total_rows, int max_t, int d, int heads, int f, int path) {
+  if (batch < 0 || total_rows < 0 || max_t < 0 || total_rows > WENC_MAX_ROWS) return WENC_ERR_ARG;
+  if ((long long)batch * max_t < total_rows) return WENC_ERR_ARG;
+  return check_shape(1, max_t, d, heads, f, path);
+}
+
+}  // namespace
+
+extern "C" {
+
+int whisper_enc_stack_forward(const float* x, float* y, const void* layers, int n_layers,
+                              const float* ln_post_g, const float* ln_post_b, int batch, int t,
+                              int d_model, int heads, int ffn_dim, int path, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  const int rc = check_shape(batch, t, d_model, heads, ffn_dim, path);
+  if (rc != WENC_OK) return rc;
+  return stack_impl(x, y, layers, n_layers, ln_post_g, ln_post_b, nullptr, batch,
+                    (size_t)batch * t, t, d_model, heads, ffn_dim, path, workspace,
+                    workspace_bytes, stream);
+}
+
+size_t whisper_enc_varlen_workspace_bytes(int batch, int total_rows, int max_t, int d_model,
+                                          int heads, int ffn_dim, int path) {
+  if (check_varlen(batch, total_rows, max_t, d_model, heads, ffn_dim, path) != WENC_OK) return 0;
+  return workspace_size((size_t)total_rows, d_model, ffn_dim, path);
+}
+
+int whisper_enc_stack_forward_varlen(const float* x, float* y, const void* layers, int n_layers,
+                                     const float* ln_post_g, const float* ln_post_b,
+                                     const int* cu_seqlens, int batch, int total_rows, int max_t,
+                                     int d_model, int heads, int ffn_dim, int path,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  const int rc = check_varlen(batch, total_rows, max_t, d_model, heads, ffn_dim, path);
+  if (rc != WENC_OK) return rc;
+  if (total_rows > 0 && n_layers > 0 && (!cu_seqlens || !aligned(cu_seqlens, 4)))
+    return WENC_ERR_ARG;
+  return stack_impl(x, y, layers, n_layers, ln_post_g, ln_post_b, cu_seqlens, batch,
+                    (size_t)total_rows, max_t, d_model, heads, ffn_dim, path, workspace,
+                    workspace_bytes, stream);
 }
 
 int whisper_enc_block_forward(const float* x, float* y, const void* layer, int batch, int t,
@@ -310,6 +357,28 @@ int whisper_enc_attention(const void* q, const void* k, const void* v, void* o, 
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return WENC_ERR_ARG;
   WENC_TRY(launch_attention(q, k, v, ld_qkv, o, ld_o, batch, t, heads, 0.125f, dt,
                             static_cast<hipStream_t>(stream)));
+  return WENC_OK;
+}
+
+int whisper_enc_attention_varlen(const void* q, const void* k, const void* v, void* o,
+                                 const int* cu_seqlens, int batch, int total_rows, int max_t,
+                                 int heads, int ld_qkv, int ld_o, int path, void* stream) {
+  const int dt = path_dtype(path);
+  if (dt < 0) return WENC_ERR_ARG;
+  if (batch < 0 || total_rows < 0 || max_t < 0 || heads <= 0 || total_rows > WENC_MAX_ROWS)
+    return WENC_ERR_ARG;
+  if ((long long)batch * max_t < total_rows) return WENC_ERR_ARG;
+  if (heads * WENC_HEAD_DIM > WENC_MAX_FFN_DIM) return WENC_ERR_ARG;
+  if (ld_qkv < heads * WENC_HEAD_DIM || ld_o < heads * WENC_HEAD_DIM || ld_qkv % 8 || ld_o % 8)
+    return WENC_ERR_ARG;
+  if ((size_t)max_t * ld_qkv * elem_bytes(path) > (size_t)INT32_MAX) return WENC_ERR_UNSUPPORTED;
+  if (total_rows == 0) return WENC_OK;
+  if (!q || !k || !v || !o || !cu_seqlens) return WENC_ERR_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(cu_seqlens, 4))
+    return WENC_ERR_ARG;
+  WENC_TRY(launch_attention(q, k, v, ld_qkv, o, ld_o, batch, max_t, heads, 0.125f, dt,
+                            static_cast<hipStream_t>(stream), cu_seqlens, total_rows));
   return WENC_OK;
 }
 

@@ -44,6 +44,26 @@ constexpr float P_BOUND = 32768.0f;  // largest probability kept without raising
 typedef __attribute__((address_space(3))) void lds_void_a;
 typedef short short4_t __attribute__((ext_vector_type(4)));
 
+// Rows of window wi: equal windows of tmax rows (cu == nullptr), or rows cu[wi] .. cu[wi + 1] - 1
+// of a packed ragged batch of `total` rows.  False (the workgroup has nothing to do) when the
+// workgroup's first query row q0 lies past the window, or when the offsets break
+// 0 <= cu[wi] <= cu[wi + 1] <= total, cu[wi + 1] - cu[wi] <= tmax: then the window is skipped and
+// nothing outside [0, total) is ever addressed.  Uniform over the workgroup, taken before any
+// LDS use or barrier.
+__device__ __forceinline__ bool window_rows(const int* cu, int total, int wi, int tmax, int q0,
+                                            size_t& win, int& t) {
+  if (cu == nullptr) {
+    win = (size_t)wi * tmax;
+    t = tmax;
+    return true;
+  }
+  const int s0 = cu[wi], s1 = cu[wi + 1];
+  if (s0 < 0 || s1 < s0 || s1 > total || s1 - s0 > tmax) return false;
+  win = (size_t)s0;
+  t = s1 - s0;
+  return q0 < t;
+}
+
 template <typename T> struct RowSum;
 template <> struct RowSum<f16_t> {
   static __device__ __forceinline__ float add(uint32_t p2, float acc) {
@@ -62,8 +82,9 @@ template <typename T>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void attn16_kernel(const uint16_t* __restrict__ Q,
                                                         const uint16_t* __restrict__ Kp,
                                                         const uint16_t* __restrict__ Vp, int ld,
-                                                        uint16_t* __restrict__ O, int ldo, int t,
-                                                        int heads, float c) {
+                                                        uint16_t* __restrict__ O, int ldo, int tmax,
+                                                        int heads, float c,
+                                                        const int* __restrict__ cu, int total) {
   __shared__ __attribute__((aligned(1024))) uint16_t st0[2 * ATILE];
   __shared__ __attribute__((aligned(1024))) uint16_t st1[2 * ATILE];
   __shared__ __attribute__((aligned(1024))) uint16_t st2[2 * ATILE];
@@ -75,11 +96,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // 1-D grid over (query block, head, window), renumbered so that the query blocks of one
   // (window, head) run on the same XCD and read its K and V through one L2.
-  const int nqb = (t + AQ - 1) / AQ;
+  const int nqb = (tmax + AQ - 1) / AQ;
   const int v = xcd_virtual_id(blockIdx.x, gridDim.x);
   const int qb = v % nqb;
   const int h = (v / nqb) % heads;
-  const size_t win = (size_t)(v / (nqb * heads)) * t;  // first row of this window
+  const int wi = v / (nqb * heads);
+  size_t win;  // first row of this window
+  int t;       // its length
+  if (!window_rows(cu, total, wi, tmax, qb * AQ, win, t)) return;
   const int col0 = h * 64;
 
   // Query fragments: B operand of S^T, lane holds q = lane%32, dims 16s + 8g .. +7.
@@ -265,8 +289,9 @@ constexpr int AFLDS = 66;  // fp32 LDS row stride
 __global__ __launch_bounds__(256) void attn32_kernel(const float* __restrict__ Q,
                                                      const float* __restrict__ Kp,
                                                      const float* __restrict__ Vp, int ld,
-                                                     float* __restrict__ O, int ldo, int t,
-                                                     float c) {
+                                                     float* __restrict__ O, int ldo, int tmax,
+                                                     float c, const int* __restrict__ cu,
+                                                     int total) {
   __shared__ __attribute__((aligned(16))) float ks[2][AK * AFLDS];
   __shared__ __attribute__((aligned(16))) float vs[2][AK * AFLDS];
 
@@ -275,7 +300,9 @@ __global__ __launch_bounds__(256) void attn32_kernel(const float* __restrict__ Q
   const int g = lane >> 5;
   const int wave = tid >> 6;
   const int h = blockIdx.y;
-  const size_t win = (size_t)blockIdx.z * t;
+  size_t win;
+  int t;
+  if (!window_rows(cu, total, blockIdx.z, tmax, blockIdx.x * AQ32, win, t)) return;
   const int col0 = h * 64;
 
   // B operand of S^T: lane holds q = lane%32 and dims 4s + 2g, 4s + 2g + 1 for s = 0..15.
@@ -412,7 +439,7 @@ __global__ __launch_bounds__(256) void attn32_kernel(const float* __restrict__ Q
 
 hipError_t launch_attention(const void* q, const void* k, const void* v, int ld_qkv, void* o,
                             int ld_o, int batch, int t, int heads, float scale, int dtype,
-                            hipStream_t st) {
+                            hipStream_t st, const int* cu, int total) {
   if (batch == 0 || t == 0) return hipSuccess;
   const float c = scale * 1.4426950408889634f;  // fold log2(e): exp(x) = exp2(x * log2 e)
   const long nblk16 = (long)((t + AQ - 1) / AQ) * heads * batch;
@@ -422,18 +449,18 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int ld_
     case DT_BF16:
       attn16_kernel<bf16_t><<<grid16, block16, 0, st>>>(
           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-          static_cast<const uint16_t*>(v), ld_qkv, static_cast<uint16_t*>(o), ld_o, t, heads, c);
+          static_cast<const uint16_t*>(v), ld_qkv, static_cast<uint16_t*>(o), ld_o, t, heads, c, cu, total);
       break;
     case DT_F16:
       attn16_kernel<f16_t><<<grid16, block16, 0, st>>>(
           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-          static_cast<const uint16_t*>(v), ld_qkv, static_cast<uint16_t*>(o), ld_o, t, heads, c);
+          static_cast<const uint16_t*>(v), ld_qkv, static_cast<uint16_t*>(o), ld_o, t, heads, c, cu, total);
       break;
     case DT_F32:
       attn32_kernel<<<grid, block, 0, st>>>(static_cast<const float*>(q),
                                             static_cast<const float*>(k),
                                             static_cast<const float*>(v), ld_qkv,
-                                            static_cast<float*>(o), ld_o, t, c);
+                                            static_cast<float*>(o), ld_o, t, c, cu, total);
       break;
     default: return hipErrorInvalidValue;
   }

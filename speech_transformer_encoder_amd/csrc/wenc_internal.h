@@ -36,9 +36,11 @@ hipError_t launch_linear(const void* a, int lda, const void* w, const float* bia
 
 // Bidirectional attention per (window, head), head_dim 64.  q/k/v/o rows of the window b at
 // ptr + (b * t + i) * ld, head h at column offset 64 * h.  scale multiplies q.k.
+// Equal windows of t rows (cu == nullptr), or a packed ragged batch: window b is rows
+// cu[b] .. cu[b + 1] - 1 (device int32 [batch + 1]) of `total`, each at most t rows long.
 hipError_t launch_attention(const void* q, const void* k, const void* v, int ld_qkv, void* o,
                             int ld_o, int batch, int t, int heads, float scale, int dtype,
-                            hipStream_t st);
+                            hipStream_t st, const int* cu = nullptr, int total = 0);
 
 // dst[i] = round(src[i]) in dtype (or a copy for DT_F32); n elements.
 hipError_t launch_convert(const float* src, void* dst, size_t n, int dtype, hipStream_t st);

@@ -80,6 +80,34 @@ class EncoderStack:
         return y
 
 
+    def forward_varlen(self, x, seqlens: Sequence[int], y=None, n_layers: Optional[int] = None,
+                       final_norm: bool = True, stream=None):
+        """Run the stack on a ragged batch: ``x [sum(seqlens), d]`` (fp32, on the device) holds
+        the windows back to back, window ``b`` the next ``seqlens[b]`` rows; returns ``y``."""
+        import torch
+        total, d = x.shape
+        assert d == self.d_model and x.dtype == torch.float32 and x.is_contiguous()
+        lens = [int(n) for n in seqlens]
+        assert sum(lens) == total and min(lens, default=0) >= 0
+        max_t = max(lens, default=0)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32),
+                          device=self.device)
+        n = self.n_layers if n_layers is None else n_layers
+        if y is None:
+            y = torch.empty_like(x)
+        need = B.whisper_enc_varlen_workspace_bytes(len(lens), total, max_t, self.d_model,
+                                                    self.heads, self.ffn_dim, self.path)
+        if need == 0 and total > 0:
+            raise B.WencError(B.WENC_ERR_ARG, "whisper_enc_varlen_workspace_bytes")
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+        g, b = (self.ln_post if (final_norm and self.ln_post is not None) else (None, None))
+        B.whisper_enc_stack_forward_varlen(x, y, self.blob, n, g, b, cu, len(lens), total, max_t,
+                                           self.d_model, self.heads, self.ffn_dim, self.path,
+                                           self._ws, self._ws.numel(), stream)
+        return y
+
+
 def build_from_workload(w, path: int, device="cuda") -> EncoderStack:
     """Pack a :class:`synth.Workload`'s layers for ``path``."""
     c = w.cfg

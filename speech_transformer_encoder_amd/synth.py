@@ -156,6 +156,13 @@ def make_workload(cfg: EncoderConfig, n_layers: Optional[int] = None) -> Workloa
     return Workload(cfg, make_input(cfg), [make_layer(cfg, i) for i in range(n)], make_ln_post(cfg))
 
 
+def ragged_lengths(seed: int, batch: int, max_t: int = 1500, min_t: int = 150) -> np.ndarray:
+    """Window lengths of a ragged batch: uniform integers in ``[min_t, max_t]`` (3 s to 30 s of
+    audio at 50 encoder positions per second), int32."""
+    rng = np.random.default_rng([seed, 300, 0])
+    return rng.integers(min_t, max_t + 1, size=batch).astype(np.int32)
+
+
 def random_qkv(seed: int, batch: int, t: int, heads: int, head_dim: int = 64,
                outlier_frac: float = 0.0, outlier_scale: float = 1.0):
     """Standalone attention operands ``q, k, v`` of shape ``[batch, t, heads*head_dim]``.

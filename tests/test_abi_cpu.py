@@ -187,3 +187,37 @@ def test_stem_sizes_and_validation(lib):
     assert go(t=2999, npos=1500, wsb=16) == B.WENC_ERR_WORKSPACE
     # no frames enqueue nothing
     assert go(mel=None, x=None, stem=FAKE, t=0, ws=None, wsb=0) == B.WENC_OK
+
+
+def test_varlen_sizes_and_validation(lib):
+    P16 = B.WENC_PATH_FP16
+    dense = B.whisper_enc_workspace_bytes(1, 9000, 1280, 20, 5120, P16)
+    assert B.whisper_enc_varlen_workspace_bytes(16, 9000, 1500, 1280, 20, 5120, P16) == dense
+    # more rows than batch * max_t, negative sizes, head_dim != 64
+    assert B.whisper_enc_varlen_workspace_bytes(2, 3001, 1500, 1280, 20, 5120, P16) == 0
+    assert B.whisper_enc_varlen_workspace_bytes(2, -1, 1500, 1280, 20, 5120, P16) == 0
+    assert B.whisper_enc_varlen_workspace_bytes(2, 100, 1500, 1280, 10, 5120, P16) == 0
+
+    def stack(x=FAKE, y=1 << 40, layers=FAKE, n_layers=2, cu=FAKE, batch=4, total=3000,
+              max_t=1500, heads=20, ws=FAKE, wsb=1 << 34):
+        return lib.whisper_enc_stack_forward_varlen(x, y, layers, n_layers, None, None, cu, batch,
+                                                    total, max_t, 1280, heads, 5120, P16, ws,
+                                                    wsb, None)
+
+    assert stack(cu=None) == B.WENC_ERR_ARG
+    assert stack(cu=FAKE + 2) == B.WENC_ERR_ARG
+    assert stack(total=6001) == B.WENC_ERR_ARG
+    assert stack(heads=10) == B.WENC_ERR_UNSUPPORTED
+    assert stack(wsb=16) == B.WENC_ERR_WORKSPACE
+    assert stack(y=FAKE + 4096) == B.WENC_ERR_ARG
+    assert stack(x=None, y=None, cu=None, total=0, ws=None, wsb=0) == B.WENC_OK
+
+    def attn(q=FAKE, cu=FAKE, batch=4, total=3000, max_t=1500, ld=3840, ldo=1280):
+        return lib.whisper_enc_attention_varlen(q, q, q, q, cu, batch, total, max_t, 20, ld, ldo,
+                                                P16, None)
+
+    assert attn(cu=None) == B.WENC_ERR_ARG
+    assert attn(total=6001) == B.WENC_ERR_ARG
+    assert attn(ld=1000) == B.WENC_ERR_ARG
+    assert attn(max_t=1 << 20) == B.WENC_ERR_UNSUPPORTED
+    assert attn(q=None, cu=None, total=0) == B.WENC_OK

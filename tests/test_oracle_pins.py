@@ -294,6 +294,53 @@ def test_stack_matches_hf_layers_and_final_norm():
     np.testing.assert_allclose(oracle.encoder_stack(x, layers, heads), h, atol=1e-11)
 
 
+def test_stack_varlen_matches_hf_padded_batch_with_key_mask():
+    """A ragged batch equals the Hugging Face layers run on the zero-padded batch with an additive
+    key mask (padded keys get -inf before the softmax), on the rows that hold real frames."""
+    d, f, heads = 128, 256, 2
+    lens = [37, 1, 64, 0, 90]
+    tmax = max(lens)
+    layers = [_rand_layer(40 + i, d, f) for i in range(2)]
+    g, b = 1 + _rng(41).standard_normal(d) * 0.1, _rng(42).standard_normal(d) * 0.1
+    x = _rng(43).standard_normal((sum(lens), d))
+    got = oracle.encoder_stack_varlen(x, lens, layers, heads, ln_post=(g, b))
+    assert got.shape == x.shape
+    pad = np.zeros((len(lens), tmax, d))
+    mask = np.full((len(lens), 1, tmax, tmax), -np.inf)
+    s = 0
+    for i, n in enumerate(lens):
+        pad[i, :n] = x[s:s + n]
+        mask[i, :, :, :n] = 0.0
+        s += n
+    mask[np.isinf(mask).all(axis=-1)] = 0.0  # an empty window's rows: any finite mask
+    h = torch.tensor(pad)
+    with torch.no_grad():
+        for p in layers:
+            layer = _hf_layer(p, d, heads, f)
+            h = layer(h, attention_mask=torch.tensor(mask))
+            h = h[0] if isinstance(h, tuple) else h
+    ref = torch.nn.functional.layer_norm(h, (d,), torch.tensor(g), torch.tensor(b), eps=1e-5).numpy()
+    s = 0
+    for i, n in enumerate(lens):
+        np.testing.assert_allclose(got[s:s + n], ref[i, :n], atol=1e-11)
+        s += n
+
+
+def test_stack_varlen_rejects_bad_lengths_and_keeps_windows_apart():
+    d, f, heads = 64, 128, 1
+    layers = [_rand_layer(50, d, f)]
+    x = _rng(51).standard_normal((10, d))
+    with pytest.raises(ValueError):
+        oracle.encoder_stack_varlen(x, [4, 5], layers, heads)
+    a = oracle.encoder_stack_varlen(x, [4, 6], layers, heads)
+    # changing the second window leaves the first one's output unchanged
+    x2 = x.copy()
+    x2[4:] += 3.0
+    b = oracle.encoder_stack_varlen(x2, [4, 6], layers, heads)
+    np.testing.assert_array_equal(a[:4], b[:4])
+    assert np.abs(a[4:] - b[4:]).max() > 1e-3
+
+
 # ---------------------------------------------------------------- metrics
 
 

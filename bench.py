@@ -280,6 +280,36 @@ def time_stem(cfg, path_name, reps):
     return out
 
 
+def time_varlen(cfg, path_name, reps, enc, padded_ms):
+    """The same stack over a ragged batch: as many windows, of 150 .. t rows (seeded uniform
+    lengths), packed back to back with no padding; throughput counts real frames only.  Beside
+    it, the real frames per second of the padded call (every window padded to t rows)."""
+    import numpy as np
+    import torch
+    from speech_transformer_encoder_amd import binding as B
+    from speech_transformer_encoder_amd import synth
+    lens = synth.ragged_lengths(cfg.seed, cfg.batch, max_t=cfg.t)
+    total, max_t = int(lens.sum()), int(lens.max())
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), device="cuda")
+    x = torch.randn(total, cfg.d_model, device="cuda")
+    y = torch.empty_like(x)
+    ws_bytes = B.whisper_enc_varlen_workspace_bytes(cfg.batch, total, max_t, cfg.d_model,
+                                                    cfg.heads, cfg.ffn_dim, enc.path)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    g, b = enc.ln_post if enc.ln_post is not None else (None, None)
+    fn = lambda: B.whisper_enc_stack_forward_varlen(  # noqa: E731
+        x, y, enc.blob, enc.n_layers, g, b, cu, cfg.batch, total, max_t, cfg.d_model, cfg.heads,
+        cfg.ffn_dim, enc.path, ws, ws.numel())
+    ms = time_events(fn, reps, torch.cuda.current_stream())
+    out = {"windows": cfg.batch, "frames": total, "min_t": int(lens.min()), "max_t": max_t,
+           "ms": round(ms, 4), "frames_per_s": round(total / (ms * 1e-3), 1),
+           "padded_ms": round(padded_ms, 4),
+           "padded_frames_per_s": round(total / (padded_ms * 1e-3), 1)}
+    del x, y, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, windows, layers):
     """The oracle as it stands, on a bounded sample of the workload (first windows / layers)."""
     import numpy as np
@@ -351,7 +381,8 @@ def main():
         torch.cuda.synchronize()
         return s.elapsed_time(e) / args.steps, time.perf_counter() - t0
 
-    ms, wall = time_forward(build_from_workload(w, path))
+    enc_main = build_from_workload(w, path)
+    ms, wall = time_forward(enc_main)
     others = {}
     for pn in [p for p in args.compare_paths.split(",") if p and p != args.path]:
         oms, _ = time_forward(build_from_workload(w, B.PATHS[pn]))
@@ -387,6 +418,7 @@ def main():
     if not args.no_next_steps:
         next_steps["stem"] = time_stem(cfg, args.path, args.kernel_reps)
         next_steps["cross_kv"] = time_cross_kv(cfg, args.path, args.kernel_reps)
+        next_steps["varlen"] = time_varlen(cfg, args.path, args.kernel_reps, enc_main, ms)
 
     cpu = None
     if not args.no_cpu_baseline:

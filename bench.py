@@ -133,6 +133,40 @@ def make_kernels(cfg, path_name):
     }
 
 
+def mfma_peak(path_name):
+    """Dense 16-bit MFMA rate this GPU sustains on register operands (the probe library beside
+    the encoder library), with the shader clock while it runs; None on the fp32 path."""
+    import ctypes
+    import torch
+    if path_name == "fp32":
+        return None
+    lib = ctypes.CDLL(os.path.join(ROOT, "speech_transformer_encoder_amd", "libwenc_probe.so"))
+    lib.wenc_probe_mfma.restype = ctypes.c_int
+    lib.wenc_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    lib.wenc_probe_mfma_flops.restype = ctypes.c_longlong
+    lib.wenc_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    dtype = {"fp16": 2, "bf16": 1}[path_name]
+    blocks, iters = 256 * 2, 100000  # two wavefronts per SIMD; ~20 ms per launch
+    clocks = torch.zeros(2, dtype=torch.int64, device="cuda")
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream()
+    fn = lambda: lib.wenc_probe_mfma(dtype, blocks, iters, clocks.data_ptr(),  # noqa: E731
+                                     sink.data_ptr(), st.cuda_stream)
+    assert fn() == 0
+    torch.cuda.synchronize()
+    best, clk = None, None
+    for _ in range(3):
+        ms = time_events(fn, 1, st)
+        c = clocks.cpu().tolist()
+        if best is None or ms < best:
+            best, clk = ms, (c[0] / c[1] * 0.1 if c[1] > 0 else None)  # GHz (100 MHz reference)
+    tf = lib.wenc_probe_mfma_flops(blocks, iters) / (best * 1e-3) / 1e12
+    return {"dtype": path_name, "tflops": round(tf, 1), "shader_clock_ghz": round(clk, 3) if clk else None,
+            "rated_tflops": PEAK_TFLOPS[path_name], "rated_clock_ghz": 2.4,
+            "probe": "v_mfma_f32_32x32x16 on register operands, 4 chains x 2 wavefronts per SIMD"}
+
+
 def kernel_breakdown(cfg, path_name, reps):
     """Each kernel of one block at the workload's shapes, timed alone on the current stream."""
     import torch
@@ -320,6 +354,13 @@ def cpu_baseline(cfg, windows, layers):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")),
+                             None)
+    except OSError:
+        pass
     nw = min(windows, cfg.batch)
     nl = min(layers, cfg.n_layers)
     sub = cfg.with_(batch=nw, n_layers=nl)
@@ -332,7 +373,7 @@ def cpu_baseline(cfg, windows, layers):
     # the blocks, so the full call would take dt * (batch/nw) * (n_layers/nl).
     full_s = dt * (cfg.batch / nw) * (cfg.n_layers / nl)
     return {"value": round(cfg.batch * cfg.t / full_s, 2), "unit": "frames/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model, "nproc": os.cpu_count(),
             "sample": f"{nw} of {cfg.batch} windows x {nl} of {cfg.n_layers} blocks "
                       f"({dt:.1f} s float64 numpy, scaled to the full workload)"}
 
@@ -413,6 +454,11 @@ def main():
     gemm_tf = flops["gemm"] / (gemm_ms * 1e-3) / 1e12
     attn_tf = flops["attention"] / (attn_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[args.path]
+    measured = mfma_peak(args.path)
+    mpeak = measured["tflops"] if measured else None
+    if mpeak and roof["unit"] == "TFLOP/s":
+        roof["measured_peak"] = mpeak
+        roof["frac_measured_peak"] = round(roof["achieved"] / mpeak, 4)
 
     next_steps = {}
     if not args.no_next_steps:
@@ -437,7 +483,10 @@ def main():
         "tflops": {"total": round(flops["total"] / (ms * 1e-3) / 1e12, 1),
                    "gemm": round(gemm_tf, 1), "gemm_frac_peak": round(gemm_tf / peak, 4),
                    "attention": round(attn_tf, 1), "attention_frac_peak": round(attn_tf / peak, 4),
-                   "peak": peak},
+                   "peak": peak, "measured_peak": mpeak,
+                   "gemm_frac_measured_peak": round(gemm_tf / mpeak, 4) if mpeak else None,
+                   "attention_frac_measured_peak": round(attn_tf / mpeak, 4) if mpeak else None},
+        "mfma_peak_measured": measured,
         "roofline": roof,
         "kernels": kern,
         "wall_s_timed": round(wall, 4),

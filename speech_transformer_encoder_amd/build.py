@@ -1,4 +1,5 @@
-"""Compile the gfx950 HIP sources in ``csrc/`` into ``libwhisper_enc.so`` next to this file.
+"""Compile the gfx950 HIP sources in ``csrc/`` into ``libwhisper_enc.so`` next to this file, and
+the measurement probe in ``csrc/probe/`` into ``libwenc_probe.so`` (used by the benchmark only).
 
 ``python -m speech_transformer_encoder_amd.build`` (or ``__graft_entry__.build()``) runs hipcc
 once over every ``.hip`` source.  hipcc cross-compiles for gfx950 without a GPU present.
@@ -12,6 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libwhisper_enc.so")
+PROBE_LIB = os.path.join(HERE, "libwenc_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -33,9 +35,9 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(HERE, "..", "include"), *sources(), "-o", tmp]
+def _hipcc(srcs, lib, verbose):
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(HERE, "..", "include"), *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,8 +47,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    _hipcc(sorted(glob.glob(os.path.join(CSRC, "probe", "*.hip"))), PROBE_LIB, verbose)
+    return _hipcc(sources(), LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -22,9 +22,10 @@
 //   * the fragments of the next 16-k step are read while the MFMAs of the current one run;
 //   * one barrier per k tile; the loads of tile kt + 2 are issued right after it.
 // The epilogue stages each wavefront's 32 x 64 block through LDS so that global stores (and the
-// residual loads) are whole 128- or 256-byte row segments.  Workgroups are renumbered so that
-// each XCD (eight, dispatched round-robin) runs a contiguous range of tiles grouped 8 m-tiles
-// deep, so tiles running together share operand rows in that XCD's L2.
+// residual loads) are whole 128- or 256-byte row segments.  The kernel is persistent, one
+// workgroup per CU: each XCD (eight, dispatched round-robin) runs a contiguous range of tiles
+// grouped 8 m-tiles deep, so tiles running together share operand rows in that XCD's L2, and
+// the next tile's first operand loads overlap the current tile's epilogue.
 #include <type_traits>
 
 #include "wenc_device.h"
@@ -73,6 +74,16 @@ constexpr int G_THREADS = 64 * G_WAVES;
 constexpr int G_LPO = 32 / G_WAVES;  // 1 KB loads per operand per wavefront and k tile
 constexpr int G_STAGE = (G_N + G_M) * G_K;  // 16-bit elements per stage
 
+// Persistent: one workgroup per CU (the grid is the CU count, a multiple of 8; workgroup b runs
+// on XCD b % 8, which dispatches round-robin).  XCD x owns the contiguous range
+// [x T / 8, (x + 1) T / 8) of the T tiles in grouped order, and its workgroup j takes tiles
+// j, j + P / 8, ... of that range, so the tiles running together on one XCD are neighbours that
+// share operand rows in its L2.  Between two tiles the epilogue overlaps memory traffic with
+// compute: the next tile's first k tile is loaded into stage 0 before the epilogue, which stages
+// through stage 1, and the epilogue's loads and stores are range-checked buffer operations issued
+// unconditionally (rows past M and columns past N are dropped by the range check), so the number
+// of vector-memory operations behind that load is fixed and the next tile waits for the load
+// alone, not for the stores.
 template <typename T, int EPI>
 __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __restrict__ X,
                                                              int lda,
@@ -80,195 +91,248 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
                                                              const float* __restrict__ bias,
                                                              const float* residual, void* C,
                                                              int ldc, int M, int N, int K) {
+  constexpr bool kResidual = EPI == EPI_BIAS_RESIDUAL || EPI == EPI_BIAS_GELU_RESIDUAL;
+  // Head-major rows scatter over windows (64-bit addresses): those stores stay plain, predicated
+  // global stores, and the next tile waits for them.
+  constexpr bool kBufferOut = EPI != EPI_BIAS_HEADMAJOR;
+  // Vector-memory operations of one wavefront's epilogue: 4 row blocks x (8 residual loads + 8
+  // stores), or 4 x 4 stores.
+  constexpr int kEpiOps = kResidual ? 64 : 16;
   __shared__ __attribute__((aligned(1024))) uint16_t s0[G_STAGE];
   __shared__ __attribute__((aligned(1024))) uint16_t s1[G_STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave / G_WM, wm = wave % G_WM;
-  const int g = lane >> 5, frow = lane & 31;
-
   const int tiles_m = (M + G_M - 1) / G_M, tiles_n = (N + G_N - 1) / G_N;
-  const int v = xcd_virtual_id(blockIdx.x, gridDim.x);
-  const int group = 8 * tiles_n;
-  const int first_m = (v / group) * 8;
-  const int gm = min(tiles_m - first_m, 8);
-  const int tm = first_m + (v % group) % gm, tn = (v % group) / gm;
-  const int n0 = tn * G_N, m0 = tm * G_M;
-
-  // Buffer resources cover exactly the tile's valid rows: loads past them return zeros.
-  const int wrows = min(N - n0, G_N), xrows = min(M - m0, G_M);
-  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(W + (size_t)n0 * K), (short)0, wrows * K * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(X + (size_t)m0 * lda), (short)0, xrows * lda * 2, 0x00020000);
-
-  // Load instruction i of wavefront w fills the 1 KB LDS block (i * 8 + w): rows 8 * block ..
-  // + 7, lane l writing row (l >> 3), slot (l & 7), which holds chunk slot ^ ((row >> 1) & 7).
-  const int lrow = 8 * wave + (lane >> 3);
-  const int lchunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
-  const int voW = lrow * K * 2 + lchunk * 16, voX = lrow * lda * 2 + lchunk * 16;
+  const int tiles = tiles_m * tiles_n;
+  const int nk = K / G_K;
+  const int per_xcd = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int t_begin = (int)((long)tiles * xcd / 8), t_end = (int)((long)tiles * (xcd + 1) / 8);
+  const int ntile = t_end - t_begin > j ? (t_end - t_begin - j + per_xcd - 1) / per_xcd : 0;
+  if (ntile <= 0) return;
   const int stepW = 64 * K * 2, stepX = 64 * lda * 2;
-  auto load_tile = [&](int kt, uint16_t* st) {
-    const int so = kt * (G_K * 2);
-#pragma unroll
-    for (int i = 0; i < G_LPO; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_void*)(st + (i * G_WAVES + wave) * 512),
-                                               16, voW + i * stepW, so, 0, 0);
-#pragma unroll
-    for (int i = 0; i < G_LPO; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rX, (lds_void*)(st + G_N * G_K + (i * G_WAVES + wave) * 512), 16, voX + i * stepX, so,
-          0, 0);
-  };
 
-  // Fragment of step s (16 k): lane l reads row (l & 31) of a 32-row block, chunk 2s + (l >> 5).
-  const int rowA = (wn * G_TN + frow) * 128;
-  const int rowB = (G_N + wm * G_TM + frow) * 128;
-  int xo[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) xo[s] = ((2 * s + g) ^ ((lane >> 1) & 7)) << 4;
-  auto read_frags = [&](const uint16_t* st, int s, u32x4 (&fa)[G_NA], u32x4 (&fb)[G_NB]) {
-    const char* base = reinterpret_cast<const char*>(st);
-    // in the order the MFMAs consume them
-    fa[0] = *reinterpret_cast<const u32x4*>(base + rowA + xo[s]);
-#pragma unroll
-    for (int b = 0; b < G_NB; ++b)
-      fb[b] = *reinterpret_cast<const u32x4*>(base + rowB + b * 4096 + xo[s]);
-#pragma unroll
-    for (int a = 1; a < G_NA; ++a)
-      fa[a] = *reinterpret_cast<const u32x4*>(base + rowA + a * 4096 + xo[s]);
+  int n0 = 0, m0 = 0;
+  u32x4 rW, rX;
+  // Tile tt of the grouped order (8 m tiles deep, m fastest); buffer resources cover exactly the
+  // tile's valid rows, so operand loads past M or N return zeros.
+  auto setup = [&](int tt) {
+    const int group = 8 * tiles_n;
+    const int first_m = (tt / group) * 8;
+    const int gm = min(tiles_m - first_m, 8);
+    const int tm = first_m + (tt % group) % gm, tn = (tt % group) / gm;
+    n0 = tn * G_N;
+    m0 = tm * G_M;
+    const int wrows = min(N - n0, G_N), xrows = min(M - m0, G_M);
+    rW = buffer_rsrc(W + (size_t)n0 * K, (uint32_t)(wrows * K * 2));
+    rX = buffer_rsrc(X + (size_t)m0 * lda, (uint32_t)(xrows * lda * 2));
   };
 
   f32x16 acc[G_NA][G_NB];
+  for (int it = 0; it < ntile; ++it) {
+    // Lane-dependent offsets are formed per tile from an opaque copy of the lane index, so that
+    // they are not all kept live across the tile loop.
+    int lane = tid & 63;
+    asm volatile("" : "+v"(lane));
+    const int g = lane >> 5, frow = lane & 31;
+
+    // Copy i of wavefront w fills the 1 KB LDS block (i * 8 + w): rows 8 * block .. + 7, lane l
+    // writing row (l >> 3), slot (l & 7), which holds chunk slot ^ ((row >> 1) & 7).
+    const int lrow = 8 * wave + (lane >> 3);
+    const int lchunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
+    const int voW = lrow * K * 2 + lchunk * 16, voX = lrow * lda * 2 + lchunk * 16;
+    auto load_tile = [&](int kt, const uint16_t* st) {
+      const int ko = kt * (G_K * 2);
+      const uint32_t base = lds_addr(st);
 #pragma unroll
-  for (int a = 0; a < G_NA; ++a)
+      for (int i = 0; i < G_LPO; ++i)
+        lds_copy16(rW, base + (uint32_t)(i * G_WAVES + wave) * 1024u, voW + i * stepW + ko);
 #pragma unroll
-    for (int b = 0; b < G_NB; ++b)
+      for (int i = 0; i < G_LPO; ++i)
+        lds_copy16(rX, base + (uint32_t)(G_N * G_K * 2) + (uint32_t)(i * G_WAVES + wave) * 1024u,
+                   voX + i * stepX + ko);
+    };
+
+    // Fragment of step s (16 k): lane l reads row (l & 31) of a 32-row block, chunk 2s + (l >> 5).
+    const int rowA = (wn * G_TN + frow) * 128;
+    const int rowB = (G_N + wm * G_TM + frow) * 128;
+    int xo[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-  auto mm = [&](const u32x4 (&fa)[G_NA], const u32x4 (&fb)[G_NB]) {
+    for (int s = 0; s < 4; ++s) xo[s] = ((2 * s + g) ^ ((lane >> 1) & 7)) << 4;
+    auto read_frags = [&](const uint16_t* st, int s, u32x4 (&fa)[G_NA], u32x4 (&fb)[G_NB]) {
+      const char* base = reinterpret_cast<const char*>(st);
+      // in the order the MFMAs consume them
+      fa[0] = *reinterpret_cast<const u32x4*>(base + rowA + xo[s]);
+#pragma unroll
+      for (int b = 0; b < G_NB; ++b)
+        fb[b] = *reinterpret_cast<const u32x4*>(base + rowB + b * 4096 + xo[s]);
+#pragma unroll
+      for (int a = 1; a < G_NA; ++a)
+        fa[a] = *reinterpret_cast<const u32x4*>(base + rowA + a * 4096 + xo[s]);
+    };
+    auto mm = [&](const u32x4 (&fa)[G_NA], const u32x4 (&fb)[G_NB]) {
+#pragma unroll
+      for (int a = 0; a < G_NA; ++a)
+#pragma unroll
+        for (int b = 0; b < G_NB; ++b) acc[a][b] = mfma32x32x16<T>(fa[a], fb[b], acc[a][b]);
+    };
+    // Interleave the next step's fragment reads with the current step's MFMAs.
+    auto sched = [&]() {
+#pragma unroll
+      for (int q = 0; q < G_NA + G_NB; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, G_NA * G_NB - G_NA - G_NB, 0);
+    };
+
+    if (it == 0) setup(t_begin + j);  // later tiles are set up where their prefetch is issued
 #pragma unroll
     for (int a = 0; a < G_NA; ++a)
 #pragma unroll
-      for (int b = 0; b < G_NB; ++b) acc[a][b] = mfma32x32x16<T>(fa[a], fb[b], acc[a][b]);
-  };
-  // Interleave the next step's fragment reads with the current step's MFMAs.
-  auto sched = [&]() {
+      for (int b = 0; b < G_NB; ++b)
 #pragma unroll
-    for (int q = 0; q < G_NA + G_NB; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, G_NA * G_NB - G_NA - G_NB, 0);
-  };
+        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  const int nk = K / G_K;
-  u32x4 fa0[G_NA], fb0[G_NB], fa1[G_NA], fb1[G_NB];
-  load_tile(0, s0);
-  if (nk > 1) {
-    load_tile(1, s1);
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * G_LPO));  // vmcnt(2 * G_LPO): tile 0 has landed
-  } else {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  }
-  __syncthreads();
-  read_frags(s0, 0, fa0, fb0);
-
-  // One k tile.  `loads` / `next` are compile-time flags so that the loop body has no branch
-  // (the scheduling barriers only act inside one basic block).
-  auto body = [&](int kt, auto loads, auto next) {
-    uint16_t* cur = (kt & 1) ? s1 : s0;
-    uint16_t* nxt = (kt & 1) ? s0 : s1;
-    read_frags(cur, 1, fa1, fb1); mm(fa0, fb0); sched();
-    read_frags(cur, 2, fa0, fb0); mm(fa1, fb1); sched();
-    read_frags(cur, 3, fa1, fb1); mm(fa0, fb0); sched();
-    if constexpr (decltype(next)::value) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // this wavefront's loads of tile kt + 1 have landed
-      __syncthreads();                     // ... everyone's, and tile kt is no longer read
-      if constexpr (decltype(loads)::value) load_tile(kt + 2, cur);
-      read_frags(nxt, 0, fa0, fb0);
-    }
-    mm(fa1, fb1);
-    if constexpr (decltype(next)::value) sched();
-  };
-  int kt = 0;
-  for (; kt + 2 < nk; ++kt) body(kt, std::true_type{}, std::true_type{});
-  if (kt + 1 < nk) {
-    body(kt, std::false_type{}, std::true_type{});
-    ++kt;
-  }
-  body(kt, std::false_type{}, std::false_type{});
-
-  // Epilogue, one 32-row block of the wavefront at a time: (acc + bias) as fp32 into the
-  // wavefront's 8 KB of LDS (row r, 16-byte chunk c at slot c ^ (r & 15)), then read back by rows
-  // (LDS operations of one wavefront complete in order, so the read-back sees the writes).
-  float* ep = reinterpret_cast<float*>(s0) + wave * (32 * 64);
-  const int nw = n0 + wn * G_TN;  // first output column of the wavefront
-  const bool cols_ok = nw < N;    // N % 64 == 0: the wavefront's 64 columns are all in or out
-  // Each wavefront uses only its own 8 KB, so after the one barrier that retires the fragment
-  // reads, the staging needs no further workgroup synchronisation.
-  __syncthreads();
-#pragma unroll
-  for (int b = 0; b < G_NB; ++b) {
-#pragma unroll
-    for (int a = 0; a < G_NA; ++a)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = a * 8 + 2 * j + g;  // columns 4c .. 4c + 3 of the wavefront
-        const float4 bb = cols_ok ? *reinterpret_cast<const float4*>(bias + nw + 4 * c)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
-        *reinterpret_cast<float4*>(ep + frow * 64 + ((c ^ (frow & 15)) << 2)) =
-            make_float4(acc[a][b][4 * j] + bb.x, acc[a][b][4 * j + 1] + bb.y,
-                        acc[a][b][4 * j + 2] + bb.z, acc[a][b][4 * j + 3] + bb.w);
-      }
-    if (!cols_ok) continue;
-    const int mb = m0 + wm * G_TM + b * 32;
-    if constexpr (EPI == EPI_BIAS_RESIDUAL || EPI == EPI_BIAS_GELU_RESIDUAL) {
-      // fp32 rows of 64 columns: 16 lanes per row, 4 rows per instruction.  All residual loads
-      // are issued before the first store.
-      float4 res[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int m = mb + (lane >> 4) + 4 * q;
-        res[q] = m < M ? *reinterpret_cast<const float4*>(residual + (size_t)m * ldc + nw +
-                                                          4 * (lane & 15))
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int r = (lane >> 4) + 4 * q, c = lane & 15;
-        const int m = mb + r;
-        float4 v4 = *reinterpret_cast<const float4*>(ep + r * 64 + ((c ^ (r & 15)) << 2));
-        if constexpr (EPI == EPI_BIAS_GELU_RESIDUAL)
-          v4 = make_float4(gelu_erf_as(v4.x), gelu_erf_as(v4.y), gelu_erf_as(v4.z), gelu_erf_as(v4.w));
-        if (m < M)
-          *reinterpret_cast<float4*>(static_cast<float*>(C) + (size_t)m * ldc + nw + 4 * c) =
-              make_float4(res[q].x + v4.x, res[q].y + v4.y, res[q].z + v4.z, res[q].w + v4.w);
+    u32x4 fa0[G_NA], fb0[G_NB], fa1[G_NA], fb1[G_NB];
+    __syncthreads();  // the previous tile's staging reads of stage 1 are done
+    if (it == 0) load_tile(0, s0);
+    if (nk > 1) {
+      load_tile(1, s1);
+      // k tile 0 has landed.  Still allowed in flight: k tile 1 and, after the first tile, the
+      // previous epilogue's operations, which were issued after k tile 0.
+      if (it == 0 || !kBufferOut) {
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * G_LPO));  // vmcnt(8)
+      } else if constexpr (kEpiOps + 2 * G_LPO >= 63) {
+        __builtin_amdgcn_s_waitcnt(0xCF7F);  // vmcnt(63): waits a little more than needed
+      } else {
+        constexpr int n = kEpiOps + 2 * G_LPO;
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
       }
     } else {
-      // 16-bit rows of 64 columns (128 bytes): 8 lanes per row, 8 rows per instruction.
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    }
+    __syncthreads();
+    read_frags(s0, 0, fa0, fb0);
+
+    // One k tile.  `loads` / `next` are compile-time flags so that the loop body has no branch
+    // (the scheduling barriers only act inside one basic block).
+    auto body = [&](int kt, auto loads, auto next) {
+      const uint16_t* cur = (kt & 1) ? s1 : s0;
+      const uint16_t* nxt = (kt & 1) ? s0 : s1;
+      read_frags(cur, 1, fa1, fb1); mm(fa0, fb0); sched();
+      read_frags(cur, 2, fa0, fb0); mm(fa1, fb1); sched();
+      read_frags(cur, 3, fa1, fb1); mm(fa0, fb0); sched();
+      if constexpr (decltype(next)::value) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // this wavefront's loads of tile kt + 1 have landed
+        __syncthreads();                     // ... everyone's, and tile kt is no longer read
+        if constexpr (decltype(loads)::value) load_tile(kt + 2, cur);
+        read_frags(nxt, 0, fa0, fb0);
+      }
+      mm(fa1, fb1);
+      if constexpr (decltype(next)::value) sched();
+    };
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) body(kt, std::true_type{}, std::true_type{});
+    if (kt + 1 < nk) {
+      body(kt, std::false_type{}, std::true_type{});
+      ++kt;
+    }
+    body(kt, std::false_type{}, std::false_type{});
+
+    // Epilogue, one 32-row block of the wavefront at a time: (acc + bias) as fp32 into the
+    // wavefront's 8 KB of stage 1 (row r, 16-byte chunk c at slot c ^ (r & 15)), then read back
+    // by rows (LDS operations of one wavefront complete in order).
+    const int em0 = m0;
+    const int nw = n0 + wn * G_TN;  // first output column of the wavefront
+    const bool cols_ok = nw < N;    // N % 64 == 0: the wavefront's 64 columns are all in or out
+    float* ep = reinterpret_cast<float*>(s1) + wave * (32 * 64);
+    float4 bias4[G_NA][4];  // loaded before the prefetch, so that nothing waits for it
+#pragma unroll
+    for (int a = 0; a < G_NA; ++a)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int r = (lane >> 3) + 8 * q, c0 = 2 * (lane & 7);
-        const int m = mb + r;
-        float4 v0 = *reinterpret_cast<const float4*>(ep + r * 64 + ((c0 ^ (r & 15)) << 2));
-        float4 v1 = *reinterpret_cast<const float4*>(ep + r * 64 + (((c0 + 1) ^ (r & 15)) << 2));
-        if constexpr (EPI == EPI_BIAS_GELU) {
-          v0 = make_float4(gelu_erf_as(v0.x), gelu_erf_as(v0.y), gelu_erf_as(v0.z), gelu_erf_as(v0.w));
-          v1 = make_float4(gelu_erf_as(v1.x), gelu_erf_as(v1.y), gelu_erf_as(v1.z), gelu_erf_as(v1.w));
+        const int c = a * 8 + 2 * q + g;  // columns 4c .. 4c + 3 of the wavefront
+        bias4[a][q] = cols_ok ? *reinterpret_cast<const float4*>(bias + nw + 4 * c)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    __syncthreads();  // every wavefront is done reading both stages
+    if (it + 1 < ntile) {
+      setup(t_begin + j + (it + 1) * per_xcd);
+      load_tile(0, s0);
+    }
+    // Output (and residual) rows of the tile from the wavefront's first column; the range covers
+    // the tile's rows below M, or nothing when the wavefront's columns are past N.
+    const size_t row0 = (size_t)em0 * ldc + nw;
+    constexpr int esz = kResidual ? 4 : 2;
+    const int nrec = cols_ok ? min(M - em0, G_M) * ldc * esz : 0;
+    const __amdgpu_buffer_rsrc_t rC = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<char*>(C) + row0 * esz, (short)0, nrec, 0x00020000);
+#pragma unroll
+    for (int b = 0; b < G_NB; ++b) {
+#pragma unroll
+      for (int a = 0; a < G_NA; ++a)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = a * 8 + 2 * q + g;
+          const float4 bb = bias4[a][q];
+          *reinterpret_cast<float4*>(ep + frow * 64 + ((c ^ (frow & 15)) << 2)) =
+              make_float4(acc[a][b][4 * q] + bb.x, acc[a][b][4 * q + 1] + bb.y,
+                          acc[a][b][4 * q + 2] + bb.z, acc[a][b][4 * q + 3] + bb.w);
         }
-        const u32x4 w4 = {pack2<T>(v0.x, v0.y), pack2<T>(v0.z, v0.w), pack2<T>(v1.x, v1.y),
-                          pack2<T>(v1.z, v1.w)};
-        if (m < M) {
-          const size_t off = EPI == EPI_BIAS_HEADMAJOR ? headmajor_offset(m, nw + 4 * c0, N, ldc)
-                                                       : (size_t)m * ldc + nw + 4 * c0;
-          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(C) + off) = w4;
+      const int rb = wm * G_TM + b * 32;  // first row of the block within the tile
+      if constexpr (kResidual) {
+        // fp32 rows of 64 columns: 16 lanes per row, 4 rows per instruction.  All residual loads
+        // are issued before the first store; the stores are non-temporal (the residual stream
+        // is next read by a different kernel).
+        const __amdgpu_buffer_rsrc_t rR = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(residual) + row0, (short)0, nrec, 0x00020000);
+        float4 res[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int r = rb + (lane >> 4) + 4 * q;
+          res[q] = __builtin_bit_cast(
+              float4, __builtin_amdgcn_raw_buffer_load_b128(rR, (r * ldc + 4 * (lane & 15)) * 4, 0, 0));
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int r = (lane >> 4) + 4 * q, c = lane & 15;
+          float4 v4 = *reinterpret_cast<const float4*>(ep + r * 64 + ((c ^ (r & 15)) << 2));
+          if constexpr (EPI == EPI_BIAS_GELU_RESIDUAL)
+            v4 = make_float4(gelu_erf_as(v4.x), gelu_erf_as(v4.y), gelu_erf_as(v4.z),
+                             gelu_erf_as(v4.w));
+          const float4 o = make_float4(res[q].x + v4.x, res[q].y + v4.y, res[q].z + v4.z,
+                                       res[q].w + v4.w);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rC,
+                                                 ((rb + r) * ldc + 4 * c) * 4, 0, 2 /* nt */);
+        }
+      } else {
+        // 16-bit rows of 64 columns (128 bytes): 8 lanes per row, 8 rows per instruction.
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = (lane >> 3) + 8 * q, c0 = 2 * (lane & 7);
+          float4 v0 = *reinterpret_cast<const float4*>(ep + r * 64 + ((c0 ^ (r & 15)) << 2));
+          float4 v1 = *reinterpret_cast<const float4*>(ep + r * 64 + (((c0 + 1) ^ (r & 15)) << 2));
+          if constexpr (EPI == EPI_BIAS_GELU) {
+            v0 = make_float4(gelu_erf_as(v0.x), gelu_erf_as(v0.y), gelu_erf_as(v0.z), gelu_erf_as(v0.w));
+            v1 = make_float4(gelu_erf_as(v1.x), gelu_erf_as(v1.y), gelu_erf_as(v1.z), gelu_erf_as(v1.w));
+          }
+          const u32x4 w4 = {pack2<T>(v0.x, v0.y), pack2<T>(v0.z, v0.w), pack2<T>(v1.x, v1.y),
+                            pack2<T>(v1.z, v1.w)};
+          if constexpr (kBufferOut) {
+            __builtin_amdgcn_raw_buffer_store_b128(w4, rC, ((rb + r) * ldc + 4 * c0) * 2, 0, 0);
+          } else {
+            const int m = em0 + rb + r;
+            if (cols_ok && m < M)
+              *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(C) +
+                                        headmajor_offset(m, nw + 4 * c0, N, ldc)) = w4;
+          }
         }
       }
     }
   }
 }
-
 // Smaller-problem variant (fewer 256 x 256 tiles than CUs, e.g. the 1500-row GEMMs of a single
 // window): 128 (n) x 256 (m) tiles with a 32-wide k tile for a 256-thread workgroup (four
 // wavefronts, 64 x 128 outputs each), two workgroups per CU so that one's barriers and epilogue
@@ -580,13 +644,25 @@ __global__ __launch_bounds__(256) void gemm32_kernel(const float* __restrict__ X
   }
 }
 
+// Workgroups of the persistent kernel: the current device's CU count, rounded down to a multiple
+// of the eight XCDs.
+static int persistent_grid() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 8)
+    return 256;
+  return cus & ~7;
+}
+
 template <typename T, int EPI>
 static void launch16_epi(const uint16_t* X, int lda, const uint16_t* W, const float* bias,
                          const float* residual, void* c, int ldc, int m, int n, int k,
                          hipStream_t st) {
   const long tiles = (long)((m + G_M - 1) / G_M) * ((n + G_N - 1) / G_N);
-  if (tiles >= 256) {
-    gemm16_kernel<T, EPI><<<dim3((unsigned)tiles), dim3(G_THREADS), 0, st>>>(
+  const int grid = persistent_grid();
+  if (tiles >= grid) {
+    gemm16_kernel<T, EPI><<<dim3((unsigned)grid), dim3(G_THREADS), 0, st>>>(
         X, lda, W, bias, residual, c, ldc, m, n, k);
   } else {
     const long small = (long)((m + H_M - 1) / H_M) * ((n + H_N - 1) / H_N);

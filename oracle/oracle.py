@@ -47,6 +47,10 @@ The step after the encoder (cross-attention keys and values of the decoder):
     ``V_l = y Wv_l^T + bv_l`` from the encoder output ``y``, stored head-major
     (turbospark-runtime ``build_cross_caches``; oxinfer ``cross_kv`` and ``Kv``).
 
+Low-precision weights (oxinfer ``Precision``: q8 / q4 blocks of 32 quantised from bf16):
+  * ``quantize_q8`` / ``quantize_q4`` and their inverses, ``quantized_layer``; the encodings are a
+    reading (the pages name the formats without printing them), stated where they are defined.
+
 Cross-check formulations (used only by the tests):
   * ``attention_two_pass`` - exact max pass, exponent/sum pass, weighted sum (inferencelayer
     ``DEC_QATTN`` shader; turbospark-runtime ``encode_layer`` score planes + ``softmax_rows``).
@@ -344,3 +348,78 @@ def conv_stem(mel, conv1_w, conv1_b, conv2_w, conv2_b, pos) -> np.ndarray:
         x = gelu_erf(conv1d_k3(h, conv2_w, conv2_b, 2))
         outs.append(x + _f64(pos)[:x.shape[0]])
     return np.stack(outs)
+
+
+# ---------------------------------------------------------------- low-precision weights
+#
+# oxinfer whisper/model.rs, Precision and make_lin: weight matrices may be stored as int8 (q8) or
+# int4 (q4, also named q4_0) blocks of 32 consecutive input columns, quantised from the matrix
+# rounded to bf16; norms, biases and positions stay f32.  The pages do not print the encodings.
+# Reading: the q8_0 / q4_0 block formats the q4_0 name refers to, each block with one fp16 scale:
+#   q8: d = amax / 127, codes q = round-half-away(x / d) in [-127, 127], value q d;
+#   q4: m = the element of largest magnitude (the first on ties), d = m / -8, codes
+#       q = min(15, floor(x / d + 8.5)) in [0, 15], value (q - 8) d.
+# The codes are integers decided by floating point, so the steps below are the float32 steps an
+# implementation takes (x times the float32 reciprocal of the float32 d; d rounded to fp16 only
+# for storage), and the tests compare codes exactly.  Dequantised values are exact in float64.
+
+QBLOCK = 32
+
+
+def bf16_round(x) -> np.ndarray:
+    """float32 -> nearest bfloat16 (ties to even), returned as float32."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return r.astype(np.uint32).view(np.float32)
+
+
+def quantize_q8(w):
+    """``w`` ``[n_out, n_in]`` (n_in a multiple of 32) -> (codes int8 ``[n_out, n_in]``, scales
+    float16 ``[n_out, n_in / 32]``), from the bf16-rounded matrix."""
+    x = bf16_round(w).reshape(w.shape[0], -1, QBLOCK)
+    amax = np.max(np.abs(x), axis=2).astype(np.float32)
+    d = (amax / np.float32(127.0)).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        idv = np.where(d != 0, np.float32(1.0) / d, np.float32(0.0)).astype(np.float32)
+    v = (x * idv[:, :, None]).astype(np.float32)
+    q = (np.sign(v) * np.floor(np.abs(v) + np.float32(0.5))).astype(np.int8)
+    return q.reshape(w.shape), d.astype(np.float16)
+
+
+def dequantize_q8(codes, scales) -> np.ndarray:
+    n = codes.shape[0]
+    q = codes.astype(np.float64).reshape(n, -1, QBLOCK)
+    return (q * scales.astype(np.float64)[:, :, None]).reshape(codes.shape)
+
+
+def quantize_q4(w):
+    """``w`` ``[n_out, n_in]`` -> (codes uint8 in [0, 15] ``[n_out, n_in]``, scales float16
+    ``[n_out, n_in / 32]``), from the bf16-rounded matrix."""
+    x = bf16_round(w).reshape(w.shape[0], -1, QBLOCK)
+    first = np.argmax(np.abs(x), axis=2)  # first index of the largest magnitude
+    m = np.take_along_axis(x, first[:, :, None], axis=2)[:, :, 0].astype(np.float32)
+    d = (m / np.float32(-8.0)).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        idv = np.where(d != 0, np.float32(1.0) / d, np.float32(0.0)).astype(np.float32)
+    v = ((x * idv[:, :, None]).astype(np.float32) + np.float32(8.5)).astype(np.float32)
+    q = np.minimum(np.floor(v), 15).astype(np.uint8)
+    return q.reshape(w.shape), d.astype(np.float16)
+
+
+def dequantize_q4(codes, scales) -> np.ndarray:
+    n = codes.shape[0]
+    q = codes.astype(np.float64).reshape(n, -1, QBLOCK) - 8.0
+    return (q * scales.astype(np.float64)[:, :, None]).reshape(codes.shape)
+
+
+QUANT_MATRICES = ("wq", "wk", "wv", "wo", "w1", "w2")
+
+
+def quantized_layer(p: Dict[str, Optional[np.ndarray]], bits: int) -> Dict[str, Optional[np.ndarray]]:
+    """The block's parameters with every weight matrix replaced by its q8 / q4 dequantised values
+    (float64); norms and biases unchanged."""
+    quant, deq = (quantize_q8, dequantize_q8) if bits == 8 else (quantize_q4, dequantize_q4)
+    out = dict(p)
+    for name in QUANT_MATRICES:
+        out[name] = deq(*quant(p[name]))
+    return out

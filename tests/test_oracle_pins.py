@@ -524,3 +524,163 @@ def test_sinusoid_positions_closed_form():
     np.testing.assert_array_equal(pos[0, :640], 0.0)
     np.testing.assert_array_equal(pos[0, 640:], 1.0)
     np.testing.assert_allclose(pos[1, 0], math.sin(1.0), rtol=1e-6)
+
+
+# ---------------------------------------------------------------- low-precision weights
+
+
+def test_bf16_rounding_matches_torch():
+    x = np.concatenate([_rng(60).standard_normal(5000).astype(np.float32),
+                        np.array([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 3.4e38, 1e-40], np.float32)])
+    ref = torch.tensor(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(oracle.bf16_round(x), ref)
+
+
+def _near_half(v, tol=1e-4):
+    return np.abs(np.abs(v - np.floor(v)) - 0.5) < tol
+
+
+def test_q8_codes_are_the_nearest_levels():
+    w = (_rng(61).standard_normal((16, 128)) * 0.05).astype(np.float32)
+    q, d = oracle.quantize_q8(w)
+    x = oracle.bf16_round(w).astype(np.float64).reshape(16, -1, 32)
+    d32 = (np.max(np.abs(x), axis=2) / 127.0)[:, :, None]
+    ks = np.arange(-127, 128, dtype=np.float64)
+    # brute force: the level k d nearest to x, ties away from zero
+    dist = np.abs(x[..., None] - ks * d32[..., None])
+    best = ks[np.argmin(dist - 1e-12 * np.abs(ks), axis=-1)]
+    exact = x / d32
+    ok = (q.reshape(best.shape) == best) | _near_half(exact)
+    assert ok.all()
+    # the block's largest magnitude maps to +-127; round trip within half a step
+    qb = q.reshape(16, -1, 32).astype(np.int64)
+    assert (np.max(np.abs(qb), axis=2) == 127).all()
+    back = oracle.dequantize_q8(q, d).reshape(x.shape)
+    d16 = d.astype(np.float64)[:, :, None]
+    assert (np.abs(back - x) <= d32 / 2 + 127 * np.abs(d16 - d32) + 1e-12).all()
+
+
+def test_q4_codes_are_the_nearest_levels():
+    w = (_rng(62).standard_normal((16, 128)) * 0.05).astype(np.float32)
+    v = np.float32(1.5 * np.abs(w[0, :32]).max())
+    w[0, 2], w[0, 5] = v, -v  # the first largest magnitude, then its negation
+    q, d = oracle.quantize_q4(w)
+    assert q.dtype == np.uint8 and q.max() <= 15
+    x = oracle.bf16_round(w).astype(np.float64).reshape(16, -1, 32)
+    first = np.argmax(np.abs(x), axis=2)
+    m = np.take_along_axis(x, first[:, :, None], axis=2)
+    d32 = m / -8.0
+    ks = np.arange(16, dtype=np.float64)
+    dist = np.abs(x[..., None] - (ks - 8) * d32[..., None])
+    best = ks[np.argmin(dist - 1e-12 * ks, axis=-1)]  # ties to the larger code
+    exact = x / d32 + 8.0
+    ok = (q.reshape(best.shape) == best) | _near_half(exact)
+    assert ok.all()
+    # the first largest magnitude maps to code 0; its negation clamps to 15
+    qb = q.reshape(16, -1, 32)
+    assert (np.take_along_axis(qb, first[:, :, None], axis=2) == 0).all()
+    assert qb[0, 0, 5] == 15
+
+
+def test_quantizers_zero_block_and_lossless_levels():
+    z = np.zeros((2, 64), np.float32)
+    q, d = oracle.quantize_q8(z)
+    assert (q == 0).all() and (d == 0).all()
+    q, d = oracle.quantize_q4(z)
+    assert (q == 8).all() and (d == 0).all()
+    assert (oracle.dequantize_q4(q, d) == 0).all()
+    r = _rng(63)
+    # q8: values k 2^-10 with +-127 in every block are stored exactly
+    k = r.integers(-127, 128, size=(8, 96))
+    k[:, ::32] = 127 * np.where(r.random((8, 3)) < 0.5, -1, 1)
+    w = (k * 2.0 ** -10).astype(np.float32)
+    q, d = oracle.quantize_q8(w)
+    np.testing.assert_array_equal(q, k)
+    np.testing.assert_array_equal(oracle.dequantize_q8(q, d), w.astype(np.float64))
+    # q4: values (k - 8) 2^-8 with a unique -8 2^-8 in every block are stored exactly
+    k = r.integers(1, 16, size=(8, 96))
+    k[:, 7::32] = 0
+    w = ((k - 8) * 2.0 ** -8).astype(np.float32)
+    q, d = oracle.quantize_q4(w)
+    np.testing.assert_array_equal(q, k)
+    np.testing.assert_array_equal(oracle.dequantize_q4(q, d), w.astype(np.float64))
+
+
+def test_quantized_layer_block_is_lossless_on_exact_levels():
+    """A block whose matrices already sit on the q8 levels gives the same output as the unquantised
+    block (catches a block or matrix applied to the wrong weights)."""
+    d, f, heads = 64, 128, 1
+    p = _rand_layer(64, d, f)
+    r = _rng(65)
+    for name in oracle.QUANT_MATRICES:
+        k = r.integers(-127, 128, size=p[name].shape)
+        k[:, ::32] = 127
+        p[name] = (k * 2.0 ** -12).astype(np.float32)
+    x = _rng(66).standard_normal((20, d))
+    np.testing.assert_allclose(oracle.encoder_block(x, oracle.quantized_layer(p, 8), heads),
+                               oracle.encoder_block(x, p, heads), atol=1e-12)
+    q = oracle.quantized_layer(p, 4)
+    assert np.abs(oracle.encoder_block(x, q, heads) - oracle.encoder_block(x, p, heads)).max() > 1e-4
+
+
+def test_q8_ties_round_away_from_zero():
+    """Exact half levels (d = 2^-10, so the reciprocal is exact) round away from zero."""
+    w = np.zeros((1, 32), np.float32)
+    w[0, 0] = 127 * 2.0 ** -10
+    w[0, 1], w[0, 2], w[0, 3] = 2.5 * 2.0 ** -10, -2.5 * 2.0 ** -10, 0.5 * 2.0 ** -10
+    q, d = oracle.quantize_q8(w)
+    assert d[0, 0] == np.float16(2.0 ** -10)
+    assert (q[0, :4] == [127, 3, -3, 1]).all()
+
+
+def _quant_pins_hold():
+    try:
+        test_q8_codes_are_the_nearest_levels()
+        test_q4_codes_are_the_nearest_levels()
+        test_quantizers_zero_block_and_lossless_levels()
+        test_q8_ties_round_away_from_zero()
+    except AssertionError:
+        return False
+    return True
+
+
+@pytest.mark.parametrize("mutation", ["q8_scale_128", "q8_round_even", "q4_offset", "q4_last_max",
+                                      "q4_dequant_offset"])
+def test_planted_quantizer_mistakes_are_caught(monkeypatch, mutation):
+    assert _quant_pins_hold()
+    real_q8, real_q4, real_dq4 = orc.quantize_q8, orc.quantize_q4, orc.dequantize_q4
+
+    def q8(w, scale=127.0, rnd=None):
+        x = orc.bf16_round(w).reshape(w.shape[0], -1, 32)
+        d = (np.max(np.abs(x), axis=2).astype(np.float32) / np.float32(scale)).astype(np.float32)
+        idv = np.where(d != 0, 1 / np.where(d != 0, d, 1), 0).astype(np.float32)
+        v = (x * idv[:, :, None]).astype(np.float32)
+        q = rnd(v) if rnd else np.sign(v) * np.floor(np.abs(v) + np.float32(0.5))
+        return np.clip(q, -128, 127).astype(np.int8).reshape(w.shape), d.astype(np.float16)
+
+    def q4(w, off=8.5, last=False):
+        x = orc.bf16_round(w).reshape(w.shape[0], -1, 32)
+        a = np.abs(x)
+        idx = (31 - np.argmax(a[:, :, ::-1], axis=2)) if last else np.argmax(a, axis=2)
+        m = np.take_along_axis(x, idx[:, :, None], axis=2)[:, :, 0].astype(np.float32)
+        d = (m / np.float32(-8.0)).astype(np.float32)
+        idv = np.where(d != 0, 1 / np.where(d != 0, d, 1), 0).astype(np.float32)
+        v = ((x * idv[:, :, None]).astype(np.float32) + np.float32(off)).astype(np.float32)
+        return np.clip(np.floor(v), 0, 15).astype(np.uint8).reshape(w.shape), d.astype(np.float16)
+
+    def plant(name, fn):  # in the module and in the package namespace the pins call
+        monkeypatch.setattr(orc, name, fn)
+        monkeypatch.setattr(oracle, name, fn)
+
+    if mutation == "q8_scale_128":
+        plant("quantize_q8", lambda w: q8(w, scale=128.0))
+    elif mutation == "q8_round_even":
+        plant("quantize_q8", lambda w: q8(w, rnd=np.rint))
+    elif mutation == "q4_offset":
+        plant("quantize_q4", lambda w: q4(w, off=8.0))
+    elif mutation == "q4_last_max":
+        plant("quantize_q4", lambda w: q4(w, last=True))
+    elif mutation == "q4_dequant_offset":
+        plant("dequantize_q4", lambda c, s: real_dq4(c, s) + s.astype(np.float64).repeat(32, axis=1))
+    assert not _quant_pins_hold()
+    del real_q8, real_q4

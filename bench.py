@@ -344,6 +344,26 @@ def time_varlen(cfg, path_name, reps, enc, padded_ms):
     return out
 
 
+def time_quantized(cfg, w, x, y, reps, bits):
+    """The same block step with the weights stored as q8 / q4 blocks of 32 (expanded to fp16 by
+    each block call); real frames per second and weight bytes at rest per layer."""
+    import torch
+    from speech_transformer_encoder_amd import binding as B
+    from speech_transformer_encoder_amd.encoder import build_from_workload
+    path = B.WENC_PATH_Q8 if bits == 8 else B.WENC_PATH_Q4
+    enc = build_from_workload(w, path)
+    enc.workspace(cfg.batch, cfg.t)
+    ms = time_events(lambda: enc.forward(x, y), reps, torch.cuda.current_stream())
+    out = {"ms": round(ms, 4), "value": round(cfg.batch * cfg.t / (ms * 1e-3), 1),
+           "unit": "frames/s",
+           "layer_bytes": B.whisper_enc_layer_bytes(cfg.d_model, cfg.ffn_dim, path),
+           "fp16_layer_bytes": B.whisper_enc_layer_bytes(cfg.d_model, cfg.ffn_dim,
+                                                         B.WENC_PATH_FP16)}
+    del enc
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, windows, layers):
     """The oracle as it stands, on a bounded sample of the workload (first windows / layers)."""
     import numpy as np
@@ -465,6 +485,9 @@ def main():
         next_steps["stem"] = time_stem(cfg, args.path, args.kernel_reps)
         next_steps["cross_kv"] = time_cross_kv(cfg, args.path, args.kernel_reps)
         next_steps["varlen"] = time_varlen(cfg, args.path, args.kernel_reps, enc_main, ms)
+        if args.path == "fp16":
+            next_steps["q8_weights"] = time_quantized(cfg, w, x, y, args.kernel_reps, 8)
+            next_steps["q4_weights"] = time_quantized(cfg, w, x, y, args.kernel_reps, 4)
 
     cpu = None
     if not args.no_cpu_baseline:

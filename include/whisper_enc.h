@@ -52,10 +52,22 @@ extern "C" {
  * statistics, softmax state and the residual stream are fp32 on every path.
  *   BF16 - bfloat16 MFMA operands (weights rounded to nearest even when packed);
  *   FP32 - fp32 operands and intermediates (fp32 MFMA), the fallback path;
- *   FP16 - IEEE half MFMA operands, same MFMA rate as BF16 with 3 more mantissa bits. */
+ *   FP16 - IEEE half MFMA operands, same MFMA rate as BF16 with 3 more mantissa bits;
+ *   Q8, Q4 - layer and stack calls only (every other entry point rejects them): the packed
+ *     weight matrices are stored as int8 (Q8) or int4 (Q4) codes in blocks of 32 consecutive
+ *     input columns with one fp16 scale per block, quantised from the matrices rounded to bf16
+ *     (oxinfer whisper/model.rs, Precision and make_lin: q8 / q4 blocks of 32 from bf16).  The
+ *     encodings follow the q8_0 / q4_0 block formats:
+ *       Q8: d = amax / 127, code = round-half-away(x / d) in [-127, 127], value = code * d;
+ *       Q4: m = first element of largest magnitude, d = m / -8,
+ *           code = min(15, floor(x / d + 8.5)) in [0, 15], value = (code - 8) * d;
+ *     (fp32 arithmetic, x times the correctly rounded fp32 1 / d; d stored as fp16).  Each block
+ *     call expands its layer's matrices to fp16 in the workspace and runs the FP16 path. */
 #define WENC_PATH_BF16 0
 #define WENC_PATH_FP32 1
 #define WENC_PATH_FP16 2
+#define WENC_PATH_Q8 3
+#define WENC_PATH_Q4 4
 
 /* Element types of step-level outputs. */
 #define WENC_DTYPE_F32 0
@@ -84,8 +96,10 @@ const char* whisper_enc_strerror(int code);
  * invalid.  The blob holds LN1/LN2 gamma and beta, the QKV bias with a zero K slot, the out,
  * fc1 and fc2 biases (all fp32), and Wqkv [3d, d] (Q, K, V row blocks), Wo [d, d],
  * W1 [ffn, d], W2 [d, ffn] in the path's operand type (oxinfer Precision: norms and biases
- * always stay f32; turbospark-runtime DecLayerGpu: packed [3d, d] QKV with a zero K bias).
- * The blob is opaque: only whisper_enc_pack_layer writes it.
+ * always stay f32; turbospark-runtime DecLayerGpu: packed [3d, d] QKV with a zero K bias);
+ * on WENC_PATH_Q8 / WENC_PATH_Q4 the matrices are held as codes plus fp16 block scales
+ * (1 + 1/16 or 1/2 + 1/16 bytes per weight).  The blob is opaque: only whisper_enc_pack_layer
+ * writes it.
  */
 size_t whisper_enc_layer_bytes(int d_model, int ffn_dim, int path);
 
@@ -107,7 +121,8 @@ int whisper_enc_pack_layer(const float* ln1_g, const float* ln1_b, const float* 
 /*
  * Workspace bytes a block/stack call needs for `batch` windows of `t` positions: the LN
  * output / attention output [batch*t, d] and the QKV / FFN hidden activations
- * [batch*t, max(3d, ffn)], in the path's operand type.  0 if the arguments are invalid.
+ * [batch*t, max(3d, ffn)], in the path's operand type, and on the Q8 / Q4 paths room for one
+ * layer's matrices expanded to fp16 (2 (4d^2 + 2 d ffn) bytes).  0 if the arguments are invalid.
  */
 size_t whisper_enc_workspace_bytes(int batch, int t, int d_model, int heads, int ffn_dim,
                                    int path);
@@ -168,6 +183,24 @@ int whisper_enc_linear(const void* a, const void* w, const float* bias, const fl
  */
 int whisper_enc_attention(const void* q, const void* k, const void* v, void* o, int batch, int t,
                           int heads, int ld_qkv, int ld_o, int path, void* stream);
+
+/* ---- Low-precision weights, one matrix at a time (what the Q8 / Q4 layer paths use). ---- */
+
+/*
+ * Quantise w [n, k] (device fp32, k % 32 == 0) into codes and fp16 scales [n, k / 32] (device,
+ * scales 2-byte aligned) with the WENC_PATH_Q8 (bits 8: int8 codes [n, k]) or WENC_PATH_Q4
+ * (bits 4: codes [n, k / 2] bytes, column 2i in the low nibble of byte i, 2i + 1 in the high one)
+ * encoding.  Asynchronous on `stream`.
+ */
+int whisper_enc_quantize_matrix(const float* w, void* codes, void* scales, int n, int k, int bits,
+                                void* stream);
+
+/*
+ * Expand codes + scales (as written by whisper_enc_quantize_matrix; codes and dst 16-byte
+ * aligned) to fp16 dst [n, k]: value code * scale (Q4: (code - 8) * scale) rounded once to fp16.
+ */
+int whisper_enc_dequantize_matrix(const void* codes, const void* scales, void* dst, int n, int k,
+                                  int bits, void* stream);
 
 /* ---- Ragged batches: windows of different lengths packed back to back. ---- */
 

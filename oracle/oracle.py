@@ -398,7 +398,8 @@ def quantize_q4(w):
     x = bf16_round(w).reshape(w.shape[0], -1, QBLOCK)
     first = np.argmax(np.abs(x), axis=2)  # first index of the largest magnitude
     m = np.take_along_axis(x, first[:, :, None], axis=2)[:, :, 0].astype(np.float32)
-    d = (m / np.float32(-8.0)).astype(np.float32)
+    # m / -8 (an all-zero block takes the scale +0: the sign of a zero scale carries nothing)
+    d = np.where(m != 0, m / np.float32(-8.0), np.float32(0.0)).astype(np.float32)
     with np.errstate(divide="ignore"):
         idv = np.where(d != 0, np.float32(1.0) / d, np.float32(0.0)).astype(np.float32)
     v = ((x * idv[:, :, None]).astype(np.float32) + np.float32(8.5)).astype(np.float32)

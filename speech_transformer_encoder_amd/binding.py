@@ -28,6 +28,8 @@ WENC_ERR_HIP = 4
 WENC_PATH_BF16 = 0
 WENC_PATH_FP32 = 1
 WENC_PATH_FP16 = 2
+WENC_PATH_Q8 = 3
+WENC_PATH_Q4 = 4
 PATHS = {"bf16": WENC_PATH_BF16, "fp32": WENC_PATH_FP32, "fp16": WENC_PATH_FP16}
 
 WENC_DTYPE_F32 = 0
@@ -58,7 +60,7 @@ EXPORTS = (
     "whisper_enc_stem_bytes", "whisper_enc_pack_stem", "whisper_enc_stem_workspace_bytes",
     "whisper_enc_stem_forward",
     "whisper_enc_varlen_workspace_bytes", "whisper_enc_stack_forward_varlen",
-    "whisper_enc_attention_varlen",
+    "whisper_enc_attention_varlen", "whisper_enc_quantize_matrix", "whisper_enc_dequantize_matrix",
 )
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -102,6 +104,8 @@ def load() -> ctypes.CDLL:
         "whisper_enc_varlen_workspace_bytes": (Z, [I, I, I, I, I, I, I]),
         "whisper_enc_stack_forward_varlen": (I, [P, P, P, I, P, P, P, I, I, I, I, I, I, I, P, Z, P]),
         "whisper_enc_attention_varlen": (I, [P, P, P, P, P, I, I, I, I, I, I, I, P]),
+        "whisper_enc_quantize_matrix": (I, [P, P, P, I, I, I, P]),
+        "whisper_enc_dequantize_matrix": (I, [P, P, P, I, I, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -261,3 +265,13 @@ def whisper_enc_attention_varlen(q, k, v, o, cu_seqlens, batch, total_rows, max_
                                                _ptr(cu_seqlens), batch, total_rows, max_t, heads,
                                                ld_qkv, ld_o, path, _stream(stream)),
            "whisper_enc_attention_varlen")
+
+
+def whisper_enc_quantize_matrix(w, codes, scales, n, k, bits, stream=None) -> None:
+    _check(load().whisper_enc_quantize_matrix(_ptr(w), _ptr(codes), _ptr(scales), n, k, bits,
+                                              _stream(stream)), "whisper_enc_quantize_matrix")
+
+
+def whisper_enc_dequantize_matrix(codes, scales, dst, n, k, bits, stream=None) -> None:
+    _check(load().whisper_enc_dequantize_matrix(_ptr(codes), _ptr(scales), _ptr(dst), n, k, bits,
+                                                _stream(stream)), "whisper_enc_dequantize_matrix")

@@ -28,11 +28,25 @@ int path_dtype(int path) {
 
 size_t elem_bytes(int path) { return path == WENC_PATH_FP32 ? 4 : 2; }
 
+// Weight storage of the q8 / q4 paths (0 for the others); their activations are fp16.
+int quant_bits(int path) { return path == WENC_PATH_Q8 ? 8 : path == WENC_PATH_Q4 ? 4 : 0; }
+
+// Operand type of a block or stack: the step-level entry points take path_dtype (no q8 / q4).
+int layer_dtype(int path) { return quant_bits(path) ? DT_F16 : path_dtype(path); }
+
+// Bytes of one stored [n][k] matrix: codes (int8 or nibbles) for q8 / q4, else operand values.
+size_t matrix_bytes(size_t n, size_t k, int path) {
+  const int bits = quant_bits(path);
+  return bits ? n * k * bits / 8 : n * k * elem_bytes(path);
+}
+size_t scale_bytes(size_t n, size_t k, int path) { return quant_bits(path) ? n * (k / 32) * 2 : 0; }
+
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct LayerLayout {
   size_t ln1_g, ln1_b, bqkv, bo, ln2_g, ln2_b, b1, b2;  // fp32 sections
-  size_t wqkv, wo, w1, w2;                              // operand-type sections
+  size_t wqkv, wo, w1, w2;  // operand-type values, or q8 / q4 codes
+  size_t sqkv, so, s1, s2;  // q8 / q4: fp16 scales [n][k / 32] (empty otherwise)
   size_t total;
 };
 
@@ -44,7 +58,6 @@ LayerLayout layer_layout(int d, int f, int path) {
     off += round_up(bytes);
     return o;
   };
-  const size_t es = elem_bytes(path);
   L.ln1_g = take(4 * (size_t)d);
   L.ln1_b = take(4 * (size_t)d);
   L.bqkv = take(4 * 3 * (size_t)d);
@@ -53,10 +66,14 @@ LayerLayout layer_layout(int d, int f, int path) {
   L.ln2_b = take(4 * (size_t)d);
   L.b1 = take(4 * (size_t)f);
   L.b2 = take(4 * (size_t)d);
-  L.wqkv = take(es * 3 * (size_t)d * d);
-  L.wo = take(es * (size_t)d * d);
-  L.w1 = take(es * (size_t)f * d);
-  L.w2 = take(es * (size_t)d * f);
+  L.wqkv = take(matrix_bytes(3 * (size_t)d, d, path));
+  L.wo = take(matrix_bytes(d, d, path));
+  L.w1 = take(matrix_bytes(f, d, path));
+  L.w2 = take(matrix_bytes(d, f, path));
+  L.sqkv = take(scale_bytes(3 * (size_t)d, d, path));
+  L.so = take(scale_bytes(d, d, path));
+  L.s1 = take(scale_bytes(f, d, path));
+  L.s2 = take(scale_bytes(d, f, path));
   L.total = off;
   return L;
 }
@@ -68,7 +85,7 @@ bool valid_dims(int d, int f) {
 
 // Shape check shared by workspace/block/stack: returns WENC_OK, ARG or UNSUPPORTED.
 int check_shape(int batch, int t, int d, int heads, int f, int path) {
-  if (path_dtype(path) < 0) return WENC_ERR_ARG;
+  if (layer_dtype(path) < 0) return WENC_ERR_ARG;
   if (batch < 0 || t < 0 || heads <= 0) return WENC_ERR_ARG;
   if ((long long)batch * t > WENC_MAX_ROWS) return WENC_ERR_ARG;
   if (!valid_dims(d, f)) return WENC_ERR_ARG;
@@ -83,18 +100,42 @@ int check_shape(int batch, int t, int d, int heads, int f, int path) {
 struct Workspace {
   void* a;  // [M, d]: LN outputs and the attention output
   void* b;  // [M, max(3d, f)]: QKV, then the FFN hidden activations
+  uint16_t* wqkv = nullptr;  // q8 / q4: the block's weights expanded to fp16
+  uint16_t* wo = nullptr;
+  uint16_t* w1 = nullptr;
+  uint16_t* w2 = nullptr;
 };
+
+// Bytes of the fp16 weights of one layer (q8 / q4 paths): [3d][d], [d][d], [f][d], [d][f].
+size_t dequant_bytes(int d, int f, int path) {
+  if (!quant_bits(path)) return 0;
+  return round_up(2 * 3 * (size_t)d * d) + round_up(2 * (size_t)d * d) +
+         2 * round_up(2 * (size_t)f * d);
+}
 
 size_t workspace_size(size_t rows, int d, int f, int path) {
   const size_t es = elem_bytes(path);
   const size_t wb = (size_t)(3 * d > f ? 3 * d : f);
-  return round_up(rows * d * es) + round_up(rows * wb * es);
+  return round_up(rows * d * es) + round_up(rows * wb * es) + dequant_bytes(d, f, path);
 }
 
-Workspace carve(void* ws, size_t rows, int d, int path) {
+Workspace carve(void* ws, size_t rows, int d, int f, int path) {
   Workspace w;
-  w.a = ws;
-  w.b = static_cast<char*>(ws) + round_up(rows * d * elem_bytes(path));
+  const size_t es = elem_bytes(path);
+  const size_t wb = (size_t)(3 * d > f ? 3 * d : f);
+  char* p = static_cast<char*>(ws);
+  w.a = p;
+  w.b = p + round_up(rows * d * es);
+  if (quant_bits(path)) {
+    char* q = p + round_up(rows * d * es) + round_up(rows * wb * es);
+    w.wqkv = reinterpret_cast<uint16_t*>(q);
+    q += round_up(2 * 3 * (size_t)d * d);
+    w.wo = reinterpret_cast<uint16_t*>(q);
+    q += round_up(2 * (size_t)d * d);
+    w.w1 = reinterpret_cast<uint16_t*>(q);
+    q += round_up(2 * (size_t)f * d);
+    w.w2 = reinterpret_cast<uint16_t*>(q);
+  }
   return w;
 }
 
@@ -107,7 +148,7 @@ Workspace carve(void* ws, size_t rows, int d, int path) {
 int run_block(const float* x, float* y, const char* blob, int rows, int t, int batch, int d,
               int heads, int f, int path, const Workspace& ws, hipStream_t st, const int* cu) {
   const LayerLayout L = layer_layout(d, f, path);
-  const int dt = path_dtype(path);
+  const int dt = layer_dtype(path);
   const size_t es = elem_bytes(path);
   auto fp = [&](size_t off) { return reinterpret_cast<const float*>(blob + off); };
   const void* wqkv = blob + L.wqkv;
@@ -115,6 +156,21 @@ int run_block(const float* x, float* y, const char* blob, int rows, int t, int b
   const void* w1 = blob + L.w1;
   const void* w2 = blob + L.w2;
   char* qkv = static_cast<char*>(ws.b);
+  if (const int bits = quant_bits(path)) {
+    // Expand this layer's q8 / q4 matrices to fp16 in the workspace; the GEMMs read those.
+    auto sc = [&](size_t off) { return reinterpret_cast<const uint16_t*>(blob + off); };
+    DequantSegments seg{{blob + L.wqkv, blob + L.wo, blob + L.w1, blob + L.w2},
+                        {sc(L.sqkv), sc(L.so), sc(L.s1), sc(L.s2)},
+                        {ws.wqkv, ws.wo, ws.w1, ws.w2},
+                        {3 * d, d, f, d},
+                        {d, d, d, f},
+                        4};
+    WENC_TRY(launch_dequant(seg, bits, st));
+    wqkv = ws.wqkv;
+    wo = ws.wo;
+    w1 = ws.w1;
+    w2 = ws.w2;
+  }
 
   WENC_TRY(launch_layernorm(x, fp(L.ln1_g), fp(L.ln1_b), ws.a, rows, d, dt, st));
   WENC_TRY(launch_linear(ws.a, d, wqkv, fp(L.bqkv), nullptr, qkv, 3 * d, rows, 3 * d, d, dt,
@@ -151,7 +207,7 @@ const char* whisper_enc_strerror(int code) {
 }
 
 size_t whisper_enc_layer_bytes(int d_model, int ffn_dim, int path) {
-  if (path_dtype(path) < 0 || !valid_dims(d_model, ffn_dim)) return 0;
+  if (layer_dtype(path) < 0 || !valid_dims(d_model, ffn_dim)) return 0;
   return layer_layout(d_model, ffn_dim, path).total;
 }
 
@@ -161,16 +217,17 @@ int whisper_enc_pack_layer(const float* ln1_g, const float* ln1_b, const float* 
                            const float* ln2_g, const float* ln2_b, const float* w1,
                            const float* b1, const float* w2, const float* b2, int d_model,
                            int ffn_dim, int path, void* dst_layer, void* stream) {
-  if (path_dtype(path) < 0 || !valid_dims(d_model, ffn_dim)) return WENC_ERR_ARG;
+  if (layer_dtype(path) < 0 || !valid_dims(d_model, ffn_dim)) return WENC_ERR_ARG;
   const float* req[] = {ln1_g, ln1_b, wq, bq, wk, wv, bv, wo, bo, ln2_g, ln2_b, w1, b1, w2, b2};
   for (const float* p : req)
     if (!p) return WENC_ERR_ARG;
   if (!dst_layer || !aligned(dst_layer, kAlign)) return WENC_ERR_ARG;
 
-  const int d = d_model, f = ffn_dim, dt = path_dtype(path);
+  const int d = d_model, f = ffn_dim, dt = layer_dtype(path);
   const size_t dd = (size_t)d * d;
   const LayerLayout L = layer_layout(d, f, path);
   const size_t es = elem_bytes(path);
+  const int bits = quant_bits(path);
   char* blob = static_cast<char*>(dst_layer);
   auto fo = [&](size_t off) { return reinterpret_cast<float*>(blob + off); };
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -185,6 +242,17 @@ int whisper_enc_pack_layer(const float* ln1_g, const float* ln1_b, const float* 
   WENC_TRY(launch_copy_or_zero(ln2_b, fo(L.ln2_b), d, st));
   WENC_TRY(launch_copy_or_zero(b1, fo(L.b1), f, st));
   WENC_TRY(launch_copy_or_zero(b2, fo(L.b2), d, st));
+  if (bits) {
+    // q8 / q4: codes and fp16 scales; Q, K and V fill rows 0, d and 2d of the fused [3d][d].
+    const size_t crow = (size_t)d * bits / 8, srow = (size_t)(d / 32) * 2;  // bytes per row
+    for (int i = 0; i < 3; ++i)
+      WENC_TRY(launch_quantize(i == 0 ? wq : i == 1 ? wk : wv, blob + L.wqkv + i * d * crow,
+                               blob + L.sqkv + i * d * srow, d, d, bits, st));
+    WENC_TRY(launch_quantize(wo, blob + L.wo, blob + L.so, d, d, bits, st));
+    WENC_TRY(launch_quantize(w1, blob + L.w1, blob + L.s1, f, d, bits, st));
+    WENC_TRY(launch_quantize(w2, blob + L.w2, blob + L.s2, d, f, bits, st));
+    return WENC_OK;
+  }
   WENC_TRY(launch_convert(wq, blob + L.wqkv, dd, dt, st));
   WENC_TRY(launch_convert(wk, blob + L.wqkv + es * dd, dd, dt, st));
   WENC_TRY(launch_convert(wv, blob + L.wqkv + es * 2 * dd, dd, dt, st));
@@ -226,7 +294,7 @@ int stack_impl(const float* x, float* y, const void* layers, int n_layers, const
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const size_t lb = layer_layout(d_model, ffn_dim, path).total;
-  const Workspace ws = carve(workspace, rows, d_model, path);
+  const Workspace ws = carve(workspace, rows, d_model, ffn_dim, path);
   const float* src = x;
   for (int l = 0; l < n_layers; ++l) {
     rc = run_block(src, y, static_cast<const char*>(layers) + (size_t)l * lb, (int)rows, t, batch,
@@ -599,6 +667,42 @@ int whisper_enc_stem_forward(const float* mel, float* x, const void* stem, int b
   WENC_TRY(launch_unfold_s2(w.h, w.cols2, fp(L.pos), x, batch, t_mel, t2, d, dt, st));
   WENC_TRY(launch_linear(w.cols2, 3 * d, blob + L.w2, fp(L.b2), x, x, d, m2, d, 3 * d, dt,
                          EPI_BIAS_GELU_RESIDUAL, st));
+  return WENC_OK;
+}
+
+}  // extern "C"
+
+// ---- Low-precision weights, one matrix at a time (the quantiser and dequantiser the q8 / q4
+// layer paths use). ----
+
+extern "C" {
+
+int whisper_enc_quantize_matrix(const float* w, void* codes, void* scales, int n, int k, int bits,
+                                void* stream) {
+  if ((bits != 8 && bits != 4) || n < 0 || k < 0 || k % 32 != 0 || n > WENC_MAX_ROWS ||
+      k > WENC_MAX_FFN_DIM)
+    return WENC_ERR_ARG;
+  if ((size_t)n * k == 0) return WENC_OK;
+  if (!w || !codes || !scales || !aligned(scales, 2)) return WENC_ERR_ARG;
+  WENC_TRY(launch_quantize(w, codes, scales, n, k, bits, static_cast<hipStream_t>(stream)));
+  return WENC_OK;
+}
+
+int whisper_enc_dequantize_matrix(const void* codes, const void* scales, void* dst, int n, int k,
+                                  int bits, void* stream) {
+  if ((bits != 8 && bits != 4) || n < 0 || k < 0 || k % 32 != 0 || n > WENC_MAX_ROWS ||
+      k > WENC_MAX_FFN_DIM)
+    return WENC_ERR_ARG;
+  if ((size_t)n * k == 0) return WENC_OK;
+  if (!codes || !scales || !dst || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(dst, 16))
+    return WENC_ERR_ARG;
+  DequantSegments seg{{codes, nullptr, nullptr, nullptr},
+                      {static_cast<const uint16_t*>(scales), nullptr, nullptr, nullptr},
+                      {static_cast<uint16_t*>(dst), nullptr, nullptr, nullptr},
+                      {n, 0, 0, 0},
+                      {k, 0, 0, 0},
+                      1};
+  WENC_TRY(launch_dequant(seg, bits, static_cast<hipStream_t>(stream)));
   return WENC_OK;
 }
 

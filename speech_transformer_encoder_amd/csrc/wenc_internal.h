@@ -47,6 +47,20 @@ hipError_t launch_convert(const float* src, void* dst, size_t n, int dtype, hipS
 // dst[i] = src ? src[i] : 0 for i < n (fp32).
 hipError_t launch_copy_or_zero(const float* src, float* dst, size_t n, hipStream_t st);
 
+// Low-precision weights (quant.hip).  quantize: w [n][k] fp32 -> codes (int8 [n][k] for bits 8;
+// nibbles [n][k / 2] for bits 4, column 2i low, 2i + 1 high) and fp16 scales [n][k / 32].
+// dequant: up to four matrices of codes + scales -> fp16 [n][k].
+struct DequantSegments {
+  const void* codes[4];
+  const uint16_t* scales[4];
+  uint16_t* dst[4];
+  int n[4], k[4];
+  int count;
+};
+hipError_t launch_quantize(const float* w, void* codes, void* scales, int n, int k, int bits,
+                           hipStream_t st);
+hipError_t launch_dequant(const DequantSegments& seg, int bits, hipStream_t st);
+
 // Conv front end rearrangements (stem.hip).  dst[o][j * cin + i] = w[o][i][j] (zero past 3 cin,
 // kp columns); unfold_s1: out[b t + i][j c + q] = src[b][i + j - 1][q] (fp32 src, kp columns);
 // unfold_s2: out[b t2 + i][j d + q] = src[b t + 2 i + j - 1][q] (src in dtype) and

@@ -78,7 +78,7 @@ def test_block_validation(lib):
     assert _block(lib, heads=5) == B.WENC_ERR_ARG              # d % heads != 0
     assert _block(lib, d=100, heads=1) == B.WENC_ERR_ARG
     assert _block(lib, f=100) == B.WENC_ERR_ARG
-    assert _block(lib, path=3) == B.WENC_ERR_ARG
+    assert _block(lib, path=7) == B.WENC_ERR_ARG
     assert _block(lib, batch=-1) == B.WENC_ERR_ARG
     assert _block(lib, x=None) == B.WENC_ERR_ARG
     assert _block(lib, layer=None) == B.WENC_ERR_ARG
@@ -221,3 +221,30 @@ def test_varlen_sizes_and_validation(lib):
     assert attn(ld=1000) == B.WENC_ERR_ARG
     assert attn(max_t=1 << 20) == B.WENC_ERR_UNSUPPORTED
     assert attn(q=None, cu=None, total=0) == B.WENC_OK
+
+
+def test_quantized_paths_sizes_and_validation(lib):
+    d, f = 1280, 5120
+    fp16 = B.whisper_enc_layer_bytes(d, f, B.WENC_PATH_FP16)
+    q8 = B.whisper_enc_layer_bytes(d, f, B.WENC_PATH_Q8)
+    q4 = B.whisper_enc_layer_bytes(d, f, B.WENC_PATH_Q4)
+    weights = 4 * d * d + 2 * d * f
+    assert q8 >= weights * (1 + 1 / 16) and q8 < fp16 * 0.55
+    assert q4 >= weights * (0.5 + 1 / 16) and q4 < fp16 * 0.3
+    ws16 = B.whisper_enc_workspace_bytes(16, 1500, d, 20, f, B.WENC_PATH_FP16)
+    assert B.whisper_enc_workspace_bytes(16, 1500, d, 20, f, B.WENC_PATH_Q8) >= ws16 + 2 * weights
+    # the step-level entry points take operand types only
+    assert lib.whisper_enc_linear(FAKE, FAKE, FAKE, None, FAKE, 64, 64, 64, B.WENC_PATH_Q8,
+                                  B.WENC_EPI_BIAS, None) == B.WENC_ERR_ARG
+    assert lib.whisper_enc_attention(FAKE, FAKE, FAKE, FAKE, 1, 64, 1, 192, 64, B.WENC_PATH_Q4,
+                                     None) == B.WENC_ERR_ARG
+    assert B.whisper_enc_stem_bytes(80, 384, 1500, B.WENC_PATH_Q8) == 0
+    assert B.whisper_enc_cross_kv_bytes(384, 4, B.WENC_PATH_Q4) == 0
+    q = lambda *a: lib.whisper_enc_quantize_matrix(*a)  # noqa: E731
+    assert q(FAKE, FAKE, FAKE, 4, 64, 5, None) == B.WENC_ERR_ARG      # bits
+    assert q(FAKE, FAKE, FAKE, 4, 48, 8, None) == B.WENC_ERR_ARG      # k % 32
+    assert q(FAKE, FAKE, FAKE + 1, 4, 64, 8, None) == B.WENC_ERR_ARG  # scales alignment
+    assert q(None, None, None, 0, 64, 4, None) == B.WENC_OK
+    dq = lambda *a: lib.whisper_enc_dequantize_matrix(*a)  # noqa: E731
+    assert dq(FAKE + 8, FAKE, FAKE, 4, 64, 8, None) == B.WENC_ERR_ARG
+    assert dq(FAKE, FAKE, None, 4, 64, 4, None) == B.WENC_ERR_ARG

@@ -351,15 +351,21 @@ def time_quantized(cfg, w, x, y, reps, bits):
     from speech_transformer_encoder_amd import binding as B
     from speech_transformer_encoder_amd.encoder import build_from_workload
     path = B.WENC_PATH_Q8 if bits == 8 else B.WENC_PATH_Q4
+    ref = build_from_workload(w, B.WENC_PATH_FP16)
     enc = build_from_workload(w, path)
+    ref.workspace(cfg.batch, cfg.t)
     enc.workspace(cfg.batch, cfg.t)
-    ms = time_events(lambda: enc.forward(x, y), reps, torch.cuda.current_stream())
-    out = {"ms": round(ms, 4), "value": round(cfg.batch * cfg.t / (ms * 1e-3), 1),
-           "unit": "frames/s",
+    st = torch.cuda.current_stream()
+    # fp16 weights timed before and after, in the same loop, against order effects
+    ms16a = time_events(lambda: ref.forward(x, y), reps, st)
+    ms = time_events(lambda: enc.forward(x, y), reps, st)
+    ms16 = 0.5 * (ms16a + time_events(lambda: ref.forward(x, y), reps, st))
+    out = {"ms": round(ms, 4), "fp16_ms_same_loop": round(ms16, 4),
+           "value": round(cfg.batch * cfg.t / (ms * 1e-3), 1), "unit": "frames/s",
            "layer_bytes": B.whisper_enc_layer_bytes(cfg.d_model, cfg.ffn_dim, path),
            "fp16_layer_bytes": B.whisper_enc_layer_bytes(cfg.d_model, cfg.ffn_dim,
                                                          B.WENC_PATH_FP16)}
-    del enc
+    del enc, ref
     torch.cuda.empty_cache()
     return out
 

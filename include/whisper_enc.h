@@ -197,7 +197,8 @@ int whisper_enc_quantize_matrix(const float* w, void* codes, void* scales, int n
 
 /*
  * Expand codes + scales (as written by whisper_enc_quantize_matrix; codes and dst 16-byte
- * aligned) to fp16 dst [n, k]: value code * scale (Q4: (code - 8) * scale) rounded once to fp16.
+ * aligned) to fp16 dst [n, k]: value code * scale (Q4: (code - 8) * scale) rounded once to fp16;
+ * n * k / 8 >= 2^31 gives WENC_ERR_UNSUPPORTED.
  */
 int whisper_enc_dequantize_matrix(const void* codes, const void* scales, void* dst, int n, int k,
                                   int bits, void* stream);

@@ -694,6 +694,7 @@ int whisper_enc_dequantize_matrix(const void* codes, const void* scales, void* d
       k > WENC_MAX_FFN_DIM)
     return WENC_ERR_ARG;
   if ((size_t)n * k == 0) return WENC_OK;
+  if ((size_t)n * (k / 8) > (size_t)INT32_MAX) return WENC_ERR_UNSUPPORTED;
   if (!codes || !scales || !dst || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(dst, 16))
     return WENC_ERR_ARG;
   DequantSegments seg{{codes, nullptr, nullptr, nullptr},

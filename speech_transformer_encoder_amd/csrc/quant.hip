@@ -11,6 +11,8 @@
 // At rest a layer's matrices stay quantised (1 + 1/16 or 1/2 + 1/16 bytes per weight); before a
 // block runs, one HBM-bound kernel expands them to fp16 in the workspace and the fp16 GEMMs read
 // those.  Dequantised values are code * d16 rounded once to fp16.
+#include <algorithm>
+
 #include "wenc_device.h"
 #include "wenc_internal.h"
 
@@ -70,40 +72,37 @@ __global__ void quantize_kernel(const float* __restrict__ w, uint8_t* __restrict
   }
 }
 
-// Eight consecutive outputs per thread over up to four matrices (segment s: rows n[s], columns
-// k[s]); fp16 results, 16-byte stores.
+// Eight consecutive outputs per thread; grid row blockIdx.y is matrix s (rows n[s], columns
+// k[s]); fp16 results, 16-byte stores.  Each matrix has fewer than 2^31 eight-column vectors.
 template <int BITS>
 __global__ void dequant_kernel(DequantSegments seg) {
-  size_t start[5] = {0, 0, 0, 0, 0};
-  for (int s = 0; s < seg.count; ++s) start[s + 1] = start[s] + (size_t)seg.n[s] * (seg.k[s] / 8);
-  const size_t total = start[seg.count];
-  for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total;
-       e += (size_t)gridDim.x * blockDim.x) {
-    int s = 0;
-    while (s + 1 < seg.count && e >= start[s + 1]) ++s;
-    const size_t local = e - start[s];
-    const int kv = seg.k[s] / 8;
-    const int row = (int)(local / kv), c0 = (int)(local % kv) * 8;
-    const float d = (float)__builtin_bit_cast(
-        _Float16, seg.scales[s][(size_t)row * (seg.k[s] / 32) + c0 / 32]);
+  const int s = blockIdx.y;
+  if (s >= seg.count) return;
+  const uint32_t k = (uint32_t)seg.k[s], kv = k / 8, nb = k / 32;
+  const uint32_t total = (uint32_t)seg.n[s] * kv;
+  const uint8_t* codes = static_cast<const uint8_t*>(seg.codes[s]);
+  const uint16_t* scales = seg.scales[s];
+  uint16_t* dst = seg.dst[s];
+  for (uint32_t e = blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += gridDim.x * blockDim.x) {
+    const uint32_t row = e / kv, c0 = (e - row * kv) * 8;
+    const float d = (float)__builtin_bit_cast(_Float16, scales[(size_t)row * nb + c0 / 32]);
     float v[8];
     if constexpr (BITS == 8) {
-      const uint2 c = *reinterpret_cast<const uint2*>(
-          reinterpret_cast<const uint8_t*>(seg.codes[s]) + (size_t)row * seg.k[s] + c0);
+      const uint2 c = *reinterpret_cast<const uint2*>(codes + (size_t)row * k + c0);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint32_t word = i < 4 ? c.x : c.y;
         v[i] = (float)(int8_t)(word >> (8 * (i & 3))) * d;
       }
     } else {
-      const uint32_t c = *reinterpret_cast<const uint32_t*>(
-          reinterpret_cast<const uint8_t*>(seg.codes[s]) + (size_t)row * (seg.k[s] / 2) + c0 / 2);
+      const uint32_t c = *reinterpret_cast<const uint32_t*>(codes + (size_t)row * (k / 2) + c0 / 2);
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = (float)((int)((c >> (4 * i)) & 15u) - 8) * d;
     }
     const u32x4 o = {Cvt<f16_t>::pack(v[0], v[1]), Cvt<f16_t>::pack(v[2], v[3]),
                      Cvt<f16_t>::pack(v[4], v[5]), Cvt<f16_t>::pack(v[6], v[7])};
-    *reinterpret_cast<u32x4*>(seg.dst[s] + (size_t)row * seg.k[s] + c0) = o;
+    *reinterpret_cast<u32x4*>(dst + (size_t)row * k + c0) = o;
   }
 }
 
@@ -129,10 +128,10 @@ hipError_t launch_quantize(const float* w, void* codes, void* scales, int n, int
 }
 
 hipError_t launch_dequant(const DequantSegments& seg, int bits, hipStream_t st) {
-  size_t total = 0;
-  for (int s = 0; s < seg.count; ++s) total += (size_t)seg.n[s] * (seg.k[s] / 8);
-  if (total == 0) return hipSuccess;
-  const dim3 g = grid_for(total);
+  size_t most = 0;
+  for (int s = 0; s < seg.count; ++s) most = std::max(most, (size_t)seg.n[s] * (seg.k[s] / 8));
+  if (most == 0) return hipSuccess;
+  const dim3 g(grid_for(most).x, (unsigned)seg.count);
   if (bits == 8)
     dequant_kernel<8><<<g, 256, 0, st>>>(seg);
   else if (bits == 4)

@@ -370,6 +370,39 @@ def time_quantized(cfg, w, x, y, reps, bits):
     return out
 
 
+def time_graph(path_name, reps):
+    """A launch-bound call: the base stack (6 blocks + final LayerNorm, one 1500-position window),
+    called eagerly (7 launches per block from the host) and replayed from a HIP graph captured
+    from the same C ABI call."""
+    import torch
+    from speech_transformer_encoder_amd import binding as B
+    from speech_transformer_encoder_amd import synth
+    from speech_transformer_encoder_amd.encoder import build_from_workload, to_device_input
+    cfg = synth.CONFIGS["base_stack"]
+    w = synth.make_workload(cfg)
+    enc = build_from_workload(w, B.PATHS[path_name])
+    x = to_device_input(w.x)
+    y = torch.empty_like(x)
+    enc.workspace(cfg.batch, cfg.t)
+    st = torch.cuda.current_stream()
+    eager = time_events(lambda: enc.forward(x, y), reps, st)
+    s = torch.cuda.Stream()
+    s.wait_stream(st)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            enc.forward(x, y, stream=s.cuda_stream)
+    torch.cuda.synchronize()
+    replay = time_events(graph.replay, reps, st)
+    frames = cfg.batch * cfg.t
+    out = {"workload": cfg.name, "blocks": cfg.n_layers, "eager_ms": round(eager, 4),
+           "graph_ms": round(replay, 4), "eager_frames_per_s": round(frames / (eager * 1e-3), 1),
+           "graph_frames_per_s": round(frames / (replay * 1e-3), 1)}
+    del graph, enc
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, windows, layers):
     """The oracle as it stands, on a bounded sample of the workload (first windows / layers)."""
     import numpy as np
@@ -491,6 +524,7 @@ def main():
         next_steps["stem"] = time_stem(cfg, args.path, args.kernel_reps)
         next_steps["cross_kv"] = time_cross_kv(cfg, args.path, args.kernel_reps)
         next_steps["varlen"] = time_varlen(cfg, args.path, args.kernel_reps, enc_main, ms)
+        next_steps["graph"] = time_graph(args.path, args.kernel_reps)
         if args.path == "fp16":
             next_steps["q8_weights"] = time_quantized(cfg, w, x, y, args.kernel_reps, 8)
             next_steps["q4_weights"] = time_quantized(cfg, w, x, y, args.kernel_reps, 4)

@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/whisper_enc.h"
 #include "wenc_internal.h"
 
@@ -100,6 +102,7 @@ int check_shape(int batch, int t, int d, int heads, int f, int path) {
 struct Workspace {
   void* a;  // [M, d]: LN outputs and the attention output
   void* b;  // [M, max(3d, f)]: QKV, then the FFN hidden activations
+  float* part = nullptr;  // split-k parts of the residual GEMMs when M is small (else empty)
   uint16_t* wqkv = nullptr;  // q8 / q4: the block's weights expanded to fp16
   uint16_t* wo = nullptr;
   uint16_t* w1 = nullptr;
@@ -113,10 +116,19 @@ size_t dequant_bytes(int d, int f, int path) {
          2 * round_up(2 * (size_t)f * d);
 }
 
+// fp32 parts of the split-k residual GEMMs of a block (out-projection and fc2, both [M, d]).
+size_t split_bytes(size_t rows, int d, int f, int path) {
+  const int dt = layer_dtype(path);
+  const int s = std::max(linear_split((int)rows, d, d, dt, EPI_BIAS_RESIDUAL),
+                         linear_split((int)rows, d, f, dt, EPI_BIAS_RESIDUAL));
+  return s > 1 ? round_up((size_t)s * rows * d * sizeof(float)) : 0;
+}
+
 size_t workspace_size(size_t rows, int d, int f, int path) {
   const size_t es = elem_bytes(path);
   const size_t wb = (size_t)(3 * d > f ? 3 * d : f);
-  return round_up(rows * d * es) + round_up(rows * wb * es) + dequant_bytes(d, f, path);
+  return round_up(rows * d * es) + round_up(rows * wb * es) + dequant_bytes(d, f, path) +
+         split_bytes(rows, d, f, path);
 }
 
 Workspace carve(void* ws, size_t rows, int d, int f, int path) {
@@ -136,6 +148,9 @@ Workspace carve(void* ws, size_t rows, int d, int f, int path) {
     q += round_up(2 * (size_t)f * d);
     w.w2 = reinterpret_cast<uint16_t*>(q);
   }
+  if (split_bytes(rows, d, f, path))
+    w.part = reinterpret_cast<float*>(p + round_up(rows * d * es) + round_up(rows * wb * es) +
+                                      dequant_bytes(d, f, path));
   return w;
 }
 
@@ -177,11 +192,13 @@ int run_block(const float* x, float* y, const char* blob, int rows, int t, int b
                          EPI_BIAS, st));
   WENC_TRY(launch_attention(qkv, qkv + es * d, qkv + es * 2 * d, 3 * d, ws.a, d, batch, t, heads,
                             0.125f, dt, st, cu, rows));
-  WENC_TRY(launch_linear(ws.a, d, wo, fp(L.bo), x, y, d, rows, d, d, dt, EPI_BIAS_RESIDUAL, st));
+  WENC_TRY(launch_linear(ws.a, d, wo, fp(L.bo), x, y, d, rows, d, d, dt, EPI_BIAS_RESIDUAL, st,
+                         ws.part));
   WENC_TRY(launch_layernorm(y, fp(L.ln2_g), fp(L.ln2_b), ws.a, rows, d, dt, st));
   WENC_TRY(launch_linear(ws.a, d, w1, fp(L.b1), nullptr, ws.b, f, rows, f, d, dt, EPI_BIAS_GELU,
                          st));
-  WENC_TRY(launch_linear(ws.b, f, w2, fp(L.b2), y, y, d, rows, d, f, dt, EPI_BIAS_RESIDUAL, st));
+  WENC_TRY(launch_linear(ws.b, f, w2, fp(L.b2), y, y, d, rows, d, f, dt, EPI_BIAS_RESIDUAL, st,
+                         ws.part));
   return WENC_OK;
 }
 

@@ -26,6 +26,7 @@
 // workgroup per CU: each XCD (eight, dispatched round-robin) runs a contiguous range of tiles
 // grouped 8 m-tiles deep, so tiles running together share operand rows in that XCD's L2, and
 // the next tile's first operand loads overlap the current tile's epilogue.
+#include <algorithm>
 #include <type_traits>
 
 #include "wenc_device.h"
@@ -352,7 +353,8 @@ constexpr int H_LW = H_N / 16 / H_WAVES, H_LX = H_M / 16 / H_WAVES;  // 1 KB cop
 template <typename T, int EPI>
 __global__ __launch_bounds__(H_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm16_small_kernel(
     const uint16_t* __restrict__ X, int lda, const uint16_t* __restrict__ W,
-    const float* __restrict__ bias, const float* residual, void* C, int ldc, int M, int N, int K) {
+    const float* __restrict__ bias, const float* residual, void* C, int ldc, int M, int N, int K,
+    int ksplit) {
   // One array for the three stages: the copies are inline assembly, invisible to the compiler's
   // wait insertion, so separate arrays buy nothing; the epilogue reuses the whole 72 KB.
   __shared__ __attribute__((aligned(1024))) uint16_t lds[3 * H_STAGE];
@@ -366,12 +368,16 @@ __global__ __launch_bounds__(H_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
   const int g = lane >> 5, frow = lane & 31;
 
   const int tiles_m = (M + H_M - 1) / H_M, tiles_n = (N + H_N - 1) / H_N;
-  const int v = xcd_virtual_id(blockIdx.x, gridDim.x);
+  // Workgroup (tile, part): with ksplit > 1 (EPI_PARTIAL) part p covers k in
+  // [p K / ksplit, (p + 1) K / ksplit).
+  const int vv = xcd_virtual_id(blockIdx.x, gridDim.x);
+  const int v = vv / ksplit, part = vv % ksplit;
   const int group = 8 * tiles_n;
   const int first_m = (v / group) * 8;
   const int gm = min(tiles_m - first_m, 8);
   const int tm = first_m + (v % group) % gm, tn = (v % group) / gm;
   const int n0 = tn * H_N, m0 = tm * H_M;
+  const int kc = K / ksplit, kbyte0 = part * kc * 2;  // this part's first k, in bytes
 
   const int wrows = min(N - n0, H_N), xrows = min(M - m0, H_M);
   const u32x4 rW = buffer_rsrc(W + (size_t)n0 * K, (uint32_t)(wrows * K * 2));
@@ -383,7 +389,7 @@ __global__ __launch_bounds__(H_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
   const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
   const int voW = lrow * K * 2 + lchunk * 16, voX = lrow * lda * 2 + lchunk * 16;
   auto load_tile = [&](int kt, const uint16_t* st) {
-    const int ko = kt * (H_K * 2);
+    const int ko = kbyte0 + kt * (H_K * 2);
     const uint32_t base = lds_addr(st);
 #pragma unroll
     for (int i = 0; i < H_LW; ++i)
@@ -432,7 +438,7 @@ __global__ __launch_bounds__(H_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
   };
 
   constexpr int LT = H_LW + H_LX;  // copies per wavefront and tile
-  const int nk = K / H_K;
+  const int nk = kc / H_K;
   u32x4 fa0[H_NA], fb0[H_NB], fa1[H_NA], fb1[H_NB];
   load_tile(0, s0);
   if (nk > 1) load_tile(1, s1);
@@ -473,15 +479,26 @@ __global__ __launch_bounds__(H_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int c = a * 8 + 2 * j + g;
-        const float4 bb = cols_ok ? *reinterpret_cast<const float4*>(bias + nw + 4 * c)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 bb = (cols_ok && EPI != EPI_PARTIAL)
+                              ? *reinterpret_cast<const float4*>(bias + nw + 4 * c)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
         *reinterpret_cast<float4*>(ep + frow * 64 + ((c ^ (frow & 15)) << 2)) =
             make_float4(acc[a][b][4 * j] + bb.x, acc[a][b][4 * j + 1] + bb.y,
                         acc[a][b][4 * j + 2] + bb.z, acc[a][b][4 * j + 3] + bb.w);
       }
     if (!cols_ok) continue;
     const int mb = m0 + wm * H_TM + b * 32;
-    if constexpr (EPI == EPI_BIAS_RESIDUAL || EPI == EPI_BIAS_GELU_RESIDUAL) {
+    if constexpr (EPI == EPI_PARTIAL) {
+      // fp32 rows of 64 columns of this part's sums: partial[part][m][n], row stride N.
+      float* P = static_cast<float*>(C) + (size_t)part * M * N;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int r = (lane >> 4) + 4 * q, c = lane & 15;
+        const int m = mb + r;
+        const float4 v4 = *reinterpret_cast<const float4*>(ep + r * 64 + ((c ^ (r & 15)) << 2));
+        if (m < M) *reinterpret_cast<float4*>(P + (size_t)m * N + nw + 4 * c) = v4;
+      }
+    } else if constexpr (EPI == EPI_BIAS_RESIDUAL || EPI == EPI_BIAS_GELU_RESIDUAL) {
       float4 res[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -644,6 +661,44 @@ __global__ __launch_bounds__(256) void gemm32_kernel(const float* __restrict__ X
   }
 }
 
+// Second pass of a split-k residual GEMM: c = residual + epi(sum of the parts + bias), the parts
+// added in order (deterministic), four columns per thread.
+template <bool GELU>
+__global__ void splitk_reduce_kernel(const float* __restrict__ part, int ksplit,
+                                     const float* __restrict__ bias, const float* residual,
+                                     float* c, int ldc, int M, int N) {
+  const size_t total = (size_t)M * (N / 4);
+  const size_t plane = (size_t)M * N;
+  for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total;
+       e += (size_t)gridDim.x * blockDim.x) {
+    const int m = (int)(e / (N / 4)), n = (int)(e % (N / 4)) * 4;
+    float4 s = *reinterpret_cast<const float4*>(part + (size_t)m * N + n);
+    for (int p = 1; p < ksplit; ++p) {
+      const float4 q = *reinterpret_cast<const float4*>(part + p * plane + (size_t)m * N + n);
+      s = make_float4(s.x + q.x, s.y + q.y, s.z + q.z, s.w + q.w);
+    }
+    const float4 b = *reinterpret_cast<const float4*>(bias + n);
+    float4 v = make_float4(s.x + b.x, s.y + b.y, s.z + b.z, s.w + b.w);
+    if constexpr (GELU) v = make_float4(gelu_erf_as(v.x), gelu_erf_as(v.y), gelu_erf_as(v.z), gelu_erf_as(v.w));
+    const float4 r = *reinterpret_cast<const float4*>(residual + (size_t)m * ldc + n);
+    *reinterpret_cast<float4*>(c + (size_t)m * ldc + n) =
+        make_float4(r.x + v.x, r.y + v.y, r.z + v.z, r.w + v.w);
+  }
+}
+
+int linear_split(int m, int n, int k, int dtype, int epilogue) {
+  if (dtype == DT_F32 || (epilogue != EPI_BIAS_RESIDUAL && epilogue != EPI_BIAS_GELU_RESIDUAL))
+    return 1;
+  // Reference device: 256 CUs.  Split only problems the persistent kernel would not take, into
+  // parts of at least 256 k, while the parts still fit one workgroup per CU.
+  const long big = (long)((m + G_M - 1) / G_M) * ((n + G_N - 1) / G_N);
+  if (big >= 256) return 1;
+  const long small = (long)((m + H_M - 1) / H_M) * ((n + H_N - 1) / H_N);
+  int s = 1;
+  while (s < 8 && small * s * 2 <= 256 && k % (s * 2 * H_K) == 0 && k / (s * 2) >= 256) s *= 2;
+  return s;
+}
+
 // Workgroups of the persistent kernel: the current device's CU count, rounded down to a multiple
 // of the eight XCDs.
 static int persistent_grid() {
@@ -658,38 +713,51 @@ static int persistent_grid() {
 template <typename T, int EPI>
 static void launch16_epi(const uint16_t* X, int lda, const uint16_t* W, const float* bias,
                          const float* residual, void* c, int ldc, int m, int n, int k,
-                         hipStream_t st) {
+                         hipStream_t st, float* partial) {
   const long tiles = (long)((m + G_M - 1) / G_M) * ((n + G_N - 1) / G_N);
+  const long small = (long)((m + H_M - 1) / H_M) * ((n + H_N - 1) / H_N);
+  const int split = partial ? linear_split(m, n, k, DT_F16, EPI) : 1;
+  if constexpr (EPI == EPI_BIAS_RESIDUAL || EPI == EPI_BIAS_GELU_RESIDUAL) {
+    if (split > 1) {
+      gemm16_small_kernel<T, EPI_PARTIAL><<<dim3((unsigned)(small * split)), dim3(H_THREADS), 0,
+                                            st>>>(X, lda, W, bias, nullptr, partial, n, m, n, k,
+                                                  split);
+      const size_t total = (size_t)m * (n / 4);
+      const unsigned g = (unsigned)std::min<size_t>((total + 255) / 256, 16384);
+      splitk_reduce_kernel<EPI == EPI_BIAS_GELU_RESIDUAL><<<g, 256, 0, st>>>(
+          partial, split, bias, residual, static_cast<float*>(c), ldc, m, n);
+      return;
+    }
+  }
   const int grid = persistent_grid();
   if (tiles >= grid) {
     gemm16_kernel<T, EPI><<<dim3((unsigned)grid), dim3(G_THREADS), 0, st>>>(
         X, lda, W, bias, residual, c, ldc, m, n, k);
   } else {
-    const long small = (long)((m + H_M - 1) / H_M) * ((n + H_N - 1) / H_N);
     gemm16_small_kernel<T, EPI><<<dim3((unsigned)small), dim3(H_THREADS), 0, st>>>(
-        X, lda, W, bias, residual, c, ldc, m, n, k);
+        X, lda, W, bias, residual, c, ldc, m, n, k, 1);
   }
 }
 
 template <typename T>
 static hipError_t launch16(const void* a, int lda, const void* w, const float* bias,
                            const float* residual, void* c, int ldc, int m, int n, int k, int epi,
-                           hipStream_t st) {
+                           hipStream_t st, float* partial) {
   auto X = static_cast<const uint16_t*>(a);
   auto W = static_cast<const uint16_t*>(w);
   switch (epi) {
-    case EPI_BIAS: launch16_epi<T, EPI_BIAS>(X, lda, W, bias, residual, c, ldc, m, n, k, st); break;
+    case EPI_BIAS: launch16_epi<T, EPI_BIAS>(X, lda, W, bias, residual, c, ldc, m, n, k, st, partial); break;
     case EPI_BIAS_GELU:
-      launch16_epi<T, EPI_BIAS_GELU>(X, lda, W, bias, residual, c, ldc, m, n, k, st);
+      launch16_epi<T, EPI_BIAS_GELU>(X, lda, W, bias, residual, c, ldc, m, n, k, st, partial);
       break;
     case EPI_BIAS_RESIDUAL:
-      launch16_epi<T, EPI_BIAS_RESIDUAL>(X, lda, W, bias, residual, c, ldc, m, n, k, st);
+      launch16_epi<T, EPI_BIAS_RESIDUAL>(X, lda, W, bias, residual, c, ldc, m, n, k, st, partial);
       break;
     case EPI_BIAS_HEADMAJOR:
-      launch16_epi<T, EPI_BIAS_HEADMAJOR>(X, lda, W, bias, residual, c, ldc, m, n, k, st);
+      launch16_epi<T, EPI_BIAS_HEADMAJOR>(X, lda, W, bias, residual, c, ldc, m, n, k, st, partial);
       break;
     case EPI_BIAS_GELU_RESIDUAL:
-      launch16_epi<T, EPI_BIAS_GELU_RESIDUAL>(X, lda, W, bias, residual, c, ldc, m, n, k, st);
+      launch16_epi<T, EPI_BIAS_GELU_RESIDUAL>(X, lda, W, bias, residual, c, ldc, m, n, k, st, partial);
       break;
     default: return hipErrorInvalidValue;
   }
@@ -729,11 +797,13 @@ static hipError_t launch32(const void* a, int lda, const void* w, const float* b
 
 hipError_t launch_linear(const void* a, int lda, const void* w, const float* bias,
                          const float* residual, void* c, int ldc, int m, int n, int k, int dtype,
-                         int epilogue, hipStream_t st) {
+                         int epilogue, hipStream_t st, float* partial) {
   if (m == 0) return hipSuccess;
   switch (dtype) {
-    case DT_BF16: return launch16<bf16_t>(a, lda, w, bias, residual, c, ldc, m, n, k, epilogue, st);
-    case DT_F16: return launch16<f16_t>(a, lda, w, bias, residual, c, ldc, m, n, k, epilogue, st);
+    case DT_BF16:
+      return launch16<bf16_t>(a, lda, w, bias, residual, c, ldc, m, n, k, epilogue, st, partial);
+    case DT_F16:
+      return launch16<f16_t>(a, lda, w, bias, residual, c, ldc, m, n, k, epilogue, st, partial);
     case DT_F32: return launch32(a, lda, w, bias, residual, c, ldc, m, n, k, epilogue, st);
   }
   return hipErrorInvalidValue;

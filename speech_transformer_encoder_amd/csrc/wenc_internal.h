@@ -14,7 +14,8 @@ enum Epilogue {
   EPI_BIAS_GELU = 1,
   EPI_BIAS_RESIDUAL = 2,
   EPI_BIAS_HEADMAJOR = 3,
-  EPI_BIAS_GELU_RESIDUAL = 4
+  EPI_BIAS_GELU_RESIDUAL = 4,
+  EPI_PARTIAL = 5  // split-k part: raw fp32 sums (no bias) to partial[split][m][n]
 };
 
 // y[rows, d] = LayerNorm(x[rows, d]) * gamma + beta, stored as out_dtype.  d % 4 == 0, d <= 4096.
@@ -30,9 +31,15 @@ hipError_t launch_layernorm(const float* x, const float* gamma, const float* bet
 //                        column n = 64 j + e go to c[((b * (n / 64 count) + j) * T + i) * 64 + e],
 //                        with the window length T passed in ldc.
 // lda / ldc are row strides in elements.  k % 64 == 0, n % 64 == 0.
+// partial: optional fp32 scratch of linear_split(m, n, k, dtype, epilogue) * m * n floats; given,
+// a residual GEMM too small to fill the GPU splits k over that many workgroups and a second
+// kernel adds the parts in a fixed order (deterministic), then bias and residual.
 hipError_t launch_linear(const void* a, int lda, const void* w, const float* bias,
                          const float* residual, void* c, int ldc, int m, int n, int k, int dtype,
-                         int epilogue, hipStream_t st);
+                         int epilogue, hipStream_t st, float* partial = nullptr);
+// Number of k parts launch_linear uses with a partial buffer (1: none).  Fixed for a shape,
+// whatever the device, so that workspace sizes are too.
+int linear_split(int m, int n, int k, int dtype, int epilogue);
 
 // Bidirectional attention per (window, head), head_dim 64.  q/k/v/o rows of the window b at
 // ptr + (b * t + i) * ld, head h at column offset 64 * h.  scale multiplies q.k.

@@ -36,7 +36,8 @@
 
 namespace wenc {
 
-constexpr int AQ = 256;   // query rows per workgroup (8 wavefronts)
+// Query rows per workgroup: 32 per wavefront, NW = 8 wavefronts (fewer when a problem has too
+// few query blocks to fill the GPU, e.g. one 1500-position window).
 constexpr int AK = 64;    // keys per tile
 constexpr int ATILE = AK * 64;  // 16-bit elements of one K or V tile
 constexpr float P_BOUND = 32768.0f;  // largest probability kept without raising the max (2^15)
@@ -78,8 +79,8 @@ template <> struct RowSum<bf16_t> {
   }
 };
 
-template <typename T>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void attn16_kernel(const uint16_t* __restrict__ Q,
+template <typename T, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4))) void attn16_kernel(const uint16_t* __restrict__ Q,
                                                         const uint16_t* __restrict__ Kp,
                                                         const uint16_t* __restrict__ Vp, int ld,
                                                         uint16_t* __restrict__ O, int ldo, int tmax,
@@ -96,6 +97,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // 1-D grid over (query block, head, window), renumbered so that the query blocks of one
   // (window, head) run on the same XCD and read its K and V through one L2.
+  constexpr int AQ = 32 * NW;  // query rows of the workgroup
+  constexpr int CPW = 8 / NW;   // 8-row blocks of each K and V tile a wavefront copies
   const int nqb = (tmax + AQ - 1) / AQ;
   const int v = xcd_virtual_id(blockIdx.x, gridDim.x);
   const int qb = v % nqb;
@@ -131,12 +134,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int lr = 8 * wave + (lane >> 3);
   const int kvo = lr * ld * 2 + (((lane & 7) ^ ((lr >> 1) & 7)) << 4);
   const int vvo = lr * ld * 2 + (((lane & 7) ^ (((lr >> 1) & 1) << 2)) << 4);
+  // With NW < 8 wavefront w also copies rows 8 (w + NW i) .. + 7, i < CPW: a shift by a multiple
+  // of 16 rows leaves both swizzles unchanged.
   const uint32_t blk = (uint32_t)wave * 1024u;
   auto load_tile = [&](int j0, const uint16_t* st) {
-    const int ro = j0 * ld * 2;
     const uint32_t base = lds_addr(st) + blk;
-    lds_copy16(rK, base, kvo + ro);
-    lds_copy16(rV, base + ATILE * 2, vvo + ro);
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int ro = (j0 + 8 * NW * i) * ld * 2;
+      lds_copy16(rK, base + (uint32_t)(NW * i) * 1024u, kvo + ro);
+      lds_copy16(rV, base + ATILE * 2 + (uint32_t)(NW * i) * 1024u, vvo + ro);
+    }
   };
 
   const int xk = (lane >> 1) & 7;  // K fragment-read swizzle of row (lane & 31)
@@ -174,7 +182,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     // Tile it has landed (this wavefront's copies: only tile it + 1 may still be in flight),
     // and every wavefront is done with tile it - 1, whose stage is `ahead`.
     if (it + 1 < ntiles)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | 2);  // vmcnt(2)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * CPW));  // the copies of tile it + 1 may be in flight
     else
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
@@ -442,20 +450,31 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int ld_
                             hipStream_t st, const int* cu, int total) {
   if (batch == 0 || t == 0) return hipSuccess;
   const float c = scale * 1.4426950408889634f;  // fold log2(e): exp(x) = exp2(x * log2 e)
-  const long nblk16 = (long)((t + AQ - 1) / AQ) * heads * batch;
-  dim3 grid16((unsigned)nblk16), block16(512);
+  // Wavefronts per workgroup: 8 (256 query rows), halved while fewer than 64 workgroups would
+  // run.  Halving keeps the wavefront count and spreads it over more CUs, with less latency
+  // hidden on each: measured, it pays for 6 or 8 heads of one window (36 or 48 workgroups) and
+  // costs time at 12 or 20 heads (72, 120).
+  int nw = 8;
+  auto blocks = [&](int w) { return (long)((t + 32 * w - 1) / (32 * w)) * heads * batch; };
+  while (nw > 2 && blocks(nw) < 64) nw /= 2;
   dim3 grid((t + AQ32 - 1) / AQ32, heads, batch), block(256);
+  auto run16 = [&](auto tag) {
+    using T = decltype(tag);
+    const auto Qp = static_cast<const uint16_t*>(q);
+    const auto Kp = static_cast<const uint16_t*>(k);
+    const auto Vp = static_cast<const uint16_t*>(v);
+    auto Op = static_cast<uint16_t*>(o);
+    const dim3 g((unsigned)blocks(nw));
+    if (nw == 8)
+      attn16_kernel<T, 8><<<g, 512, 0, st>>>(Qp, Kp, Vp, ld_qkv, Op, ld_o, t, heads, c, cu, total);
+    else if (nw == 4)
+      attn16_kernel<T, 4><<<g, 256, 0, st>>>(Qp, Kp, Vp, ld_qkv, Op, ld_o, t, heads, c, cu, total);
+    else
+      attn16_kernel<T, 2><<<g, 128, 0, st>>>(Qp, Kp, Vp, ld_qkv, Op, ld_o, t, heads, c, cu, total);
+  };
   switch (dtype) {
-    case DT_BF16:
-      attn16_kernel<bf16_t><<<grid16, block16, 0, st>>>(
-          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-          static_cast<const uint16_t*>(v), ld_qkv, static_cast<uint16_t*>(o), ld_o, t, heads, c, cu, total);
-      break;
-    case DT_F16:
-      attn16_kernel<f16_t><<<grid16, block16, 0, st>>>(
-          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-          static_cast<const uint16_t*>(v), ld_qkv, static_cast<uint16_t*>(o), ld_o, t, heads, c, cu, total);
-      break;
+    case DT_BF16: run16(bf16_t{}); break;
+    case DT_F16: run16(f16_t{}); break;
     case DT_F32:
       attn32_kernel<<<grid, block, 0, st>>>(static_cast<const float*>(q),
                                             static_cast<const float*>(k),

@@ -441,8 +441,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(windows shard by data parallelism with no exchange; see the design notes). "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(windows shard by data parallelism with no exchange between GPUs). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

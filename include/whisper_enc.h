@@ -121,8 +121,11 @@ int whisper_enc_pack_layer(const float* ln1_g, const float* ln1_b, const float* 
 /*
  * Workspace bytes a block/stack call needs for `batch` windows of `t` positions: the LN
  * output / attention output [batch*t, d] and the QKV / FFN hidden activations
- * [batch*t, max(3d, ffn)], in the path's operand type, and on the Q8 / Q4 paths room for one
- * layer's matrices expanded to fp16 (2 (4d^2 + 2 d ffn) bytes).  0 if the arguments are invalid.
+ * [batch*t, max(3d, ffn)], in the path's operand type; on the Q8 / Q4 paths room for one
+ * layer's matrices expanded to fp16 (2 (4d^2 + 2 d ffn) bytes); and, when batch*t is too small
+ * for the out-projection and fc2 to fill the GPU (one window), fp32 partial sums of those
+ * split-k products (up to 8 x batch*t x d floats, added in a fixed order: results stay
+ * deterministic).  The size depends only on the arguments.  0 if the arguments are invalid.
  */
 size_t whisper_enc_workspace_bytes(int batch, int t, int d_model, int heads, int ffn_dim,
                                    int path);

@@ -149,7 +149,10 @@ int whisper_enc_block_forward(const float* x, float* y, const void* layer, int b
  * model replaced it with Identity"; oxinfer encode, enc_ln).  layers: n_layers blobs packed
  * back to back, blob i at (char*)layers + i * whisper_enc_layer_bytes(...).  n_layers >= 0
  * (0 applies only the final LayerNorm, or copies x to y).  ln_post_b must be non-NULL when
- * ln_post_g is.  Other arguments as for whisper_enc_block_forward.
+ * ln_post_g is.  Other arguments as for whisper_enc_block_forward.  The result is bit-identical
+ * to one whisper_enc_block_forward call per layer followed by whisper_enc_layernorm (where the
+ * residual products split k, the LayerNorm that reads a block's output runs inside their final
+ * pass, with the same rounding).
  */
 int whisper_enc_stack_forward(const float* x, float* y, const void* layers, int n_layers,
                               const float* ln_post_g, const float* ln_post_b, int batch, int t,

@@ -160,8 +160,14 @@ Workspace carve(void* ws, size_t rows, int d, int f, int path) {
   } while (0)
 
 // Enqueue one block; all arguments already validated.  cu: ragged-batch offsets or nullptr.
+// ln1_ready: ws.a already holds LN1(x) (fused into the previous block's last pass).  next: the
+// LayerNorm that reads this block's output (the next block's LN1, or the stack's final norm);
+// when fc2 splits k it is fused into fc2's second pass and *next_done is set.  Where the
+// out-projection splits k, LN2 is fused into its second pass the same way.
 int run_block(const float* x, float* y, const char* blob, int rows, int t, int batch, int d,
-              int heads, int f, int path, const Workspace& ws, hipStream_t st, const int* cu) {
+              int heads, int f, int path, const Workspace& ws, hipStream_t st, const int* cu,
+              bool ln1_ready, const LnFuse* next, bool* next_done) {
+  *next_done = false;
   const LayerLayout L = layer_layout(d, f, path);
   const int dt = layer_dtype(path);
   const size_t es = elem_bytes(path);
@@ -187,18 +193,27 @@ int run_block(const float* x, float* y, const char* blob, int rows, int t, int b
     w2 = ws.w2;
   }
 
-  WENC_TRY(launch_layernorm(x, fp(L.ln1_g), fp(L.ln1_b), ws.a, rows, d, dt, st));
+  if (!ln1_ready)
+    WENC_TRY(launch_layernorm(x, fp(L.ln1_g), fp(L.ln1_b), ws.a, rows, d, dt, st));
   WENC_TRY(launch_linear(ws.a, d, wqkv, fp(L.bqkv), nullptr, qkv, 3 * d, rows, 3 * d, d, dt,
                          EPI_BIAS, st));
   WENC_TRY(launch_attention(qkv, qkv + es * d, qkv + es * 2 * d, 3 * d, ws.a, d, batch, t, heads,
                             0.125f, dt, st, cu, rows));
-  WENC_TRY(launch_linear(ws.a, d, wo, fp(L.bo), x, y, d, rows, d, d, dt, EPI_BIAS_RESIDUAL, st,
-                         ws.part));
-  WENC_TRY(launch_layernorm(y, fp(L.ln2_g), fp(L.ln2_b), ws.a, rows, d, dt, st));
+  if (ws.part && linear_split(rows, d, d, dt, EPI_BIAS_RESIDUAL) > 1) {
+    const LnFuse ln2{fp(L.ln2_g), fp(L.ln2_b), ws.a, dt, true};
+    WENC_TRY(launch_linear(ws.a, d, wo, fp(L.bo), x, y, d, rows, d, d, dt, EPI_BIAS_RESIDUAL, st,
+                           ws.part, &ln2));
+  } else {
+    WENC_TRY(launch_linear(ws.a, d, wo, fp(L.bo), x, y, d, rows, d, d, dt, EPI_BIAS_RESIDUAL, st,
+                           ws.part));
+    WENC_TRY(launch_layernorm(y, fp(L.ln2_g), fp(L.ln2_b), ws.a, rows, d, dt, st));
+  }
   WENC_TRY(launch_linear(ws.a, d, w1, fp(L.b1), nullptr, ws.b, f, rows, f, d, dt, EPI_BIAS_GELU,
                          st));
+  const bool fuse_next = next && ws.part && linear_split(rows, d, f, dt, EPI_BIAS_RESIDUAL) > 1;
   WENC_TRY(launch_linear(ws.b, f, w2, fp(L.b2), y, y, d, rows, d, f, dt, EPI_BIAS_RESIDUAL, st,
-                         ws.part));
+                         ws.part, fuse_next ? next : nullptr));
+  *next_done = fuse_next;
   return WENC_OK;
 }
 
@@ -313,15 +328,32 @@ int stack_impl(const float* x, float* y, const void* layers, int n_layers, const
   const size_t lb = layer_layout(d_model, ffn_dim, path).total;
   const Workspace ws = carve(workspace, rows, d_model, ffn_dim, path);
   const float* src = x;
+  const LayerLayout L = layer_layout(d_model, ffn_dim, path);
+  const int dt = layer_dtype(path);
+  bool ln1_ready = false, post_done = false;
   for (int l = 0; l < n_layers; ++l) {
-    rc = run_block(src, y, static_cast<const char*>(layers) + (size_t)l * lb, (int)rows, t, batch,
-                   d_model, heads, ffn_dim, path, ws, st, cu);
+    // The LayerNorm that reads this block's output: the next block's LN1 (into the workspace's
+    // operand buffer) or the final norm (into y, the block output itself not kept).
+    const char* blob = static_cast<const char*>(layers) + (size_t)l * lb;
+    LnFuse next{nullptr, nullptr, nullptr, 0, true};
+    if (l + 1 < n_layers) {
+      const char* nb = blob + lb;
+      next = {reinterpret_cast<const float*>(nb + L.ln1_g),
+              reinterpret_cast<const float*>(nb + L.ln1_b), ws.a, dt, true};
+    } else if (ln_post_g) {
+      next = {ln_post_g, ln_post_b, y, DT_F32, false};
+    }
+    bool done = false;
+    rc = run_block(src, y, blob, (int)rows, t, batch, d_model, heads, ffn_dim, path, ws, st, cu,
+                   ln1_ready, next.gamma ? &next : nullptr, &done);
     if (rc != WENC_OK) return rc;
+    ln1_ready = done && l + 1 < n_layers;
+    post_done = done && l + 1 == n_layers;
     src = y;
   }
-  if (ln_post_g) {
+  if (ln_post_g && !post_done) {
     WENC_TRY(launch_layernorm(src, ln_post_g, ln_post_b, y, (int)rows, d_model, DT_F32, st));
-  } else if (src != y) {
+  } else if (!ln_post_g && src != y) {
     WENC_TRY(hipMemcpyAsync(y, src, xbytes, hipMemcpyDeviceToDevice, st));
   }
   return WENC_OK;

@@ -662,27 +662,29 @@ __global__ __launch_bounds__(256) void gemm32_kernel(const float* __restrict__ X
 }
 
 // Second pass of a split-k residual GEMM: c = residual + epi(sum of the parts + bias), the parts
-// added in order (deterministic), four columns per thread.
+// added in order (deterministic).  A workgroup per row (grid-stride over rows), four columns per
+// thread.  (When a LayerNorm reads the result, launch_splitk_reduce_ln does this pass instead.)
 template <bool GELU>
 __global__ void splitk_reduce_kernel(const float* __restrict__ part, int ksplit,
                                      const float* __restrict__ bias, const float* residual,
                                      float* c, int ldc, int M, int N) {
-  const size_t total = (size_t)M * (N / 4);
   const size_t plane = (size_t)M * N;
-  for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total;
-       e += (size_t)gridDim.x * blockDim.x) {
-    const int m = (int)(e / (N / 4)), n = (int)(e % (N / 4)) * 4;
-    float4 s = *reinterpret_cast<const float4*>(part + (size_t)m * N + n);
-    for (int p = 1; p < ksplit; ++p) {
-      const float4 q = *reinterpret_cast<const float4*>(part + p * plane + (size_t)m * N + n);
-      s = make_float4(s.x + q.x, s.y + q.y, s.z + q.z, s.w + q.w);
+  for (int m = blockIdx.x; m < M; m += gridDim.x) {
+    for (int n = 4 * threadIdx.x; n < N; n += 4 * blockDim.x) {
+      const size_t e = (size_t)m * N + n;
+      float4 s = *reinterpret_cast<const float4*>(part + e);
+      for (int p = 1; p < ksplit; ++p) {
+        const float4 q = *reinterpret_cast<const float4*>(part + p * plane + e);
+        s = make_float4(s.x + q.x, s.y + q.y, s.z + q.z, s.w + q.w);
+      }
+      const float4 b = *reinterpret_cast<const float4*>(bias + n);
+      float4 v = make_float4(s.x + b.x, s.y + b.y, s.z + b.z, s.w + b.w);
+      if constexpr (GELU)
+        v = make_float4(gelu_erf_as(v.x), gelu_erf_as(v.y), gelu_erf_as(v.z), gelu_erf_as(v.w));
+      const float4 r = *reinterpret_cast<const float4*>(residual + (size_t)m * ldc + n);
+      *reinterpret_cast<float4*>(c + (size_t)m * ldc + n) =
+          make_float4(r.x + v.x, r.y + v.y, r.z + v.z, r.w + v.w);
     }
-    const float4 b = *reinterpret_cast<const float4*>(bias + n);
-    float4 v = make_float4(s.x + b.x, s.y + b.y, s.z + b.z, s.w + b.w);
-    if constexpr (GELU) v = make_float4(gelu_erf_as(v.x), gelu_erf_as(v.y), gelu_erf_as(v.z), gelu_erf_as(v.w));
-    const float4 r = *reinterpret_cast<const float4*>(residual + (size_t)m * ldc + n);
-    *reinterpret_cast<float4*>(c + (size_t)m * ldc + n) =
-        make_float4(r.x + v.x, r.y + v.y, r.z + v.z, r.w + v.w);
   }
 }
 
@@ -711,22 +713,26 @@ static int persistent_grid() {
 }
 
 template <typename T, int EPI>
-static void launch16_epi(const uint16_t* X, int lda, const uint16_t* W, const float* bias,
-                         const float* residual, void* c, int ldc, int m, int n, int k,
-                         hipStream_t st, float* partial) {
+static hipError_t launch16_epi(const uint16_t* X, int lda, const uint16_t* W, const float* bias,
+                               const float* residual, void* c, int ldc, int m, int n, int k,
+                               hipStream_t st, float* partial, const LnFuse* ln) {
   const long tiles = (long)((m + G_M - 1) / G_M) * ((n + G_N - 1) / G_N);
   const long small = (long)((m + H_M - 1) / H_M) * ((n + H_N - 1) / H_N);
   const int split = partial ? linear_split(m, n, k, DT_F16, EPI) : 1;
+  if (ln && (EPI != EPI_BIAS_RESIDUAL || split < 2 || ldc != n)) return hipErrorInvalidValue;
   if constexpr (EPI == EPI_BIAS_RESIDUAL || EPI == EPI_BIAS_GELU_RESIDUAL) {
     if (split > 1) {
       gemm16_small_kernel<T, EPI_PARTIAL><<<dim3((unsigned)(small * split)), dim3(H_THREADS), 0,
                                             st>>>(X, lda, W, bias, nullptr, partial, n, m, n, k,
                                                   split);
-      const size_t total = (size_t)m * (n / 4);
-      const unsigned g = (unsigned)std::min<size_t>((total + 255) / 256, 16384);
+      if (ln)
+        return launch_splitk_reduce_ln(partial, split, bias, residual,
+                                       ln->keep_x ? static_cast<float*>(c) : nullptr, ln->gamma,
+                                       ln->beta, ln->y, ln->y_dtype, m, n, st);
+      const unsigned g = (unsigned)std::min(m, 16384);
       splitk_reduce_kernel<EPI == EPI_BIAS_GELU_RESIDUAL><<<g, 256, 0, st>>>(
           partial, split, bias, residual, static_cast<float*>(c), ldc, m, n);
-      return;
+      return hipGetLastError();
     }
   }
   const int grid = persistent_grid();
@@ -737,31 +743,32 @@ static void launch16_epi(const uint16_t* X, int lda, const uint16_t* W, const fl
     gemm16_small_kernel<T, EPI><<<dim3((unsigned)small), dim3(H_THREADS), 0, st>>>(
         X, lda, W, bias, residual, c, ldc, m, n, k, 1);
   }
+  return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch16(const void* a, int lda, const void* w, const float* bias,
                            const float* residual, void* c, int ldc, int m, int n, int k, int epi,
-                           hipStream_t st, float* partial) {
+                           hipStream_t st, float* partial, const LnFuse* ln) {
   auto X = static_cast<const uint16_t*>(a);
   auto W = static_cast<const uint16_t*>(w);
   switch (epi) {
-    case EPI_BIAS: launch16_epi<T, EPI_BIAS>(X, lda, W, bias, residual, c, ldc, m, n, k, st, partial); break;
+    case EPI_BIAS:
+      return launch16_epi<T, EPI_BIAS>(X, lda, W, bias, residual, c, ldc, m, n, k, st, partial, ln);
     case EPI_BIAS_GELU:
-      launch16_epi<T, EPI_BIAS_GELU>(X, lda, W, bias, residual, c, ldc, m, n, k, st, partial);
-      break;
+      return launch16_epi<T, EPI_BIAS_GELU>(X, lda, W, bias, residual, c, ldc, m, n, k, st,
+                                            partial, ln);
     case EPI_BIAS_RESIDUAL:
-      launch16_epi<T, EPI_BIAS_RESIDUAL>(X, lda, W, bias, residual, c, ldc, m, n, k, st, partial);
-      break;
+      return launch16_epi<T, EPI_BIAS_RESIDUAL>(X, lda, W, bias, residual, c, ldc, m, n, k, st,
+                                                partial, ln);
     case EPI_BIAS_HEADMAJOR:
-      launch16_epi<T, EPI_BIAS_HEADMAJOR>(X, lda, W, bias, residual, c, ldc, m, n, k, st, partial);
-      break;
+      return launch16_epi<T, EPI_BIAS_HEADMAJOR>(X, lda, W, bias, residual, c, ldc, m, n, k, st,
+                                                 partial, ln);
     case EPI_BIAS_GELU_RESIDUAL:
-      launch16_epi<T, EPI_BIAS_GELU_RESIDUAL>(X, lda, W, bias, residual, c, ldc, m, n, k, st, partial);
-      break;
-    default: return hipErrorInvalidValue;
+      return launch16_epi<T, EPI_BIAS_GELU_RESIDUAL>(X, lda, W, bias, residual, c, ldc, m, n, k,
+                                                     st, partial, ln);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 static hipError_t launch32(const void* a, int lda, const void* w, const float* bias,
@@ -797,14 +804,18 @@ static hipError_t launch32(const void* a, int lda, const void* w, const float* b
 
 hipError_t launch_linear(const void* a, int lda, const void* w, const float* bias,
                          const float* residual, void* c, int ldc, int m, int n, int k, int dtype,
-                         int epilogue, hipStream_t st, float* partial) {
+                         int epilogue, hipStream_t st, float* partial, const LnFuse* ln) {
   if (m == 0) return hipSuccess;
   switch (dtype) {
     case DT_BF16:
-      return launch16<bf16_t>(a, lda, w, bias, residual, c, ldc, m, n, k, epilogue, st, partial);
+      return launch16<bf16_t>(a, lda, w, bias, residual, c, ldc, m, n, k, epilogue, st, partial,
+                              ln);
     case DT_F16:
-      return launch16<f16_t>(a, lda, w, bias, residual, c, ldc, m, n, k, epilogue, st, partial);
-    case DT_F32: return launch32(a, lda, w, bias, residual, c, ldc, m, n, k, epilogue, st);
+      return launch16<f16_t>(a, lda, w, bias, residual, c, ldc, m, n, k, epilogue, st, partial,
+                             ln);
+    case DT_F32:
+      if (ln) return hipErrorInvalidValue;
+      return launch32(a, lda, w, bias, residual, c, ldc, m, n, k, epilogue, st);
   }
   return hipErrorInvalidValue;
 }

@@ -39,27 +39,18 @@ struct LnStore<NV, f16_t> {
   }
 };
 
-// NV = float4 vectors per lane (d <= 256 * NV).
+// Normalises one row held in a wavefront's registers (lane l has columns 4 (l + 64 j) .. + 3 in
+// v[j]; entries past d are ignored) and stores it as OutT.  Both the plain LayerNorm and the fused
+// split-k reduction below end in this routine, so they round identically.
 template <int NV, typename OutT>
-__global__ __launch_bounds__(256) void layernorm_rows(const float* __restrict__ x,
-                                                      const float* __restrict__ gamma,
-                                                      const float* __restrict__ beta,
-                                                      void* y, int rows, int d, float eps) {
-  const int lane = threadIdx.x & 63;
-  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= (size_t)rows) return;
-  const float* xr = x + row * d;
-  float4 v[NV];
+__device__ __forceinline__ void ln_row(float4 (&v)[NV], int lane, const float* __restrict__ gamma,
+                                       const float* __restrict__ beta, void* y, size_t row, int d,
+                                       float eps) {
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int c = (lane + 64 * j) * 4;
-    if (c < d) {
-      v[j] = *reinterpret_cast<const float4*>(xr + c);
-      s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
-    } else {
-      v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    if (c < d) s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
   }
   const float inv_d = 1.0f / (float)d;
   const float mean = wave_sum(s) * inv_d;
@@ -90,6 +81,67 @@ __global__ __launch_bounds__(256) void layernorm_rows(const float* __restrict__ 
   }
 }
 
+// NV = float4 vectors per lane (d <= 256 * NV).
+template <int NV, typename OutT>
+__global__ __launch_bounds__(256) void layernorm_rows(const float* __restrict__ x,
+                                                      const float* __restrict__ gamma,
+                                                      const float* __restrict__ beta,
+                                                      void* y, int rows, int d, float eps) {
+  const int lane = threadIdx.x & 63;
+  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (size_t)rows) return;
+  const float* xr = x + row * d;
+  float4 v[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int c = (lane + 64 * j) * 4;
+    v[j] = c < d ? *reinterpret_cast<const float4*>(xr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  ln_row<NV, OutT>(v, lane, gamma, beta, y, row, d, eps);
+}
+
+// Second pass of a split-k residual GEMM fused with the LayerNorm that reads its output: per row,
+// x = residual + (sum of the k parts, added in order, + bias) -- the same sums as the plain
+// reduction kernel -- stored to x_out when given, then y = LayerNorm(x) * gamma + beta.  One
+// wavefront per row reads the whole row before it writes, so x_out and y may alias residual.
+template <int NV, typename OutT>
+__global__ __launch_bounds__(256) void splitk_reduce_ln_rows(
+    const float* __restrict__ part, int ksplit, const float* __restrict__ bias,
+    const float* residual, float* x_out, const float* __restrict__ gamma,
+    const float* __restrict__ beta, void* y, int rows, int d, float eps) {
+  const int lane = threadIdx.x & 63;
+  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (size_t)rows) return;
+  const size_t plane = (size_t)rows * d;
+  float4 v[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int c = (lane + 64 * j) * 4;
+    if (c < d) {
+      const size_t e = row * d + c;
+      float4 s = *reinterpret_cast<const float4*>(part + e);
+      for (int p = 1; p < ksplit; ++p) {
+        const float4 q = *reinterpret_cast<const float4*>(part + p * plane + e);
+        s = make_float4(s.x + q.x, s.y + q.y, s.z + q.z, s.w + q.w);
+      }
+      const float4 b = *reinterpret_cast<const float4*>(bias + c);
+      const float4 u = make_float4(s.x + b.x, s.y + b.y, s.z + b.z, s.w + b.w);
+      const float4 r = *reinterpret_cast<const float4*>(residual + e);
+      v[j] = make_float4(r.x + u.x, r.y + u.y, r.z + u.z, r.w + u.w);
+    } else {
+      v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  if (x_out) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int c = (lane + 64 * j) * 4;
+      if (c < d) *reinterpret_cast<float4*>(x_out + row * d + c) = v[j];
+    }
+  }
+  ln_row<NV, OutT>(v, lane, gamma, beta, y, row, d, eps);
+}
+
 template <typename OutT>
 static hipError_t launch_ln_t(const float* x, const float* g, const float* b, void* y, int rows,
                               int d, hipStream_t st) {
@@ -107,6 +159,48 @@ static hipError_t launch_ln_t(const float* x, const float* g, const float* b, vo
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <typename OutT>
+static hipError_t launch_reduce_ln_t(const float* part, int ksplit, const float* bias,
+                                     const float* residual, float* x_out, const float* g,
+                                     const float* b, void* y, int rows, int d, hipStream_t st) {
+  dim3 grid((rows + 3) / 4), block(256);
+  const float eps = 1e-5f;
+  const int nv = (d + 255) / 256;
+  switch (nv) {
+#define WENC_RLN_CASE(N)                                                                       \
+  case N:                                                                                      \
+    splitk_reduce_ln_rows<N, OutT><<<grid, block, 0, st>>>(part, ksplit, bias, residual, x_out, \
+                                                           g, b, y, rows, d, eps);             \
+    break;
+    WENC_RLN_CASE(1) WENC_RLN_CASE(2) WENC_RLN_CASE(3) WENC_RLN_CASE(4) WENC_RLN_CASE(5)
+    WENC_RLN_CASE(6) WENC_RLN_CASE(7) WENC_RLN_CASE(8) WENC_RLN_CASE(9) WENC_RLN_CASE(10)
+    WENC_RLN_CASE(11) WENC_RLN_CASE(12) WENC_RLN_CASE(13) WENC_RLN_CASE(14) WENC_RLN_CASE(15)
+    WENC_RLN_CASE(16)
+#undef WENC_RLN_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce_ln(const float* part, int ksplit, const float* bias,
+                                   const float* residual, float* x_out, const float* gamma,
+                                   const float* beta, void* y, int y_dtype, int rows, int d,
+                                   hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  switch (y_dtype) {
+    case DT_F32:
+      return launch_reduce_ln_t<float>(part, ksplit, bias, residual, x_out, gamma, beta, y, rows,
+                                       d, st);
+    case DT_BF16:
+      return launch_reduce_ln_t<bf16_t>(part, ksplit, bias, residual, x_out, gamma, beta, y,
+                                        rows, d, st);
+    case DT_F16:
+      return launch_reduce_ln_t<f16_t>(part, ksplit, bias, residual, x_out, gamma, beta, y, rows,
+                                       d, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, void* y, int rows,

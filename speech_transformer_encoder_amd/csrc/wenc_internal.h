@@ -22,6 +22,24 @@ enum Epilogue {
 hipError_t launch_layernorm(const float* x, const float* gamma, const float* beta, void* y,
                             int rows, int d, int out_dtype, hipStream_t st);
 
+// Second pass of a split-k residual GEMM with the LayerNorm that follows it: per row of [rows, d],
+// x = residual + (part[0] + ... + part[ksplit - 1] + bias) (parts of rows * d floats, added in
+// order), stored to x_out unless it is null, and y = LayerNorm(x) * gamma + beta as y_dtype.
+// Rounds exactly as the plain reduction followed by launch_layernorm.  x_out / y may alias residual.
+hipError_t launch_splitk_reduce_ln(const float* part, int ksplit, const float* bias,
+                                   const float* residual, float* x_out, const float* gamma,
+                                   const float* beta, void* y, int y_dtype, int rows, int d,
+                                   hipStream_t st);
+
+// A LayerNorm to fuse into the second pass of a split-k residual GEMM (launch_linear).
+struct LnFuse {
+  const float* gamma;
+  const float* beta;
+  void* y;       // [m, n] in y_dtype
+  int y_dtype;
+  bool keep_x;   // also store the GEMM's own output c
+};
+
 // c[m, n] = epilogue(a[m, k] . w[n, k]^T + bias[n]) with 16-bit (dtype) or fp32 operands.
 //   EPI_BIAS          -> c in the operand dtype (fp32 for DT_F32)
 //   EPI_BIAS_GELU     -> c = gelu_erf(.) in the operand dtype
@@ -34,9 +52,12 @@ hipError_t launch_layernorm(const float* x, const float* gamma, const float* bet
 // partial: optional fp32 scratch of linear_split(m, n, k, dtype, epilogue) * m * n floats; given,
 // a residual GEMM too small to fill the GPU splits k over that many workgroups and a second
 // kernel adds the parts in a fixed order (deterministic), then bias and residual.
+// ln: with a split EPI_BIAS_RESIDUAL GEMM (ldc == n), the second kernel also applies this
+// LayerNorm to the rows it forms (launch_splitk_reduce_ln); anything else with ln is an error.
 hipError_t launch_linear(const void* a, int lda, const void* w, const float* bias,
                          const float* residual, void* c, int ldc, int m, int n, int k, int dtype,
-                         int epilogue, hipStream_t st, float* partial = nullptr);
+                         int epilogue, hipStream_t st, float* partial = nullptr,
+                         const LnFuse* ln = nullptr);
 // Number of k parts launch_linear uses with a partial buffer (1: none).  Fixed for a shape,
 // whatever the device, so that workspace sizes are too.
 int linear_split(int m, int n, int k, int dtype, int epilogue);

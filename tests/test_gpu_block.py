@@ -116,6 +116,32 @@ def test_windows_are_independent():
     np.testing.assert_array_equal(full[2:3], alone)
 
 
+@pytest.mark.parametrize("path", [B.WENC_PATH_BF16, B.WENC_PATH_FP16, B.WENC_PATH_Q8])
+def test_stack_equals_chained_blocks(path):
+    """A stack call is bit-identical to one block call per layer followed by the final LayerNorm.
+
+    At one 1500-position window the residual GEMMs split k, and the stack call folds each
+    following LayerNorm (the next block's LN1, then the final norm) into fc2's reduction pass;
+    the chained calls run those norms as separate LayerNorm launches.  Both must round alike."""
+    import torch
+    cfg = synth.CONFIGS["base_stack"].with_(n_layers=3)
+    w = synth.make_workload(cfg)
+    enc = build_from_workload(w, path)
+    x = to_device_input(w.x)
+    print(f"[case] stack vs chained blocks path={path}", flush=True)
+    stacked = host(enc.forward(x))
+    batch, t, d = x.shape
+    ws = enc.workspace(batch, t)
+    cur, nxt = x.clone(), torch.empty_like(x)
+    for l in range(cfg.n_layers):
+        B.whisper_enc_block_forward(cur, nxt, enc.blob.data_ptr() + l * enc.layer_bytes, batch, t,
+                                    d, cfg.heads, cfg.ffn_dim, path, ws, ws.numel())
+        cur, nxt = nxt, cur
+    g, b = enc.ln_post
+    B.whisper_enc_layernorm(cur, g, b, nxt, batch * t, d, B.WENC_DTYPE_F32)
+    np.testing.assert_array_equal(stacked, host(nxt))
+
+
 @pytest.mark.parametrize("path", [B.WENC_PATH_BF16, B.WENC_PATH_FP16])
 def test_pack_rounds_to_nearest_even(path):
     """Packing fp32 weights rounds them exactly as PyTorch's RNE conversion does: the block on

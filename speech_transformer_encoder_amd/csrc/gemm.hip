@@ -673,6 +673,7 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int ksplit,
     for (int n = 4 * threadIdx.x; n < N; n += 4 * blockDim.x) {
       const size_t e = (size_t)m * N + n;
       float4 s = *reinterpret_cast<const float4*>(part + e);
+#pragma unroll 4
       for (int p = 1; p < ksplit; ++p) {
         const float4 q = *reinterpret_cast<const float4*>(part + p * plane + e);
         s = make_float4(s.x + q.x, s.y + q.y, s.z + q.z, s.w + q.w);

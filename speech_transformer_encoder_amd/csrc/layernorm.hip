@@ -113,24 +113,34 @@ __global__ __launch_bounds__(256) void splitk_reduce_ln_rows(
   const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= (size_t)rows) return;
   const size_t plane = (size_t)rows * d;
-  float4 v[NV];
+  const float* pr = part + row * d;
+  // Parts outermost, the row's columns innermost, with no branches around the loads (columns
+  // past d read column d - 4 and are ignored by ln_row): each step keeps NV independent loads in
+  // flight, which a row owned by one wavefront needs to move enough bytes.  Per element the
+  // parts are still added in order 0, 1, ...
+  int cl[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) cl[j] = min((lane + 64 * j) * 4, d - 4);
+  float4 v[NV], r[NV], b[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int c = (lane + 64 * j) * 4;
-    if (c < d) {
-      const size_t e = row * d + c;
-      float4 s = *reinterpret_cast<const float4*>(part + e);
-      for (int p = 1; p < ksplit; ++p) {
-        const float4 q = *reinterpret_cast<const float4*>(part + p * plane + e);
-        s = make_float4(s.x + q.x, s.y + q.y, s.z + q.z, s.w + q.w);
-      }
-      const float4 b = *reinterpret_cast<const float4*>(bias + c);
-      const float4 u = make_float4(s.x + b.x, s.y + b.y, s.z + b.z, s.w + b.w);
-      const float4 r = *reinterpret_cast<const float4*>(residual + e);
-      v[j] = make_float4(r.x + u.x, r.y + u.y, r.z + u.z, r.w + u.w);
-    } else {
-      v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    r[j] = *reinterpret_cast<const float4*>(residual + row * d + cl[j]);
+    b[j] = *reinterpret_cast<const float4*>(bias + cl[j]);
+    v[j] = *reinterpret_cast<const float4*>(pr + cl[j]);
+  }
+#pragma unroll 4
+  for (int p = 1; p < ksplit; ++p) {
+    float4 q[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) q[j] = *reinterpret_cast<const float4*>(pr + p * plane + cl[j]);
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      v[j] = make_float4(v[j].x + q[j].x, v[j].y + q[j].y, v[j].z + q[j].z, v[j].w + q[j].w);
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const float4 u = make_float4(v[j].x + b[j].x, v[j].y + b[j].y, v[j].z + b[j].z, v[j].w + b[j].w);
+    v[j] = make_float4(r[j].x + u.x, r[j].y + u.y, r[j].z + u.z, r[j].w + u.w);
   }
   if (x_out) {
 #pragma unroll

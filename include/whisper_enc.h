@@ -125,7 +125,9 @@ int whisper_enc_pack_layer(const float* ln1_g, const float* ln1_b, const float* 
  * layer's matrices expanded to fp16 (2 (4d^2 + 2 d ffn) bytes); and, when batch*t is too small
  * for the out-projection and fc2 to fill the GPU (one window), fp32 partial sums of those
  * split-k products (up to 8 x batch*t x d floats, added in a fixed order: results stay
- * deterministic).  The size depends only on the arguments.  0 if the arguments are invalid.
+ * deterministic), a region that also holds the two key halves' partial attention state
+ * (2 x batch*t x heads x 66 floats) when too few query blocks would run to fill the GPU.
+ * The size depends only on the arguments.  0 if the arguments are invalid.
  */
 size_t whisper_enc_workspace_bytes(int batch, int t, int d_model, int heads, int ffn_dim,
                                    int path);

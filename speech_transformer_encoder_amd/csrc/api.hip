@@ -124,14 +124,26 @@ size_t split_bytes(size_t rows, int d, int f, int path) {
   return s > 1 ? round_up((size_t)s * rows * d * sizeof(float)) : 0;
 }
 
-size_t workspace_size(size_t rows, int d, int f, int path) {
+// fp32 (O, m, l) of both key halves when attention splits its keys (few query blocks).
+size_t attn_split_bytes(int batch, int t, int heads, size_t rows, int path) {
+  if (attention_split(batch, t, heads, layer_dtype(path)) < 2) return 0;
+  return round_up(2 * rows * (size_t)heads * 66 * sizeof(float));
+}
+
+// One scratch region serves both: attention's halves are merged before the out-projection runs.
+size_t scratch_bytes(int batch, int t, int heads, size_t rows, int d, int f, int path) {
+  return std::max(split_bytes(rows, d, f, path), attn_split_bytes(batch, t, heads, rows, path));
+}
+
+// rows: batch * t, or the packed rows of a ragged batch (t = its longest window).
+size_t workspace_size(int batch, int t, int heads, size_t rows, int d, int f, int path) {
   const size_t es = elem_bytes(path);
   const size_t wb = (size_t)(3 * d > f ? 3 * d : f);
   return round_up(rows * d * es) + round_up(rows * wb * es) + dequant_bytes(d, f, path) +
-         split_bytes(rows, d, f, path);
+         scratch_bytes(batch, t, heads, rows, d, f, path);
 }
 
-Workspace carve(void* ws, size_t rows, int d, int f, int path) {
+Workspace carve(void* ws, int batch, int t, int heads, size_t rows, int d, int f, int path) {
   Workspace w;
   const size_t es = elem_bytes(path);
   const size_t wb = (size_t)(3 * d > f ? 3 * d : f);
@@ -148,7 +160,7 @@ Workspace carve(void* ws, size_t rows, int d, int f, int path) {
     q += round_up(2 * (size_t)f * d);
     w.w2 = reinterpret_cast<uint16_t*>(q);
   }
-  if (split_bytes(rows, d, f, path))
+  if (scratch_bytes(batch, t, heads, rows, d, f, path))
     w.part = reinterpret_cast<float*>(p + round_up(rows * d * es) + round_up(rows * wb * es) +
                                       dequant_bytes(d, f, path));
   return w;
@@ -198,7 +210,7 @@ int run_block(const float* x, float* y, const char* blob, int rows, int t, int b
   WENC_TRY(launch_linear(ws.a, d, wqkv, fp(L.bqkv), nullptr, qkv, 3 * d, rows, 3 * d, d, dt,
                          EPI_BIAS, st));
   WENC_TRY(launch_attention(qkv, qkv + es * d, qkv + es * 2 * d, 3 * d, ws.a, d, batch, t, heads,
-                            0.125f, dt, st, cu, rows));
+                            0.125f, dt, st, cu, rows, ws.part));
   if (ws.part && linear_split(rows, d, d, dt, EPI_BIAS_RESIDUAL) > 1) {
     const LnFuse ln2{fp(L.ln2_g), fp(L.ln2_b), ws.a, dt, true};
     WENC_TRY(launch_linear(ws.a, d, wo, fp(L.bo), x, y, d, rows, d, d, dt, EPI_BIAS_RESIDUAL, st,
@@ -297,7 +309,7 @@ int whisper_enc_pack_layer(const float* ln1_g, const float* ln1_b, const float* 
 size_t whisper_enc_workspace_bytes(int batch, int t, int d_model, int heads, int ffn_dim,
                                    int path) {
   if (check_shape(batch, t, d_model, heads, ffn_dim, path) != WENC_OK) return 0;
-  return workspace_size((size_t)batch * t, d_model, ffn_dim, path);
+  return workspace_size(batch, t, heads, (size_t)batch * t, d_model, ffn_dim, path);
 }
 
 }  // extern "C"
@@ -321,12 +333,13 @@ int stack_impl(const float* x, float* y, const void* layers, int n_layers, const
   if (n_layers > 0) {
     if (!layers || !aligned(layers, kAlign)) return WENC_ERR_ARG;
     if (!workspace || !aligned(workspace, kAlign)) return WENC_ERR_ARG;
-    if (workspace_bytes < workspace_size(rows, d_model, ffn_dim, path)) return WENC_ERR_WORKSPACE;
+    if (workspace_bytes < workspace_size(batch, t, heads, rows, d_model, ffn_dim, path))
+      return WENC_ERR_WORKSPACE;
   }
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const size_t lb = layer_layout(d_model, ffn_dim, path).total;
-  const Workspace ws = carve(workspace, rows, d_model, ffn_dim, path);
+  const Workspace ws = carve(workspace, batch, t, heads, rows, d_model, ffn_dim, path);
   const float* src = x;
   const LayerLayout L = layer_layout(d_model, ffn_dim, path);
   const int dt = layer_dtype(path);
@@ -385,7 +398,7 @@ int whisper_enc_stack_forward(const float* x, float* y, const void* layers, int 
 size_t whisper_enc_varlen_workspace_bytes(int batch, int total_rows, int max_t, int d_model,
                                           int heads, int ffn_dim, int path) {
   if (check_varlen(batch, total_rows, max_t, d_model, heads, ffn_dim, path) != WENC_OK) return 0;
-  return workspace_size((size_t)total_rows, d_model, ffn_dim, path);
+  return workspace_size(batch, max_t, heads, (size_t)total_rows, d_model, ffn_dim, path);
 }
 
 int whisper_enc_stack_forward_varlen(const float* x, float* y, const void* layers, int n_layers,

@@ -79,13 +79,18 @@ template <> struct RowSum<bf16_t> {
   }
 };
 
+// kvs = 1: O = softmax(.) V, normalised, in T.  kvs = 2 (too few query blocks to fill the GPU):
+// each query block's keys are split in two halves handled by two workgroups, which write the
+// unnormalised partial O (fp32) and their (m, l) to `part`; attn_merge_kernel combines them.
+// total: rows of the packed batch (batch * tmax for equal windows).
 template <typename T, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4))) void attn16_kernel(const uint16_t* __restrict__ Q,
                                                         const uint16_t* __restrict__ Kp,
                                                         const uint16_t* __restrict__ Vp, int ld,
                                                         uint16_t* __restrict__ O, int ldo, int tmax,
                                                         int heads, float c,
-                                                        const int* __restrict__ cu, int total) {
+                                                        const int* __restrict__ cu, int total,
+                                                        int kvs, float* __restrict__ part) {
   __shared__ __attribute__((aligned(1024))) uint16_t st0[2 * ATILE];
   __shared__ __attribute__((aligned(1024))) uint16_t st1[2 * ATILE];
   __shared__ __attribute__((aligned(1024))) uint16_t st2[2 * ATILE];
@@ -100,7 +105,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
   constexpr int AQ = 32 * NW;  // query rows of the workgroup
   constexpr int CPW = 8 / NW;   // 8-row blocks of each K and V tile a wavefront copies
   const int nqb = (tmax + AQ - 1) / AQ;
-  const int v = xcd_virtual_id(blockIdx.x, gridDim.x);
+  const int vk = xcd_virtual_id(blockIdx.x, gridDim.x);
+  const int half = vk % kvs, v = vk / kvs;  // the two halves of a query block are neighbours
   const int qb = v % nqb;
   const int h = (v / nqb) % heads;
   const int wi = v / (nqb * heads);
@@ -137,6 +143,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
   // With NW < 8 wavefront w also copies rows 8 (w + NW i) .. + 7, i < CPW: a shift by a multiple
   // of 16 rows leaves both swizzles unchanged.
   const uint32_t blk = (uint32_t)wave * 1024u;
+  // This workgroup's key tiles: all of the window's, or one half of them (kvs = 2).
+  const int ntile_all = (t + AK - 1) / AK;
+  const int per = (ntile_all + kvs - 1) / kvs;
+  const int kt0 = min(ntile_all, half * per);
+  const int ntiles = min(ntile_all, kt0 + per) - kt0;
+  const int kbase = kt0 * AK;  // first key
   auto load_tile = [&](int j0, const uint16_t* st) {
     const uint32_t base = lds_addr(st) + blk;
 #pragma unroll
@@ -172,13 +184,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
   float m_run = -INFINITY;  // max used in the exponents (scaled units), per query
   float l_part = 0.f;       // this lane's share of the running denominator
 
-  const int ntiles = (t + AK - 1) / AK;
-  load_tile(0, st0);
-  if (ntiles > 1) load_tile(AK, st1);
+  if (ntiles > 0) load_tile(kbase, st0);
+  if (ntiles > 1) load_tile(kbase + AK, st1);
 
   // One key tile from stage `cur`; the tile two ahead is loaded into stage `ahead`.
   auto tile = [&](int it, const uint16_t* cur, const uint16_t* ahead) {
-    const int j0 = it * AK;
+    const int j0 = kbase + it * AK;
     // Tile it has landed (this wavefront's copies: only tile it + 1 may still be in flight),
     // and every wavefront is done with tile it - 1, whose stage is `ahead`.
     if (it + 1 < ntiles)
@@ -276,6 +287,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
   if (it < ntiles) tile(it, st0, st2);
   if (it + 1 < ntiles) tile(it + 1, st1, st0);
 
+  if (kvs > 1) {
+    // Partial state of this half: unnormalised O (fp32) [half][row][head][64], then (m, l)
+    // [half][row][head][2], rows numbered as in the packed batch.
+    const float l_all = halves_sum(l_part);
+    if (qi < t) {
+      const size_t slot = ((size_t)half * total + win + qi) * heads + h;
+      float* po = part + slot * 64;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int dim = db * 32 + j * 8 + g * 4;
+          *reinterpret_cast<float4*>(po + dim) = make_float4(oacc[db][4 * j], oacc[db][4 * j + 1],
+                                                            oacc[db][4 * j + 2], oacc[db][4 * j + 3]);
+        }
+      if (g == 0) {
+        float* pml = part + (size_t)kvs * total * heads * 64 + slot * 2;
+        *reinterpret_cast<float2*>(pml) = make_float2(m_run, l_all);
+      }
+    }
+    return;
+  }
   const float inv = 1.0f / halves_sum(l_part);
   if (qi < t) {
     uint16_t* orow = O + (win + qi) * ldo + col0;
@@ -445,17 +478,58 @@ __global__ __launch_bounds__(256) void attn32_kernel(const float* __restrict__ Q
   }
 }
 
+// Combines the two key halves of a split attention: per (row, head), with a_h = exp2(m_h - m),
+// m = max(m_0, m_1), O = (a_0 O_0 + a_1 O_1) / (a_0 l_0 + a_1 l_1), which is the softmax over
+// all keys (the same recurrence the online form runs tile by tile, applied once more).  One
+// 64-lane wavefront per (window, head, 4 rows): 16 lanes per row, 4 dims each.  Windows whose
+// offsets are invalid are skipped, as in the attention kernel.
+template <typename T>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part,
+                                                         uint16_t* __restrict__ O, int ldo,
+                                                         int tmax, int heads,
+                                                         const int* __restrict__ cu, int total) {
+  const int wi = blockIdx.z, h = blockIdx.y;
+  const int i = (blockIdx.x * 256 + threadIdx.x) >> 4;  // row within the window
+  const int dim = (threadIdx.x & 15) * 4;
+  size_t win;
+  int t;
+  if (!window_rows(cu, total, wi, tmax, blockIdx.x * 16, win, t) || i >= t) return;
+  const size_t s0 = (win + i) * heads + h, s1 = ((size_t)total + win + i) * heads + h;
+  const float* ml = part + (size_t)2 * total * heads * 64;
+  const float2 a = *reinterpret_cast<const float2*>(ml + s0 * 2);
+  const float2 b = *reinterpret_cast<const float2*>(ml + s1 * 2);
+  const float m = fmaxf(a.x, b.x);
+  const float ca = fast_exp2(a.x - m), cb = fast_exp2(b.x - m);
+  const float inv = 1.0f / (ca * a.y + cb * b.y);
+  const float4 oa = *reinterpret_cast<const float4*>(part + s0 * 64 + dim);
+  const float4 ob = *reinterpret_cast<const float4*>(part + s1 * 64 + dim);
+  u32x2 w = {pack2<T>((ca * oa.x + cb * ob.x) * inv, (ca * oa.y + cb * ob.y) * inv),
+             pack2<T>((ca * oa.z + cb * ob.z) * inv, (ca * oa.w + cb * ob.w) * inv)};
+  *reinterpret_cast<u32x2*>(O + (win + i) * ldo + h * 64 + dim) = w;
+}
+
+int attention_split(int batch, int t, int heads, int dtype) {
+  // Query blocks of 256 rows: between 64 and 127 workgroups would leave half of a 256-CU GPU
+  // idle (e.g. one 1500-position window with 12 or 20 heads); fewer are spread by smaller
+  // workgroups instead, more fill the GPU as they are.
+  if (dtype == DT_F32) return 1;
+  const long blocks = (long)((t + 255) / 256) * heads * batch;
+  return blocks >= 64 && blocks < 128 ? 2 : 1;
+}
+
 hipError_t launch_attention(const void* q, const void* k, const void* v, int ld_qkv, void* o,
                             int ld_o, int batch, int t, int heads, float scale, int dtype,
-                            hipStream_t st, const int* cu, int total) {
+                            hipStream_t st, const int* cu, int total, float* part) {
   if (batch == 0 || t == 0) return hipSuccess;
+  if (!cu) total = batch * t;
+  const int kvs = part ? attention_split(batch, t, heads, dtype) : 1;
   const float c = scale * 1.4426950408889634f;  // fold log2(e): exp(x) = exp2(x * log2 e)
   // Wavefronts per workgroup: 8 (256 query rows), halved while fewer than 64 workgroups would
   // run.  Halving keeps the wavefront count and spreads it over more CUs, with less latency
   // hidden on each: measured, it pays for 6 or 8 heads of one window (36 or 48 workgroups) and
   // costs time at 12 or 20 heads (72, 120).
   int nw = 8;
-  auto blocks = [&](int w) { return (long)((t + 32 * w - 1) / (32 * w)) * heads * batch; };
+  auto blocks = [&](int w) { return (long)((t + 32 * w - 1) / (32 * w)) * heads * batch * kvs; };
   while (nw > 2 && blocks(nw) < 64) nw /= 2;
   dim3 grid((t + AQ32 - 1) / AQ32, heads, batch), block(256);
   auto run16 = [&](auto tag) {
@@ -465,12 +539,19 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int ld_
     const auto Vp = static_cast<const uint16_t*>(v);
     auto Op = static_cast<uint16_t*>(o);
     const dim3 g((unsigned)blocks(nw));
+    float* pp = kvs > 1 ? part : nullptr;
     if (nw == 8)
-      attn16_kernel<T, 8><<<g, 512, 0, st>>>(Qp, Kp, Vp, ld_qkv, Op, ld_o, t, heads, c, cu, total);
+      attn16_kernel<T, 8><<<g, 512, 0, st>>>(Qp, Kp, Vp, ld_qkv, Op, ld_o, t, heads, c, cu, total,
+                                             kvs, pp);
     else if (nw == 4)
-      attn16_kernel<T, 4><<<g, 256, 0, st>>>(Qp, Kp, Vp, ld_qkv, Op, ld_o, t, heads, c, cu, total);
+      attn16_kernel<T, 4><<<g, 256, 0, st>>>(Qp, Kp, Vp, ld_qkv, Op, ld_o, t, heads, c, cu, total,
+                                             kvs, pp);
     else
-      attn16_kernel<T, 2><<<g, 128, 0, st>>>(Qp, Kp, Vp, ld_qkv, Op, ld_o, t, heads, c, cu, total);
+      attn16_kernel<T, 2><<<g, 128, 0, st>>>(Qp, Kp, Vp, ld_qkv, Op, ld_o, t, heads, c, cu, total,
+                                             kvs, pp);
+    if (kvs > 1)
+      attn_merge_kernel<T><<<dim3((unsigned)((t + 15) / 16), (unsigned)heads, (unsigned)batch), 256,
+                             0, st>>>(part, Op, ld_o, t, heads, cu, total);
   };
   switch (dtype) {
     case DT_BF16: run16(bf16_t{}); break;

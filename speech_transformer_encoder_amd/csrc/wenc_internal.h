@@ -66,9 +66,16 @@ int linear_split(int m, int n, int k, int dtype, int epilogue);
 // ptr + (b * t + i) * ld, head h at column offset 64 * h.  scale multiplies q.k.
 // Equal windows of t rows (cu == nullptr), or a packed ragged batch: window b is rows
 // cu[b] .. cu[b + 1] - 1 (device int32 [batch + 1]) of `total`, each at most t rows long.
+// part: optional fp32 scratch of attention_split(batch, t, heads, dtype) == 2 ?
+// 2 * rows * heads * 66 floats (rows = batch * t, or total for a ragged batch); given, a problem
+// with too few query blocks to fill the GPU splits each block's keys in two halves over two
+// workgroups and a second kernel merges the halves' (O, m, l).
 hipError_t launch_attention(const void* q, const void* k, const void* v, int ld_qkv, void* o,
                             int ld_o, int batch, int t, int heads, float scale, int dtype,
-                            hipStream_t st, const int* cu = nullptr, int total = 0);
+                            hipStream_t st, const int* cu = nullptr, int total = 0,
+                            float* part = nullptr);
+// Key halves launch_attention uses with a part buffer (1: none).  Fixed for a shape.
+int attention_split(int batch, int t, int heads, int dtype);
 
 // dst[i] = round(src[i]) in dtype (or a copy for DT_F32); n elements.
 hipError_t launch_convert(const float* src, void* dst, size_t n, int dtype, hipStream_t st);

@@ -120,6 +120,20 @@ def test_stack_varlen(path):
 
 
 @pytest.mark.parametrize("path", PATHS)
+def test_stack_varlen_key_halves(path):
+    """Four short windows x 16 heads = 64 query blocks: the keys of each block are split in two
+    halves and merged, with windows of one key tile (the second half empty) and of one row."""
+    lens = [50, 1, 64, 200]
+    cfg = synth.CONFIGS["tiny_block"].with_(d_model=1024, heads=16, ffn_dim=1024)
+    w, x = _ragged_workload(cfg, lens, n_layers=1)
+    enc = build_from_workload(w, path)
+    print(f"[case] stack varlen key halves path={path} lens={lens}", flush=True)
+    got = host(enc.forward_varlen(to_device_input(x), lens))
+    ref = oracle.encoder_stack_varlen(x, lens, w.layers, cfg.heads, w.ln_post)
+    _check_block(errors(got, ref), path, "stack varlen key halves")
+
+
+@pytest.mark.parametrize("path", PATHS)
 def test_varlen_equal_lengths_is_the_dense_call(path):
     """Equal window lengths: the ragged entry point reproduces the dense one bit for bit."""
     cfg = synth.CONFIGS["tiny_block"].with_(batch=3, t=333)

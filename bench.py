@@ -403,6 +403,34 @@ def time_graph(path_name, reps):
     return out
 
 
+def time_one_window(path_name, reps, peak, mpeak, layers=4):
+    """The same large-v3 block at one 1500-position window (M = 1500 rows per GEMM, the shape of
+    the 32-block stack workload), timed as a stack call of `layers` blocks plus the final
+    LayerNorm: per-block time and the algorithmic TFLOP/s of the whole block beside the batched
+    figure.  Every block of that stack does the same work, so a few stand for the 32."""
+    import torch
+    from speech_transformer_encoder_amd import binding as B
+    from speech_transformer_encoder_amd import synth
+    from speech_transformer_encoder_amd.encoder import build_from_workload, to_device_input
+    cfg = synth.CONFIGS["large_v3_stack"].with_(n_layers=layers)
+    w = synth.make_workload(cfg)
+    enc = build_from_workload(w, B.PATHS[path_name])
+    x = to_device_input(w.x)
+    y = torch.empty_like(x)
+    enc.workspace(cfg.batch, cfg.t)
+    ms = time_events(lambda: enc.forward(x, y), reps, torch.cuda.current_stream())
+    fl = cfg.flops()
+    tf = fl["total"] / (ms * 1e-3) / 1e12
+    out = {"workload": "large_v3_one_window", "blocks_timed": layers, "final_layernorm": True,
+           "ms_per_block": round(ms / layers, 4),
+           "frames_per_s_32_blocks": round(cfg.t / (ms / layers * 32 * 1e-3), 1),
+           "tflops": round(tf, 1), "frac_peak": round(tf / peak, 4),
+           "frac_measured_peak": round(tf / mpeak, 4) if mpeak else None}
+    del enc
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, windows, layers):
     """The oracle as it stands, on a bounded sample of the workload (first windows / layers)."""
     import numpy as np
@@ -519,6 +547,10 @@ def main():
         roof["measured_peak"] = mpeak
         roof["frac_measured_peak"] = round(roof["achieved"] / mpeak, 4)
 
+    one_window = None
+    if cfg.batch > 1 and args.path != "fp32" and not args.no_next_steps:
+        one_window = time_one_window(args.path, args.kernel_reps, peak, mpeak)
+
     next_steps = {}
     if not args.no_next_steps:
         next_steps["stem"] = time_stem(cfg, args.path, args.kernel_reps)
@@ -550,6 +582,7 @@ def main():
                    "gemm_frac_measured_peak": round(gemm_tf / mpeak, 4) if mpeak else None,
                    "attention_frac_measured_peak": round(attn_tf / mpeak, 4) if mpeak else None},
         "mfma_peak_measured": measured,
+        "one_window": one_window,
         "roofline": roof,
         "kernels": kern,
         "wall_s_timed": round(wall, 4),

@@ -335,23 +335,26 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
   }
 }
 // Smaller-problem variant (fewer 256 x 256 tiles than CUs, e.g. the 1500-row GEMMs of a single
-// window): 128 (n) x 256 (m) tiles with a 32-wide k tile for a 256-thread workgroup (four
-// wavefronts, 64 x 128 outputs each), two workgroups per CU so that one's barriers and epilogue
-// overlap the other's MFMAs, three LDS stages of 64-byte rows (chunk c of row r at slot
-// c ^ ((r >> 2) & 3), conflict-free for the 16-lane fragment phases).  The tile copies are
-// inline assembly (lds_copy16), so the kernel's own s_waitcnt vmcnt is the only wait on them.
+// window): 128 (n) x 256 (m) tiles with a 32-wide k tile for a 512-thread workgroup (eight
+// wavefronts, 64 x 64 outputs each, two per SIMD so that one's waits overlap the other's MFMAs
+// even when each CU holds a single workgroup, as at one window), three LDS stages of 64-byte rows
+// (chunk c of row r at slot c ^ ((r >> 2) & 3), conflict-free for the 16-lane fragment phases).
+// The tile copies are inline assembly (lds_copy16), so the kernel's own s_waitcnt vmcnt is the
+// only wait on them.  (Four wavefronts of 64 x 128 read a third fewer fragments per MFMA but
+// leave one wavefront per SIMD at one workgroup per CU: 12-14 % slower on the one-window QKV and
+// fc1 shapes.)
 constexpr int H_N = 128, H_M = 256, H_K = 32;
-constexpr int H_WN = 2, H_WM = 2;
-constexpr int H_TN = H_N / H_WN, H_TM = H_M / H_WM;  // 64 x 128 per wavefront
-constexpr int H_NA = H_TN / 32, H_NB = H_TM / 32;     // 2 x 4
+constexpr int H_WN = 2, H_WM = 4;
+constexpr int H_TN = H_N / H_WN, H_TM = H_M / H_WM;  // 64 x 64 per wavefront
+constexpr int H_NA = H_TN / 32, H_NB = H_TM / 32;     // 2 x 2
 constexpr int H_WAVES = H_WN * H_WM;
 constexpr int H_THREADS = 64 * H_WAVES;
 constexpr int H_ROWS = H_N + H_M;                      // 64-byte rows per stage
 constexpr int H_STAGE = H_ROWS * H_K;                  // 16-bit elements per stage
-constexpr int H_LW = H_N / 16 / H_WAVES, H_LX = H_M / 16 / H_WAVES;  // 1 KB copies per wave: 2, 4
+constexpr int H_LW = H_N / 16 / H_WAVES, H_LX = H_M / 16 / H_WAVES;  // 1 KB copies per wave: 1, 2
 
 template <typename T, int EPI>
-__global__ __launch_bounds__(H_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm16_small_kernel(
+__global__ __launch_bounds__(H_THREADS) __attribute__((amdgpu_waves_per_eu(2, 4))) void gemm16_small_kernel(
     const uint16_t* __restrict__ X, int lda, const uint16_t* __restrict__ W,
     const float* __restrict__ bias, const float* residual, void* C, int ldc, int M, int N, int K,
     int ksplit) {
@@ -383,7 +386,7 @@ __global__ __launch_bounds__(H_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
   const u32x4 rW = buffer_rsrc(W + (size_t)n0 * K, (uint32_t)(wrows * K * 2));
   const u32x4 rX = buffer_rsrc(X + (size_t)m0 * lda, (uint32_t)(xrows * lda * 2));
 
-  // Copy i of wavefront w fills 1 KB block (i * 4 + w) of its operand: 16 rows of 64 bytes,
+  // Copy i of wavefront w fills 1 KB block (i * 8 + w) of its operand: 16 rows of 64 bytes,
   // lane l row (l >> 2), slot (l & 3) holding chunk slot ^ ((row >> 2) & 3).
   const int lrow = 16 * wave + (lane >> 2);
   const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
@@ -393,10 +396,12 @@ __global__ __launch_bounds__(H_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
     const uint32_t base = lds_addr(st);
 #pragma unroll
     for (int i = 0; i < H_LW; ++i)
-      lds_copy16(rW, base + (uint32_t)(i * 4 + wave) * 1024u, voW + i * 64 * K * 2 + ko);
+      lds_copy16(rW, base + (uint32_t)(i * H_WAVES + wave) * 1024u,
+                 voW + i * 16 * H_WAVES * K * 2 + ko);
 #pragma unroll
     for (int i = 0; i < H_LX; ++i)
-      lds_copy16(rX, base + H_N * 64 + (uint32_t)(i * 4 + wave) * 1024u, voX + i * 64 * lda * 2 + ko);
+      lds_copy16(rX, base + H_N * 64 + (uint32_t)(i * H_WAVES + wave) * 1024u,
+                 voX + i * 16 * H_WAVES * lda * 2 + ko);
   };
 
   const int rowA = (wn * H_TN + frow) * 64;
@@ -466,7 +471,7 @@ __global__ __launch_bounds__(H_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
     if (kt + 2 < nk) body(kt + 2, s2, s0, s1);
   }
 
-  // Epilogue as in the 8-wave kernel: 32-row blocks staged through the wavefront's own 8 KB of
+  // Epilogue as in the persistent kernel: 32-row blocks staged through the wavefront's own 8 KB of
   // LDS (wavefront-private, so only the first reuse of the stage memory needs a barrier).
   __syncthreads();
   float* ep = reinterpret_cast<float*>(lds) + wave * (32 * 64);

@@ -85,13 +85,16 @@ constexpr int G_STAGE = (G_N + G_M) * G_K;  // 16-bit elements per stage
 // unconditionally (rows past M and columns past N are dropped by the range check), so the number
 // of vector-memory operations behind that load is fixed and the next tile waits for the load
 // alone, not for the stores.
+// tiles_lim: the first tiles_lim tiles of the grouped order (the rest, when the tiles do not
+// divide into whole rounds, go to gemm16_small_kernel as half tiles).
 template <typename T, int EPI>
 __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __restrict__ X,
                                                              int lda,
                                                              const uint16_t* __restrict__ W,
                                                              const float* __restrict__ bias,
                                                              const float* residual, void* C,
-                                                             int ldc, int M, int N, int K) {
+                                                             int ldc, int M, int N, int K,
+                                                             int tiles_lim) {
   constexpr bool kResidual = EPI == EPI_BIAS_RESIDUAL || EPI == EPI_BIAS_GELU_RESIDUAL;
   // Head-major rows scatter over windows (64-bit addresses): those stores stay plain, predicated
   // global stores, and the next tile waits for them.
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave / G_WM, wm = wave % G_WM;
   const int tiles_m = (M + G_M - 1) / G_M, tiles_n = (N + G_N - 1) / G_N;
-  const int tiles = tiles_m * tiles_n;
+  const int tiles = min(tiles_m * tiles_n, tiles_lim);
   const int nk = K / G_K;
   const int per_xcd = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
@@ -357,7 +360,7 @@ template <typename T, int EPI>
 __global__ __launch_bounds__(H_THREADS) __attribute__((amdgpu_waves_per_eu(2, 4))) void gemm16_small_kernel(
     const uint16_t* __restrict__ X, int lda, const uint16_t* __restrict__ W,
     const float* __restrict__ bias, const float* residual, void* C, int ldc, int M, int N, int K,
-    int ksplit) {
+    int ksplit, int big0) {
   // One array for the three stages: the copies are inline assembly, invisible to the compiler's
   // wait insertion, so separate arrays buy nothing; the epilogue reuses the whole 72 KB.
   __shared__ __attribute__((aligned(1024))) uint16_t lds[3 * H_STAGE];
@@ -375,11 +378,25 @@ __global__ __launch_bounds__(H_THREADS) __attribute__((amdgpu_waves_per_eu(2, 4)
   // [p K / ksplit, (p + 1) K / ksplit).
   const int vv = xcd_virtual_id(blockIdx.x, gridDim.x);
   const int v = vv / ksplit, part = vv % ksplit;
-  const int group = 8 * tiles_n;
-  const int first_m = (v / group) * 8;
-  const int gm = min(tiles_m - first_m, 8);
-  const int tm = first_m + (v % group) % gm, tn = (v % group) / gm;
-  const int n0 = tn * H_N, m0 = tm * H_M;
+  int n0, m0;
+  if (big0 < 0) {
+    const int group = 8 * tiles_n;
+    const int first_m = (v / group) * 8;
+    const int gm = min(tiles_m - first_m, 8);
+    const int tm = first_m + (v % group) % gm, tn = (v % group) / gm;
+    n0 = tn * H_N;
+    m0 = tm * H_M;
+  } else {
+    // Half (128 columns) v % 2 of the 256 x 256 tile big0 + v / 2 in the persistent kernel's
+    // grouped order: the tiles left over after its whole rounds.
+    const int gtn = (N + G_N - 1) / G_N;
+    const int tb = big0 + v / 2, group = 8 * gtn;
+    const int first_m = (tb / group) * 8;
+    const int gm = min(tiles_m - first_m, 8);
+    n0 = ((tb % group) / gm) * G_N + (v & 1) * H_N;
+    m0 = (first_m + (tb % group) % gm) * G_M;
+    if (n0 >= N) return;  // the second half of a last tile only 64 columns wide
+  }
   const int kc = K / ksplit, kbyte0 = part * kc * 2;  // this part's first k, in bytes
 
   const int wrows = min(N - n0, H_N), xrows = min(M - m0, H_M);
@@ -730,7 +747,7 @@ static hipError_t launch16_epi(const uint16_t* X, int lda, const uint16_t* W, co
     if (split > 1) {
       gemm16_small_kernel<T, EPI_PARTIAL><<<dim3((unsigned)(small * split)), dim3(H_THREADS), 0,
                                             st>>>(X, lda, W, bias, nullptr, partial, n, m, n, k,
-                                                  split);
+                                                  split, -1);
       if (ln)
         return launch_splitk_reduce_ln(partial, split, bias, residual,
                                        ln->keep_x ? static_cast<float*>(c) : nullptr, ln->gamma,
@@ -743,11 +760,20 @@ static hipError_t launch16_epi(const uint16_t* X, int lda, const uint16_t* W, co
   }
   const int grid = persistent_grid();
   if (tiles >= grid) {
+    // Whole rounds on the persistent kernel.  A last partial round that would leave most CUs
+    // idle for a whole tile runs instead as half tiles (128 columns) on the small kernel, at most
+    // one per CU, in about half the time; each output is still one wavefront's k-ordered sum, so
+    // the results do not change.
+    const long whole = tiles / grid * grid, tail = tiles - whole;
+    const bool halves = tail > 0 && 2 * tail <= grid;
     gemm16_kernel<T, EPI><<<dim3((unsigned)grid), dim3(G_THREADS), 0, st>>>(
-        X, lda, W, bias, residual, c, ldc, m, n, k);
+        X, lda, W, bias, residual, c, ldc, m, n, k, (int)(halves ? whole : tiles));
+    if (halves)
+      gemm16_small_kernel<T, EPI><<<dim3((unsigned)(2 * tail)), dim3(H_THREADS), 0, st>>>(
+          X, lda, W, bias, residual, c, ldc, m, n, k, 1, (int)whole);
   } else {
     gemm16_small_kernel<T, EPI><<<dim3((unsigned)small), dim3(H_THREADS), 0, st>>>(
-        X, lda, W, bias, residual, c, ldc, m, n, k, 1);
+        X, lda, W, bias, residual, c, ldc, m, n, k, 1, -1);
   }
   return hipGetLastError();
 }

@@ -209,6 +209,11 @@ def test_full_config(name, path):
     if name in ("small_stack", "large_v3_stack"):
         g = np.load(os.path.join(GOLDEN, f"{name}_rows.npz"))
         e = errors(got[0][g["rows"]], g["y"])
+        # Diagnostic only (parity is graded on the stack output): the residual stream before the
+        # final LayerNorm, whose absolute scale grows with depth.
+        pre = run_gpu(w, path, final_norm=False)
+        report(f"{name} before the final norm, diagnostic [{PATH_NAMES[path]}]",
+               errors(pre[0][g["rows"]], g["pre_rows"]))
     elif cfg.batch > 1:
         idx, ref = _sampled_block_rows(w)
         e = errors(np.concatenate([got[b][rows] for b, rows in idx]), ref)

@@ -191,15 +191,20 @@ def kernel_breakdown(cfg, path_name, reps):
 
 def pmc_run(cfg, path_name):
     """For `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE`: two passes of one launch of each
-    block kernel (in KERNEL_ORDER), each followed by a plain device copy of COPY_BYTES that
-    scales the counters (the last pass is the one read)."""
+    block kernel (in KERNEL_ORDER; a step may be more than one dispatch, e.g. a GEMM whose last
+    partial round runs as half tiles), each step followed by a small fill that separates it from
+    the next, and each pass by a plain device copy of COPY_BYTES that scales the counters (the
+    last pass is the one read)."""
     import torch
     kern = make_kernels(cfg, path_name)
     src = torch.zeros(COPY_BYTES // 4, device="cuda")
     dst = torch.empty_like(src)
+    sep = torch.empty(64, device="cuda")
     for _ in range(2):
         for name in KERNEL_ORDER:
             kern[name][0]()
+            torch.cuda.synchronize()
+            sep.fill_(1.0)
             torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
@@ -215,13 +220,25 @@ def _counter_rows(path):
 
 
 def _last_pass(rows, counter):
-    """(per-kernel KiB in KERNEL_ORDER, copy KiB) of the last pmc pass in a counter CSV."""
+    """(per-step KiB in KERNEL_ORDER, copy KiB, kernel names) of the last pmc pass in a counter
+    CSV.  A step's dispatches are the library's kernels between two separating fills; their
+    readings are added."""
     rows = [r for r in rows if r["Counter_Name"] == counter]
     copy_idx = max(i for i, r in enumerate(rows) if "opy" in r["Kernel_Name"]
                    and "wenc" not in r["Kernel_Name"])
-    ours = [r for r in rows[:copy_idx] if "wenc::" in r["Kernel_Name"]][-len(KERNEL_ORDER):]
-    return [float(r["Counter_Value"]) for r in ours], float(rows[copy_idx]["Counter_Value"]), \
-        [r["Kernel_Name"] for r in ours]
+    groups, cur = [], []
+    for r in rows[:copy_idx]:
+        if "wenc::" in r["Kernel_Name"]:
+            cur.append(r)
+        elif cur:
+            groups.append(cur)
+            cur = []
+    if cur:
+        groups.append(cur)
+    ours = groups[-len(KERNEL_ORDER):]
+    return [sum(float(r["Counter_Value"]) for r in g) for g in ours], \
+        float(rows[copy_idx]["Counter_Value"]), \
+        [" + ".join(r["Kernel_Name"].split("(")[0] for r in g) for g in ours]
 
 
 def ingest_pmc(cfg, path_name, fetch_csv, write_csv, command):

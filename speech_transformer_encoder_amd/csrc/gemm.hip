@@ -25,7 +25,8 @@
 // residual loads) are whole 128- or 256-byte row segments.  The kernel is persistent, one
 // workgroup per CU: each XCD (eight, dispatched round-robin) runs a contiguous range of tiles
 // grouped 8 m-tiles deep, so tiles running together share operand rows in that XCD's L2, and
-// the next tile's first operand loads overlap the current tile's epilogue.
+// the next tile's first operand loads overlap the current tile's epilogue.  A short last round
+// (at most half the CUs' worth of tiles) runs as half tiles on the small kernel instead.
 #include <algorithm>
 #include <type_traits>
 

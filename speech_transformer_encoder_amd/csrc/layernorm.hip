@@ -10,6 +10,10 @@
 // loads (d <= 4096), reduces with cross-lane shuffles, and writes the normalised row in the
 // GEMM operand type (bf16 / fp16) or fp32.  Four rows per 256-thread workgroup.  The pass is
 // HBM-bound: 4 bytes read and 2 (or 4) bytes written per element.
+//
+// When the residual GEMM before a LayerNorm splits k (one window), the GEMM's second pass and the
+// LayerNorm are one kernel here (splitk_reduce_ln_rows): the row is formed from the parts in
+// registers, stored, and normalised by the same row routine, so x is not read back.
 #include "wenc_device.h"
 #include "wenc_internal.h"
 

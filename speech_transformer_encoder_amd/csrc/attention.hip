@@ -83,8 +83,10 @@ template <> struct RowSum<bf16_t> {
 // each query block's keys are split in two halves handled by two workgroups, which write the
 // unnormalised partial O (fp32) and their (m, l) to `part`; attn_merge_kernel combines them.
 // total: rows of the packed batch (batch * tmax for equal windows).
+// Eight-wavefront workgroups run two per CU (four wavefronts per SIMD, 128 VGPRs each); the
+// narrower ones serve grids smaller than the GPU and keep two wavefronts per SIMD.
 template <typename T, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4))) void attn16_kernel(const uint16_t* __restrict__ Q,
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 4 : 2, NW == 8 ? 4 : 2))) void attn16_kernel(const uint16_t* __restrict__ Q,
                                                         const uint16_t* __restrict__ Kp,
                                                         const uint16_t* __restrict__ Vp, int ld,
                                                         uint16_t* __restrict__ O, int ldo, int tmax,

@@ -510,13 +510,18 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   *reinterpret_cast<u32x2*>(O + (win + i) * ldo + h * 64 + dim) = w;
 }
 
+// Query blocks of 128 rows (four-wavefront workgroups) per (window, head) over the batch.
+static long query_blocks128(int batch, int t, int heads) {
+  return (long)((t + 127) / 128) * heads * batch;
+}
+
 int attention_split(int batch, int t, int heads, int dtype) {
-  // Query blocks of 256 rows: between 64 and 127 workgroups would leave half of a 256-CU GPU
-  // idle (e.g. one 1500-position window with 12 or 20 heads); fewer are spread by smaller
-  // workgroups instead, more fill the GPU as they are.
+  // Fewer than 128 blocks of 128 query rows (one 1500-position window with 6 or 8 heads) leave
+  // most of a 256-CU GPU idle: the keys of each block are then split in two halves.  Measured
+  // on one window: 6 heads 20.4 -> 18.2 us, 8 heads 20.7 -> 19.3 us (merge included); at 12 and
+  // 20 heads (144, 240 blocks) the split costs more than it gains.
   if (dtype == DT_F32) return 1;
-  const long blocks = (long)((t + 255) / 256) * heads * batch;
-  return blocks >= 64 && blocks < 128 ? 2 : 1;
+  return query_blocks128(batch, t, heads) < 128 ? 2 : 1;
 }
 
 hipError_t launch_attention(const void* q, const void* k, const void* v, int ld_qkv, void* o,
@@ -526,11 +531,13 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int ld_
   if (!cu) total = batch * t;
   const int kvs = part ? attention_split(batch, t, heads, dtype) : 1;
   const float c = scale * 1.4426950408889634f;  // fold log2(e): exp(x) = exp2(x * log2 e)
-  // Wavefronts per workgroup: 8 (256 query rows), halved while fewer than 64 workgroups would
-  // run.  Halving keeps the wavefront count and spreads it over more CUs, with less latency
-  // hidden on each: measured, it pays for 6 or 8 heads of one window (36 or 48 workgroups) and
-  // costs time at 12 or 20 heads (72, 120).
-  int nw = 8;
+  // Wavefronts per workgroup: 8 (256 query rows, two workgroups per CU) once there are at least
+  // 256 blocks of 128 rows, else 4, halved again while fewer than 64 workgroups would run.
+  // Narrower workgroups spread the same wavefronts over more CUs, with less latency hidden on
+  // each.  Measured, four-wavefront workgroups win for one window at every head count (20
+  // heads: 23.1 us against 31.4 us for eight and 30.8 us for eight with key halves) and for two
+  // windows of 8 heads, break even near 256 blocks and lose from four 20-head windows on.
+  int nw = query_blocks128(batch, t, heads) >= 256 ? 8 : 4;
   auto blocks = [&](int w) { return (long)((t + 32 * w - 1) / (32 * w)) * heads * batch * kvs; };
   while (nw > 2 && blocks(nw) < 64) nw /= 2;
   dim3 grid((t + AQ32 - 1) / AQ32, heads, batch), block(256);

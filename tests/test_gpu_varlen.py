@@ -121,10 +121,11 @@ def test_stack_varlen(path):
 
 @pytest.mark.parametrize("path", PATHS)
 def test_stack_varlen_key_halves(path):
-    """Four short windows x 16 heads = 64 query blocks: the keys of each block are split in two
-    halves and merged, with windows of one key tile (the second half empty) and of one row."""
+    """Four short windows (the longest 200 rows) x 8 heads = 64 blocks of 128 query rows: the
+    keys of each block are split in two halves and merged, with windows of one key tile (the
+    second half empty) and of one row."""
     lens = [50, 1, 64, 200]
-    cfg = synth.CONFIGS["tiny_block"].with_(d_model=1024, heads=16, ffn_dim=1024)
+    cfg = synth.CONFIGS["tiny_block"].with_(d_model=512, heads=8, ffn_dim=1024)
     w, x = _ragged_workload(cfg, lens, n_layers=1)
     enc = build_from_workload(w, path)
     print(f"[case] stack varlen key halves path={path} lens={lens}", flush=True)

@@ -353,40 +353,46 @@ constexpr int H_TN = H_N / H_WN, H_TM = H_M / H_WM;  // 64 x 64 per wavefront
 constexpr int H_NA = H_TN / 32, H_NB = H_TM / 32;     // 2 x 2
 constexpr int H_WAVES = H_WN * H_WM;
 constexpr int H_THREADS = 64 * H_WAVES;
-constexpr int H_ROWS = H_N + H_M;                      // 64-byte rows per stage
-constexpr int H_STAGE = H_ROWS * H_K;                  // 16-bit elements per stage
-constexpr int H_LW = H_N / 16 / H_WAVES, H_LX = H_M / 16 / H_WAVES;  // 1 KB copies per wave: 1, 2
 
-template <typename T, int EPI>
-__global__ __launch_bounds__(H_THREADS) __attribute__((amdgpu_waves_per_eu(2, 4))) void gemm16_small_kernel(
+// WM wavefronts along m: 4 (128 x 256 tiles, eight wavefronts) or 2 (128 x 128 tiles, four
+// wavefronts, for problems whose 128 x 256 grid would leave most CUs idle, e.g. the 1500-row
+// GEMMs of a base- or small-shaped window).  Each wavefront computes 64 x 64 outputs either way,
+// with the same k-ordered MFMA chain per output, so both widths give identical results.
+template <typename T, int EPI, int WM = H_WM>
+__global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))) void gemm16_small_kernel(
     const uint16_t* __restrict__ X, int lda, const uint16_t* __restrict__ W,
     const float* __restrict__ bias, const float* residual, void* C, int ldc, int M, int N, int K,
     int ksplit, int big0) {
+  constexpr int HM = 64 * WM;                              // rows of the tile
+  constexpr int HW = H_WN * WM;                            // wavefronts
+  constexpr int HLW = H_N / 16 / HW, HLX = HM / 16 / HW;   // 1 KB copies per wavefront: 1, 2 or 2, 2
+  constexpr int HSTAGE = (H_N + HM) * H_K;                 // 16-bit elements per stage
+  static_assert(WM == 2 || WM == 4, "four or eight wavefronts");
   // One array for the three stages: the copies are inline assembly, invisible to the compiler's
-  // wait insertion, so separate arrays buy nothing; the epilogue reuses the whole 72 KB.
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[3 * H_STAGE];
+  // wait insertion, so separate arrays buy nothing; the epilogue reuses it (8 KB per wavefront).
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[3 * HSTAGE];
   uint16_t* const s0 = lds;
-  uint16_t* const s1 = lds + H_STAGE;
-  uint16_t* const s2 = lds + 2 * H_STAGE;
+  uint16_t* const s1 = lds + HSTAGE;
+  uint16_t* const s2 = lds + 2 * HSTAGE;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave / H_WM, wm = wave % H_WM;
+  const int wn = wave / WM, wm = wave % WM;
   const int g = lane >> 5, frow = lane & 31;
 
-  const int tiles_m = (M + H_M - 1) / H_M, tiles_n = (N + H_N - 1) / H_N;
+  const int tiles_m = (M + HM - 1) / HM, tiles_n = (N + H_N - 1) / H_N;
   // Workgroup (tile, part): with ksplit > 1 (EPI_PARTIAL) part p covers k in
   // [p K / ksplit, (p + 1) K / ksplit).
   const int vv = xcd_virtual_id(blockIdx.x, gridDim.x);
   const int v = vv / ksplit, part = vv % ksplit;
   int n0, m0;
-  if (big0 < 0) {
+  if (WM != 4 || big0 < 0) {  // the half tiles below are 256 rows high: eight wavefronts only
     const int group = 8 * tiles_n;
     const int first_m = (v / group) * 8;
     const int gm = min(tiles_m - first_m, 8);
     const int tm = first_m + (v % group) % gm, tn = (v % group) / gm;
     n0 = tn * H_N;
-    m0 = tm * H_M;
+    m0 = tm * HM;
   } else {
     // Half (128 columns) v % 2 of the 256 x 256 tile big0 + v / 2 in the persistent kernel's
     // grouped order: the tiles left over after its whole rounds.
@@ -400,11 +406,11 @@ __global__ __launch_bounds__(H_THREADS) __attribute__((amdgpu_waves_per_eu(2, 4)
   }
   const int kc = K / ksplit, kbyte0 = part * kc * 2;  // this part's first k, in bytes
 
-  const int wrows = min(N - n0, H_N), xrows = min(M - m0, H_M);
+  const int wrows = min(N - n0, H_N), xrows = min(M - m0, HM);
   const u32x4 rW = buffer_rsrc(W + (size_t)n0 * K, (uint32_t)(wrows * K * 2));
   const u32x4 rX = buffer_rsrc(X + (size_t)m0 * lda, (uint32_t)(xrows * lda * 2));
 
-  // Copy i of wavefront w fills 1 KB block (i * 8 + w) of its operand: 16 rows of 64 bytes,
+  // Copy i of wavefront w fills 1 KB block (i * HW + w) of its operand: 16 rows of 64 bytes,
   // lane l row (l >> 2), slot (l & 3) holding chunk slot ^ ((row >> 2) & 3).
   const int lrow = 16 * wave + (lane >> 2);
   const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
@@ -413,13 +419,12 @@ __global__ __launch_bounds__(H_THREADS) __attribute__((amdgpu_waves_per_eu(2, 4)
     const int ko = kbyte0 + kt * (H_K * 2);
     const uint32_t base = lds_addr(st);
 #pragma unroll
-    for (int i = 0; i < H_LW; ++i)
-      lds_copy16(rW, base + (uint32_t)(i * H_WAVES + wave) * 1024u,
-                 voW + i * 16 * H_WAVES * K * 2 + ko);
+    for (int i = 0; i < HLW; ++i)
+      lds_copy16(rW, base + (uint32_t)(i * HW + wave) * 1024u, voW + i * 16 * HW * K * 2 + ko);
 #pragma unroll
-    for (int i = 0; i < H_LX; ++i)
-      lds_copy16(rX, base + H_N * 64 + (uint32_t)(i * H_WAVES + wave) * 1024u,
-                 voX + i * 16 * H_WAVES * lda * 2 + ko);
+    for (int i = 0; i < HLX; ++i)
+      lds_copy16(rX, base + H_N * 64 + (uint32_t)(i * HW + wave) * 1024u,
+                 voX + i * 16 * HW * lda * 2 + ko);
   };
 
   const int rowA = (wn * H_TN + frow) * 64;
@@ -460,7 +465,7 @@ __global__ __launch_bounds__(H_THREADS) __attribute__((amdgpu_waves_per_eu(2, 4)
     __builtin_amdgcn_sched_group_barrier(0x008, H_NA * H_NB - H_NA - H_NB, 0);
   };
 
-  constexpr int LT = H_LW + H_LX;  // copies per wavefront and tile
+  constexpr int LT = HLW + HLX;  // copies per wavefront and tile
   const int nk = kc / H_K;
   u32x4 fa0[H_NA], fb0[H_NB], fa1[H_NA], fb1[H_NB];
   load_tile(0, s0);
@@ -772,6 +777,14 @@ static hipError_t launch16_epi(const uint16_t* X, int lda, const uint16_t* W, co
     if (halves)
       gemm16_small_kernel<T, EPI><<<dim3((unsigned)(2 * tail)), dim3(H_THREADS), 0, st>>>(
           X, lda, W, bias, residual, c, ldc, m, n, k, 1, (int)whole);
+  } else if (2 * small < grid) {
+    // Fewer 128 x 256 tiles than half the CUs: 128 x 128 tiles of four wavefronts, twice as many
+    // workgroups.  Measured at M = 1500 (us, 128 x 256 -> 128 x 128): d 512 QKV 10.4 -> 8.9 and
+    // fc1 13.7 -> 11.0, d 768 QKV 14.3 -> 12.1; with 144 tiles or more (d 768 fc1, d 1280) the
+    // eight-wavefront tiles stay faster.
+    const long small2 = (long)((m + 127) / 128) * ((n + H_N - 1) / H_N);
+    gemm16_small_kernel<T, EPI, 2><<<dim3((unsigned)small2), dim3(256), 0, st>>>(
+        X, lda, W, bias, residual, c, ldc, m, n, k, 1, -1);
   } else {
     gemm16_small_kernel<T, EPI><<<dim3((unsigned)small), dim3(H_THREADS), 0, st>>>(
         X, lda, W, bias, residual, c, ldc, m, n, k, 1, -1);

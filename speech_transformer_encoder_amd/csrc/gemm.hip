@@ -354,23 +354,26 @@ constexpr int H_NA = H_TN / 32, H_NB = H_TM / 32;     // 2 x 2
 constexpr int H_WAVES = H_WN * H_WM;
 constexpr int H_THREADS = 64 * H_WAVES;
 
-// WM wavefronts along m: 4 (128 x 256 tiles, eight wavefronts) or 2 (128 x 128 tiles, four
-// wavefronts, for problems whose 128 x 256 grid would leave most CUs idle, e.g. the 1500-row
-// GEMMs of a base- or small-shaped window).  Each wavefront computes 64 x 64 outputs either way,
-// with the same k-ordered MFMA chain per output, so both widths give identical results.
-template <typename T, int EPI, int WM = H_WM>
+// WM wavefronts along m, HM rows per tile: (4, 256) for 128 x 256 tiles of eight wavefronts of
+// 64 x 64; for problems whose 128 x 256 grid would leave most CUs idle (e.g. the 1500-row GEMMs of
+// a tiny-, base- or small-shaped window), (4, 128): 128 x 128 tiles of eight wavefronts of 64 x 32.
+// (2, 128), four wavefronts of 64 x 64, is kept as a shape the kernel supports.  Every output is
+// the same k-ordered MFMA chain whatever the tile, so all shapes give identical results.
+template <typename T, int EPI, int WM = H_WM, int HM = H_M>
 __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))) void gemm16_small_kernel(
     const uint16_t* __restrict__ X, int lda, const uint16_t* __restrict__ W,
     const float* __restrict__ bias, const float* residual, void* C, int ldc, int M, int N, int K,
     int ksplit, int big0) {
-  constexpr int HM = 64 * WM;                              // rows of the tile
   constexpr int HW = H_WN * WM;                            // wavefronts
-  constexpr int HLW = H_N / 16 / HW, HLX = HM / 16 / HW;   // 1 KB copies per wavefront: 1, 2 or 2, 2
+  constexpr int TM = HM / WM, NB = TM / 32;                // rows per wavefront, 32-row blocks
+  constexpr int HLW = H_N / 16 / HW, HLX = HM / 16 / HW;   // 1 KB copies per wavefront and operand
   constexpr int HSTAGE = (H_N + HM) * H_K;                 // 16-bit elements per stage
-  static_assert(WM == 2 || WM == 4, "four or eight wavefronts");
+  // Three stages, or the epilogue's 8 KB (4096 16-bit elements) per wavefront if that is more.
+  constexpr int LDS_ELEMS = 3 * HSTAGE > HW * 4096 ? 3 * HSTAGE : HW * 4096;
+  static_assert((WM == 4 && (HM == 256 || HM == 128)) || (WM == 2 && HM == 128), "tile shapes");
   // One array for the three stages: the copies are inline assembly, invisible to the compiler's
   // wait insertion, so separate arrays buy nothing; the epilogue reuses it (8 KB per wavefront).
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[3 * HSTAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
   uint16_t* const s0 = lds;
   uint16_t* const s1 = lds + HSTAGE;
   uint16_t* const s2 = lds + 2 * HSTAGE;
@@ -386,7 +389,7 @@ __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))
   const int vv = xcd_virtual_id(blockIdx.x, gridDim.x);
   const int v = vv / ksplit, part = vv % ksplit;
   int n0, m0;
-  if (WM != 4 || big0 < 0) {  // the half tiles below are 256 rows high: eight wavefronts only
+  if (HM != G_M || big0 < 0) {  // the half tiles below are 256 rows high
     const int group = 8 * tiles_n;
     const int first_m = (v / group) * 8;
     const int gm = min(tiles_m - first_m, 8);
@@ -428,46 +431,48 @@ __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))
   };
 
   const int rowA = (wn * H_TN + frow) * 64;
-  const int rowB = (H_N + wm * H_TM + frow) * 64;
+  const int rowB = (H_N + wm * TM + frow) * 64;
   int xo[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) xo[s] = ((2 * s + g) ^ ((lane >> 2) & 3)) << 4;
-  auto read_frags = [&](const uint16_t* st, int s, u32x4 (&fa)[H_NA], u32x4 (&fb)[H_NB]) {
+  auto read_frags = [&](const uint16_t* st, int s, u32x4 (&fa)[H_NA], u32x4 (&fb)[NB]) {
     const char* base = reinterpret_cast<const char*>(st);
     fa[0] = *reinterpret_cast<const u32x4*>(base + rowA + xo[s]);
 #pragma unroll
-    for (int b = 0; b < H_NB; ++b)
+    for (int b = 0; b < NB; ++b)
       fb[b] = *reinterpret_cast<const u32x4*>(base + rowB + b * 2048 + xo[s]);
 #pragma unroll
     for (int a = 1; a < H_NA; ++a)
       fa[a] = *reinterpret_cast<const u32x4*>(base + rowA + a * 2048 + xo[s]);
   };
 
-  f32x16 acc[H_NA][H_NB];
+  f32x16 acc[H_NA][NB];
 #pragma unroll
   for (int a = 0; a < H_NA; ++a)
 #pragma unroll
-    for (int b = 0; b < H_NB; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-  auto mm = [&](const u32x4 (&fa)[H_NA], const u32x4 (&fb)[H_NB]) {
+  auto mm = [&](const u32x4 (&fa)[H_NA], const u32x4 (&fb)[NB]) {
 #pragma unroll
     for (int a = 0; a < H_NA; ++a)
 #pragma unroll
-      for (int b = 0; b < H_NB; ++b) acc[a][b] = mfma32x32x16<T>(fa[a], fb[b], acc[a][b]);
+      for (int b = 0; b < NB; ++b) acc[a][b] = mfma32x32x16<T>(fa[a], fb[b], acc[a][b]);
   };
   auto sched = [&]() {
+    constexpr int R = H_NA + NB, MF = H_NA * NB, P = R < MF ? R : MF;  // reads, MFMAs, pairs
 #pragma unroll
-    for (int q = 0; q < H_NA + H_NB; ++q) {
+    for (int q = 0; q < P; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, H_NA * H_NB - H_NA - H_NB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, MF - P, 0);
+    if constexpr (R > P) __builtin_amdgcn_sched_group_barrier(0x100, R - P, 0);
   };
 
   constexpr int LT = HLW + HLX;  // copies per wavefront and tile
   const int nk = kc / H_K;
-  u32x4 fa0[H_NA], fb0[H_NB], fa1[H_NA], fb1[H_NB];
+  u32x4 fa0[H_NA], fb0[NB], fa1[H_NA], fb1[NB];
   load_tile(0, s0);
   if (nk > 1) load_tile(1, s1);
   if (nk > 1) __builtin_amdgcn_s_waitcnt(0x0F70 | LT); else __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -501,7 +506,7 @@ __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))
   const int nw = n0 + wn * H_TN;
   const bool cols_ok = nw < N;
 #pragma unroll
-  for (int b = 0; b < H_NB; ++b) {
+  for (int b = 0; b < NB; ++b) {
 #pragma unroll
     for (int a = 0; a < H_NA; ++a)
 #pragma unroll
@@ -515,7 +520,7 @@ __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))
                         acc[a][b][4 * j + 2] + bb.z, acc[a][b][4 * j + 3] + bb.w);
       }
     if (!cols_ok) continue;
-    const int mb = m0 + wm * H_TM + b * 32;
+    const int mb = m0 + wm * TM + b * 32;
     if constexpr (EPI == EPI_PARTIAL) {
       // fp32 rows of 64 columns of this part's sums: partial[part][m][n], row stride N.
       float* P = static_cast<float*>(C) + (size_t)part * M * N;
@@ -749,11 +754,20 @@ static hipError_t launch16_epi(const uint16_t* X, int lda, const uint16_t* W, co
   const long small = (long)((m + H_M - 1) / H_M) * ((n + H_N - 1) / H_N);
   const int split = partial ? linear_split(m, n, k, DT_F16, EPI) : 1;
   if (ln && (EPI != EPI_BIAS_RESIDUAL || split < 2 || ldc != n)) return hipErrorInvalidValue;
+  const int grid = persistent_grid();
+  const long small2 = (long)((m + 127) / 128) * ((n + H_N - 1) / H_N);  // 128 x 128 tiles
   if constexpr (EPI == EPI_BIAS_RESIDUAL || EPI == EPI_BIAS_GELU_RESIDUAL) {
     if (split > 1) {
-      gemm16_small_kernel<T, EPI_PARTIAL><<<dim3((unsigned)(small * split)), dim3(H_THREADS), 0,
-                                            st>>>(X, lda, W, bias, nullptr, partial, n, m, n, k,
-                                                  split, -1);
+      // The parts' tiles are 128 x 128 when 128 x 256 ones would fill under half the CUs (as
+      // below); the parts themselves do not depend on the tile shape.
+      if (2 * small * split < grid)
+        gemm16_small_kernel<T, EPI_PARTIAL, 4, 128><<<dim3((unsigned)(small2 * split)),
+                                                       dim3(H_THREADS), 0, st>>>(
+            X, lda, W, bias, nullptr, partial, n, m, n, k, split, -1);
+      else
+        gemm16_small_kernel<T, EPI_PARTIAL><<<dim3((unsigned)(small * split)), dim3(H_THREADS),
+                                              0, st>>>(X, lda, W, bias, nullptr, partial, n, m, n,
+                                                       k, split, -1);
       if (ln)
         return launch_splitk_reduce_ln(partial, split, bias, residual,
                                        ln->keep_x ? static_cast<float*>(c) : nullptr, ln->gamma,
@@ -764,7 +778,6 @@ static hipError_t launch16_epi(const uint16_t* X, int lda, const uint16_t* W, co
       return hipGetLastError();
     }
   }
-  const int grid = persistent_grid();
   if (tiles >= grid) {
     // Whole rounds on the persistent kernel.  A last partial round that would leave most CUs
     // idle for a whole tile runs instead as half tiles (128 columns) on the small kernel, at most
@@ -778,12 +791,12 @@ static hipError_t launch16_epi(const uint16_t* X, int lda, const uint16_t* W, co
       gemm16_small_kernel<T, EPI><<<dim3((unsigned)(2 * tail)), dim3(H_THREADS), 0, st>>>(
           X, lda, W, bias, residual, c, ldc, m, n, k, 1, (int)whole);
   } else if (2 * small < grid) {
-    // Fewer 128 x 256 tiles than half the CUs: 128 x 128 tiles of four wavefronts, twice as many
-    // workgroups.  Measured at M = 1500 (us, 128 x 256 -> 128 x 128): d 512 QKV 10.4 -> 8.9 and
-    // fc1 13.7 -> 11.0, d 768 QKV 14.3 -> 12.1; with 144 tiles or more (d 768 fc1, d 1280) the
-    // eight-wavefront tiles stay faster.
-    const long small2 = (long)((m + 127) / 128) * ((n + H_N - 1) / H_N);
-    gemm16_small_kernel<T, EPI, 2><<<dim3((unsigned)small2), dim3(256), 0, st>>>(
+    // Fewer 128 x 256 tiles than half the CUs: 128 x 128 tiles, eight wavefronts of 64 x 32, twice
+    // as many workgroups.  Measured at M = 1500 (us, 128 x 256 -> 128 x 128 with four wavefronts
+    // of 64 x 64 -> with eight of 64 x 32): d 384 QKV 9.2 -> 7.6 -> 6.4, fc1 12.2 -> 9.6 -> 8.3;
+    // d 512 QKV 10.7 -> 8.8 -> 7.5, fc1 14.0 -> 11.0 -> 9.7; d 768 QKV 14.4 -> 12.0 -> 11.0.  With
+    // 144 tiles or more (d 768 fc1, d 1280) the 128 x 256 tiles stay as fast or faster.
+    gemm16_small_kernel<T, EPI, 4, 128><<<dim3((unsigned)small2), dim3(H_THREADS), 0, st>>>(
         X, lda, W, bias, residual, c, ldc, m, n, k, 1, -1);
   } else {
     gemm16_small_kernel<T, EPI><<<dim3((unsigned)small), dim3(H_THREADS), 0, st>>>(

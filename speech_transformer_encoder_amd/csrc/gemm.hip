@@ -27,6 +27,11 @@
 // grouped 8 m-tiles deep, so tiles running together share operand rows in that XCD's L2, and
 // the next tile's first operand loads overlap the current tile's epilogue.  A short last round
 // (at most half the CUs' worth of tiles) runs as half tiles on the small kernel instead.
+//
+// Problems with fewer 256 x 256 tiles than CUs (the 1500-row GEMMs of one window) run on the
+// small kernel: 128 x 256 tiles of eight wavefronts, or 128 x 128 tiles where those would leave
+// more than half the CUs idle, with the residual GEMMs split over k (fp32 parts added in a fixed
+// order by a second kernel, which can also apply the LayerNorm that follows).
 #include <algorithm>
 #include <type_traits>
 

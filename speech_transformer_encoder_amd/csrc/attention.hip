@@ -8,7 +8,9 @@
 // memory.
 //
 // gfx950 mapping.  One 512-thread workgroup per (256 query rows, head, window); wavefront w owns
-// 32 queries.  Keys go in tiles of 64 through three LDS stages, each a K tile and a V tile of
+// 32 queries.  (Problems with fewer than 256 blocks of 128 query rows, e.g. one window, run
+// workgroups of four or two wavefronts instead, and split the keys of each query block in two
+// halves when there are fewer than 128 blocks.)  Keys go in tiles of 64 through three LDS stages, each a K tile and a V tile of
 // 64 rows x 128 bytes, loaded global -> LDS directly (buffer_load_dwordx4 ... lds, range-checked
 // so that keys past t read as zeros) two tiles ahead of their use.  Chunk c (16 bytes) of row r
 // sits at slot c ^ f(r), f chosen per tile so that the 16-lane phases of its reads hit distinct

@@ -745,9 +745,6 @@ static int split_plan(int m, int n, int k, int* tile_rows) {
   const long small = (long)((m + H_M - 1) / H_M) * ((n + H_N - 1) / H_N);
   int s = 1;
   while (s < 8 && small * s * 2 <= 256 && k % (s * 2 * H_K) == 0 && k / (s * 2) >= 256) s *= 2;
-  // k too short for two parts of 256 (d 384: the out-projection): two parts of at least 128,
-  // whose second pass can then also apply the LayerNorm that follows (a launch saved).
-  if (s == 1 && small * 2 <= 256 && k % (2 * H_K) == 0 && k / 2 >= 128) s = 2;
   if (2 * small * s < 256) {
     *tile_rows = 128;
   } else if (s >= 4 && k / s < 512) {

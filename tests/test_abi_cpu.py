@@ -58,6 +58,22 @@ def test_sizes():
     assert B.whisper_enc_workspace_bytes(1, 1500, 1280, 16, 5120, 0) == 0  # head_dim 80
 
 
+def test_workspace_follows_the_split_plans(lib):
+    """One window: the workspace holds the 16-bit activations ([t, d] and [t, max(3d, f)]) and one
+    scratch region sized for the larger of the residual GEMMs' fp32 k parts and the attention key
+    halves' (O, m, l).  The sizes pin the largest part count (fc2's) against the key halves:
+      d 1280, 20 heads: fc2 4 parts (the out-projection 2); 240 query blocks of 128 rows, no key
+        halves -> 4 x 1500 x 1280 floats;
+      d 512, 8 heads: fc2 4 parts (8 parts of 256 k halved); 96 blocks, key halves
+        (2 x 1500 x 8 x 66 floats, smaller) -> 4 x 1500 x 512 floats;
+      d 384, 6 heads: fc2 4 parts (the out-projection unsplit: k 384 has no two parts of 256);
+        72 blocks, key halves -> 4 x 1500 x 384 floats."""
+    P16 = B.WENC_PATH_FP16
+    for d, h, f in [(1280, 20, 5120), (512, 8, 2048), (384, 6, 1536)]:
+        act = 1500 * d * 2 + 1500 * max(3 * d, f) * 2
+        assert B.whisper_enc_workspace_bytes(1, 1500, d, h, f, P16) == act + 4 * 1500 * d * 4, d
+
+
 def test_strerror(lib):
     for code in range(5):
         assert B.strerror(code)

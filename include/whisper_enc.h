@@ -19,8 +19,9 @@
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers (memory of the current HIP device) unless marked "host".
  *     The caller owns every buffer; the library never allocates, frees or synchronises, keeps
- *     no mutable global state, and enqueues all work on `stream` (a hipStream_t; NULL = the
- *     default stream).  Results are ready when the stream's work completes.
+ *     no mutable global state (apart from the static scratch of
+ *     whisper_enc_stack_forward_noalloc), and enqueues all work on `stream` (a hipStream_t;
+ *     NULL = the default stream).  Results are ready when the stream's work completes.
  *   - Matrices are row-major.  Activations x, y are [batch, t, d_model] fp32; weights are in
  *     PyTorch layout [n_out, n_in].
  *   - Every argument is validated before anything is enqueued; a call that returns an error
@@ -47,6 +48,8 @@ extern "C" {
                                /* window's QKV rows (t * 3 d_model elements) >= 2 GiB        */
 #define WENC_ERR_WORKSPACE 3   /* workspace_bytes below whisper_enc_workspace_bytes()       */
 #define WENC_ERR_HIP 4         /* HIP reported an error for a launch                         */
+#define WENC_ERR_SCRATCH 5     /* whisper_enc_stack_forward_noalloc: the shape needs more     */
+                               /* workspace than its static scratch holds                    */
 
 /* Arithmetic paths: the type of every matrix-multiply operand.  Accumulation, LayerNorm
  * statistics, softmax state and the residual stream are fp32 on every path.
@@ -160,6 +163,25 @@ int whisper_enc_stack_forward(const float* x, float* y, const void* layers, int 
                               const float* ln_post_g, const float* ln_post_b, int batch, int t,
                               int d_model, int heads, int ffn_dim, int path, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/*
+ * whisper_enc_stack_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The workspace is a static device array of WENC_NOALLOC_SCRATCH_BYTES per GPU,
+ * held from the first call on that GPU until the process ends; the call itself allocates
+ * nothing.  64 MiB hold the workspace of one 1500-position window of every Whisper encoder size
+ * (large-v3: 47.6 MiB on the 16-bit paths, 36.6 MiB on fp32, 85.1 MiB on Q8 / Q4, which is
+ * rejected).  A shape whose whisper_enc_workspace_bytes() exceeds it returns WENC_ERR_SCRATCH
+ * (having enqueued nothing).  The array of the current device is used (the stream must belong to
+ * it), so calls that overlap on one GPU (other threads, or other streams) race on it: serialise
+ * them.  Other arguments and the result are exactly those of whisper_enc_stack_forward.  The
+ * first call on a device looks the array's address up (a HIP query, no allocation).
+ */
+#define WENC_NOALLOC_SCRATCH_BYTES (64 << 20)
+int whisper_enc_stack_forward_noalloc(const float* x, float* y, const void* layers, int n_layers,
+                                      const float* ln_post_g, const float* ln_post_b, int batch,
+                                      int t, int d_model, int heads, int ffn_dim, int path,
+                                      void* stream);
 
 /* ---- Step-level entry points: one step of the block each, for tests and profiling. ---- */
 

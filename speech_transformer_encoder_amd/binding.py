@@ -24,6 +24,8 @@ WENC_ERR_ARG = 1
 WENC_ERR_UNSUPPORTED = 2
 WENC_ERR_WORKSPACE = 3
 WENC_ERR_HIP = 4
+WENC_ERR_SCRATCH = 5
+WENC_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 WENC_PATH_BF16 = 0
 WENC_PATH_FP32 = 1
@@ -61,6 +63,7 @@ EXPORTS = (
     "whisper_enc_stem_forward",
     "whisper_enc_varlen_workspace_bytes", "whisper_enc_stack_forward_varlen",
     "whisper_enc_attention_varlen", "whisper_enc_quantize_matrix", "whisper_enc_dequantize_matrix",
+    "whisper_enc_stack_forward_noalloc",
 )
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -106,6 +109,7 @@ def load() -> ctypes.CDLL:
         "whisper_enc_attention_varlen": (I, [P, P, P, P, P, I, I, I, I, I, I, I, P]),
         "whisper_enc_quantize_matrix": (I, [P, P, P, I, I, I, P]),
         "whisper_enc_dequantize_matrix": (I, [P, P, P, I, I, I, P]),
+        "whisper_enc_stack_forward_noalloc": (I, [P, P, P, I, P, P, I, I, I, I, I, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -174,6 +178,15 @@ def whisper_enc_stack_forward(x, y, layers, n_layers, ln_post_g, ln_post_b, batc
                                             heads, ffn_dim, path, _ptr(workspace),
                                             workspace_bytes, _stream(stream)),
            "whisper_enc_stack_forward")
+
+
+def whisper_enc_stack_forward_noalloc(x, y, layers, n_layers, ln_post_g, ln_post_b, batch, t,
+                                      d_model, heads, ffn_dim, path, stream=None) -> None:
+    _check(load().whisper_enc_stack_forward_noalloc(_ptr(x), _ptr(y), _ptr(layers), n_layers,
+                                                    _ptr(ln_post_g), _ptr(ln_post_b), batch, t,
+                                                    d_model, heads, ffn_dim, path,
+                                                    _stream(stream)),
+           "whisper_enc_stack_forward_noalloc")
 
 
 def whisper_enc_layernorm(x, gamma, beta, y, rows, d, out_dtype, stream=None) -> None:

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/whisper_enc.h"
 #include "wenc_internal.h"
@@ -246,6 +247,9 @@ const char* whisper_enc_strerror(int code) {
     case WENC_ERR_UNSUPPORTED: return "unsupported shape (head_dim must be 64)";
     case WENC_ERR_WORKSPACE: return "workspace too small";
     case WENC_ERR_HIP: return "HIP launch error";
+    case WENC_ERR_SCRATCH:
+      return "shape needs more workspace than the no-alloc entry point's static scratch "
+             "(WENC_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status code";
 }
@@ -316,22 +320,29 @@ size_t whisper_enc_workspace_bytes(int batch, int t, int d_model, int heads, int
 
 namespace {
 
+// Pointer and count checks of a stack call (shapes already checked).
+int check_stack_args(const float* x, const float* y, const void* layers, int n_layers,
+                     const float* ln_post_g, const float* ln_post_b, size_t rows, int d_model) {
+  if (n_layers < 0) return WENC_ERR_ARG;
+  if ((ln_post_g == nullptr) != (ln_post_b == nullptr)) return WENC_ERR_ARG;
+  if (rows == 0) return WENC_OK;
+  if (!x || !y || !aligned(x, 16) || !aligned(y, 16)) return WENC_ERR_ARG;
+  if (overlaps_partially(x, y, rows * d_model * sizeof(float))) return WENC_ERR_ARG;
+  if (ln_post_g && (!aligned(ln_post_g, 16) || !aligned(ln_post_b, 16))) return WENC_ERR_ARG;
+  if (n_layers > 0 && (!layers || !aligned(layers, kAlign))) return WENC_ERR_ARG;
+  return WENC_OK;
+}
+
 // Stack over `rows` rows: equal windows of t (cu == nullptr) or a ragged batch (t = longest
 // window); shapes already checked.
 int stack_impl(const float* x, float* y, const void* layers, int n_layers, const float* ln_post_g,
                const float* ln_post_b, const int* cu, int batch, size_t rows, int t, int d_model,
                int heads, int ffn_dim, int path, void* workspace, size_t workspace_bytes,
                void* stream) {
-  int rc;
-  if (n_layers < 0) return WENC_ERR_ARG;
-  if ((ln_post_g == nullptr) != (ln_post_b == nullptr)) return WENC_ERR_ARG;
-  if (rows == 0) return WENC_OK;
+  int rc = check_stack_args(x, y, layers, n_layers, ln_post_g, ln_post_b, rows, d_model);
+  if (rc != WENC_OK || rows == 0) return rc;
   const size_t xbytes = rows * d_model * sizeof(float);
-  if (!x || !y || !aligned(x, 16) || !aligned(y, 16)) return WENC_ERR_ARG;
-  if (overlaps_partially(x, y, xbytes)) return WENC_ERR_ARG;
-  if (ln_post_g && (!aligned(ln_post_g, 16) || !aligned(ln_post_b, 16))) return WENC_ERR_ARG;
   if (n_layers > 0) {
-    if (!layers || !aligned(layers, kAlign)) return WENC_ERR_ARG;
     if (!workspace || !aligned(workspace, kAlign)) return WENC_ERR_ARG;
     if (workspace_bytes < workspace_size(batch, t, heads, rows, d_model, ffn_dim, path))
       return WENC_ERR_WORKSPACE;
@@ -424,6 +435,68 @@ int whisper_enc_block_forward(const float* x, float* y, const void* layer, int b
   if (!layer) return WENC_ERR_ARG;
   return whisper_enc_stack_forward(x, y, layer, 1, nullptr, nullptr, batch, t, d_model, heads,
                                    ffn_dim, path, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- The stack without a caller workspace, for callers that cannot allocate. ----
+//
+// The workspace lives in a static device array of WENC_NOALLOC_SCRATCH_BYTES (one copy per GPU,
+// held until the process ends).  In host code the array's name stands for a host-side shadow,
+// not a device address, so the address every kernel receives is the one hipGetSymbolAddress
+// returns for the current device, looked up once per device and kept.  No kernel of the block
+// reads workspace memory it has not written in the same call, so nothing needs clearing
+// between calls; calls that overlap on one GPU share the array and race.
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+__device__ __attribute__((aligned(256))) unsigned char scratch[WENC_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch` (looked up on first use).
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return WENC_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return WENC_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return WENC_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return WENC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int whisper_enc_stack_forward_noalloc(const float* x, float* y, const void* layers, int n_layers,
+                                      const float* ln_post_g, const float* ln_post_b, int batch,
+                                      int t, int d_model, int heads, int ffn_dim, int path,
+                                      void* stream) {
+  int rc = check_shape(batch, t, d_model, heads, ffn_dim, path);
+  if (rc != WENC_OK) return rc;
+  const size_t rows = (size_t)batch * t;
+  rc = check_stack_args(x, y, layers, n_layers, ln_post_g, ln_post_b, rows, d_model);
+  if (rc != WENC_OK || rows == 0) return rc;
+  if (n_layers > 0 && workspace_size(batch, t, heads, rows, d_model, ffn_dim, path) >
+                          (size_t)WENC_NOALLOC_SCRATCH_BYTES)
+    return WENC_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (n_layers > 0) {  // every argument is valid: now look up the device's scratch
+    rc = scratch_of_current_device(&ws);
+    if (rc != WENC_OK) return rc;
+  }
+  return stack_impl(x, y, layers, n_layers, ln_post_g, ln_post_b, nullptr, batch, rows, t,
+                    d_model, heads, ffn_dim, path, ws, ws ? (size_t)WENC_NOALLOC_SCRATCH_BYTES : 0,
+                    stream);
 }
 
 int whisper_enc_layernorm(const float* x, const float* gamma, const float* beta, void* y,

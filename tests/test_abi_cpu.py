@@ -75,7 +75,7 @@ def test_workspace_follows_the_split_plans(lib):
 
 
 def test_strerror(lib):
-    for code in range(5):
+    for code in range(6):
         assert B.strerror(code)
     assert "unknown" in B.strerror(99)
 
@@ -123,6 +123,33 @@ def test_stack_validation(lib):
     bad = list(args); bad[9] = 16
     assert f(*bad) == B.WENC_ERR_UNSUPPORTED
     assert ok  # the valid call itself needs a GPU
+
+
+def test_noalloc_validation(lib):
+    """The no-allocation entry point checks every argument, and the shape's workspace against its
+    static scratch, before its first HIP call (the device's scratch address lookup)."""
+    f = lib.whisper_enc_stack_forward_noalloc
+    args = [FAKE, FAKE + (1 << 28), FAKE, 2, None, None, 1, 1500, 1280, 20, 5120,
+            B.WENC_PATH_FP16, None]
+    assert B.whisper_enc_workspace_bytes(1, 1500, 1280, 20, 5120, B.WENC_PATH_FP16) \
+        <= B.WENC_NOALLOC_SCRATCH_BYTES
+    bad = list(args); bad[6] = 2                               # two windows: 65.9 MiB
+    assert f(*bad) == B.WENC_ERR_SCRATCH
+    bad = list(args); bad[11] = B.WENC_PATH_Q8                 # + fp16 expansion: 85.1 MiB
+    assert f(*bad) == B.WENC_ERR_SCRATCH
+    bad = list(args); bad[3] = -1
+    assert f(*bad) == B.WENC_ERR_ARG
+    bad = list(args); bad[0] = FAKE + 4                        # misaligned x
+    assert f(*bad) == B.WENC_ERR_ARG
+    bad = list(args); bad[2] = None
+    assert f(*bad) == B.WENC_ERR_ARG
+    bad = list(args); bad[4] = FAKE                            # gamma without beta
+    assert f(*bad) == B.WENC_ERR_ARG
+    bad = list(args); bad[9] = 16                              # head_dim 80
+    assert f(*bad) == B.WENC_ERR_UNSUPPORTED
+    bad = list(args); bad[6] = 0                               # no rows: nothing to do
+    assert f(*bad) == B.WENC_OK
+    assert B.strerror(B.WENC_ERR_SCRATCH).startswith("shape needs more workspace")
 
 
 def test_step_validation(lib):

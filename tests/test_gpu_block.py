@@ -109,6 +109,25 @@ def test_block_attention_key_halves(path):
     check(errors(got, ref), path, "block d512 h8 t1100")
 
 
+def test_block_key_halves_large_logits():
+    """The key-halves configuration of the last test (four-wavefront workgroups, 72 query blocks,
+    each block's keys split in two and merged) with Wq scaled by 100: logits then spread over
+    about +-100 (standard deviation 20), so the running max is raised in the middle of the key
+    loop of most rows, in both halves, and the merge combines halves whose maxima differ widely.
+    fp16 operands: rounding q, k and the probabilities to fp16 moves the block output by an MAE of
+    3.4e-4 and a max relative error of 4.5e-3 at these logits (float64 emulation of those
+    roundings), inside the block's bar; a wrong rescale would move it by the size of v.  (With
+    bf16 operands the rounding of q alone moves logits of 100 by ~0.2, beyond the bar; the
+    step-level outlier tests cover bf16 with a componentwise bound.)"""
+    cfg = synth.CONFIGS["tiny_block"].with_(t=1100, d_model=512, heads=8, ffn_dim=1024)
+    w = synth.make_workload(cfg)
+    w.layers[0]["wq"] = (w.layers[0]["wq"] * 100.0).astype(np.float32)
+    print("[case] block key halves, logits +-100, fp16", flush=True)
+    got = run_gpu(w, B.WENC_PATH_FP16)
+    ref = oracle.encoder_block(w.x, w.layers[0], cfg.heads)
+    check(errors(got, ref), B.WENC_PATH_FP16, "block d512 h8 t1100 Wq x100")
+
+
 def test_in_place_and_determinism():
     cfg = synth.CONFIGS["tiny_block"].with_(batch=3, t=150)
     w = synth.make_workload(cfg)
@@ -120,13 +139,37 @@ def test_in_place_and_determinism():
 
 
 def test_windows_are_independent():
-    """A window's output is bit-identical whether it runs alone or inside a batch."""
+    """At this shape a window's output is bit-identical whether it runs alone or inside a batch
+    of four: 300 and 1200 rows get the same split-k plans (fc2 in 4 parts on 128-row tiles, the
+    out-projection unsplit), and the attention result does not depend on the workgroup width or
+    the key split.  Where the plans differ, results differ in the last bits
+    (test_window_alone_vs_batched_large_v3)."""
     cfg = synth.CONFIGS["tiny_block"].with_(batch=4, t=300)
     w = synth.make_workload(cfg)
     enc = build_from_workload(w, B.WENC_PATH_BF16)
     full = host(enc.forward(to_device_input(w.x)))
     alone = host(enc.forward(to_device_input(w.x[2:3])))
     np.testing.assert_array_equal(full[2:3], alone)
+
+
+def test_window_alone_vs_batched_large_v3():
+    """One large-v3 window alone runs its out-projection and fc2 as split-k products (2 and 4
+    fp32 parts added in order, LN2 fused into the reduction), while inside the batch of 16 the
+    same GEMMs run unsplit on the persistent kernel: the fp32 sums are formed in another order, so
+    the two outputs may differ in the last bits.  Both must meet the block's bar against the
+    oracle on sampled rows (the batch's other 15 windows do not matter)."""
+    cfg = synth.CONFIGS["large_v3_batch16_block"]
+    w = synth.make_workload(cfg)
+    enc = build_from_workload(w, B.WENC_PATH_FP16)
+    print("[case] large-v3 window 3 alone vs in the batch of 16", flush=True)
+    batched = host(enc.forward(to_device_input(w.x)))[3]
+    alone = host(enc.forward(to_device_input(w.x[3:4])))[0]
+    big = np.where(np.abs(w.x[3]).max(axis=1) > 10)[0][:2]
+    rows = np.unique(np.concatenate([[0, 1, 700, cfg.t - 1], big]))
+    ref = oracle.encoder_block_rows(w.x[3], w.layers[0], cfg.heads, rows)
+    check(errors(alone[rows], ref), B.WENC_PATH_FP16, "large-v3 window alone")
+    check(errors(batched[rows], ref), B.WENC_PATH_FP16, "large-v3 window in the batch")
+    report("large-v3 window alone vs batched (mutual)", errors(alone, batched))
 
 
 @pytest.mark.parametrize("path", [B.WENC_PATH_BF16, B.WENC_PATH_FP16, B.WENC_PATH_Q8])

@@ -30,6 +30,9 @@ class EncoderStack:
 
     ``layers``: per-block parameter dicts in PyTorch layout (numpy or torch, fp32 values), keys
     ``ln1_g ln1_b wq bq wk bk wv bv wo bo ln2_g ln2_b w1 b1 w2 b2`` (``bk`` may be None).
+
+    One object holds one workspace: calls that may run at the same time on different streams
+    need one object each (or are ordered by the caller), since they would share it.
     """
 
     def __init__(self, layers: Sequence[Dict], d_model: int, heads: int, ffn_dim: int,
@@ -54,6 +57,23 @@ class EncoderStack:
             self.ln_post = (_device_f32(ln_post[0], self.device), _device_f32(ln_post[1], self.device))
         self._ws = None
 
+    def _launch_stream(self, stream):
+        """The stream the library enqueues on, as a torch stream object (``None``: torch's
+        current stream; an integer: a raw ``hipStream_t`` handle)."""
+        import torch
+        if stream is None:
+            return torch.cuda.current_stream(self.device)
+        if isinstance(stream, int):
+            return torch.cuda.ExternalStream(stream, device=self.device)
+        return stream
+
+    def _keep_for(self, tensor, launch):
+        """Tensors the kernels read must outlive the work enqueued on ``launch``: tell the caching
+        allocator so when ``launch`` is not the stream they were allocated on."""
+        import torch
+        if launch != torch.cuda.current_stream(self.device):
+            tensor.record_stream(launch)
+
     def workspace(self, batch: int, t: int):
         import torch
         need = B.whisper_enc_workspace_bytes(batch, t, self.d_model, self.heads, self.ffn_dim,
@@ -74,9 +94,11 @@ class EncoderStack:
         if y is None:
             y = torch.empty_like(x)
         ws = self.workspace(batch, t)
+        launch = self._launch_stream(stream)
+        self._keep_for(ws, launch)
         g, b = (self.ln_post if (final_norm and self.ln_post is not None) else (None, None))
         B.whisper_enc_stack_forward(x, y, self.blob, n, g, b, batch, t, self.d_model, self.heads,
-                                    self.ffn_dim, self.path, ws, ws.numel(), stream)
+                                    self.ffn_dim, self.path, ws, ws.numel(), launch.cuda_stream)
         return y
 
 
@@ -90,8 +112,11 @@ class EncoderStack:
         lens = [int(n) for n in seqlens]
         assert sum(lens) == total and min(lens, default=0) >= 0
         max_t = max(lens, default=0)
-        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32),
-                          device=self.device)
+        launch = self._launch_stream(stream)
+        # The offsets are copied to the device on the launch stream and kept alive for it.
+        with torch.cuda.stream(launch):
+            cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32),
+                              device=self.device)
         n = self.n_layers if n_layers is None else n_layers
         if y is None:
             y = torch.empty_like(x)
@@ -101,10 +126,11 @@ class EncoderStack:
             raise B.WencError(B.WENC_ERR_ARG, "whisper_enc_varlen_workspace_bytes")
         if self._ws is None or self._ws.numel() < need:
             self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+        self._keep_for(self._ws, launch)
         g, b = (self.ln_post if (final_norm and self.ln_post is not None) else (None, None))
         B.whisper_enc_stack_forward_varlen(x, y, self.blob, n, g, b, cu, len(lens), total, max_t,
                                            self.d_model, self.heads, self.ffn_dim, self.path,
-                                           self._ws, self._ws.numel(), stream)
+                                           self._ws, self._ws.numel(), launch.cuda_stream)
         return y
 
 

@@ -49,7 +49,9 @@ def parse():
                     help="write profiles/hbm_traffic.json from two rocprofv3 counter CSVs")
     ap.add_argument("--pmc-command", default="", help="command line recorded with --ingest-pmc")
     ap.add_argument("--no-next-steps", action="store_true",
-                    help="skip timing the adjacent steps (cross-attention K/V precompute)")
+                    help="skip timing the adjacent steps (front end, cross K/V, ragged, q8/q4)")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip timing the other workloads and the fp32 path")
     return ap.parse_args()
 
 
@@ -457,30 +459,32 @@ def time_graph(path_name, reps):
     return out
 
 
-def time_one_window(path_name, reps, peak, mpeak, layers=4):
-    """The same large-v3 block at one 1500-position window (M = 1500 rows per GEMM, the shape of
-    the 32-block stack workload), timed as a stack call of `layers` blocks plus the final
-    LayerNorm: per-block time and the algorithmic TFLOP/s of the whole block beside the batched
-    figure.  Every block of that stack does the same work, so a few stand for the 32."""
+def time_config(name, path_name, reps, peak, mpeak):
+    """One whole workload as the C ABI call its name says (a block, or a stack of all its blocks
+    plus the final LayerNorm), timed with HIP events on the launch stream: ms per call, frames/s
+    and the algorithmic TFLOP/s of the call."""
     import torch
     from speech_transformer_encoder_amd import binding as B
     from speech_transformer_encoder_amd import synth
     from speech_transformer_encoder_amd.encoder import build_from_workload, to_device_input
-    cfg = synth.CONFIGS["large_v3_stack"].with_(n_layers=layers)
+    cfg = synth.CONFIGS[name]
     w = synth.make_workload(cfg)
     enc = build_from_workload(w, B.PATHS[path_name])
     x = to_device_input(w.x)
     y = torch.empty_like(x)
     enc.workspace(cfg.batch, cfg.t)
+    del w
     ms = time_events(lambda: enc.forward(x, y), reps, torch.cuda.current_stream())
     fl = cfg.flops()
     tf = fl["total"] / (ms * 1e-3) / 1e12
-    out = {"workload": "large_v3_one_window", "blocks_timed": layers, "final_layernorm": True,
-           "ms_per_block": round(ms / layers, 4),
-           "frames_per_s_32_blocks": round(cfg.t / (ms / layers * 32 * 1e-3), 1),
-           "tflops": round(tf, 1), "frac_peak": round(tf / peak, 4),
-           "frac_measured_peak": round(tf / mpeak, 4) if mpeak else None}
-    del enc
+    pk = PEAK_TFLOPS[path_name]
+    out = {"path": path_name, "blocks": cfg.n_layers, "batch_windows": cfg.batch,
+           "final_layernorm": cfg.ln_post, "ms": round(ms, 4),
+           "ms_per_block": round(ms / cfg.n_layers, 4),
+           "frames_per_s": round(cfg.batch * cfg.t / (ms * 1e-3), 1),
+           "tflops": round(tf, 1), "frac_peak": round(tf / pk, 4),
+           "frac_measured_peak": round(tf / mpeak, 4) if (mpeak and path_name != "fp32") else None}
+    del enc, x, y
     torch.cuda.empty_cache()
     return out
 
@@ -601,9 +605,16 @@ def main():
         roof["measured_peak"] = mpeak
         roof["frac_measured_peak"] = round(roof["achieved"] / mpeak, 4)
 
-    one_window = None
-    if cfg.batch > 1 and args.path != "fp32" and not args.no_next_steps:
-        one_window = time_one_window(args.path, args.kernel_reps, peak, mpeak)
+    # Every other workload, timed whole (the 32-block large-v3 stack as one call), on the same
+    # operand type; and the fp32 fallback path on the bench workload itself.
+    configs = {}
+    if not args.no_other_configs:
+        for name in synth.CONFIGS:
+            if name != cfg.name:
+                configs[name] = time_config(name, args.path, args.kernel_reps, peak, mpeak)
+        if args.path != "fp32":
+            configs[cfg.name + "/fp32"] = time_config(cfg.name, "fp32", max(3, args.kernel_reps // 3),
+                                                      PEAK_TFLOPS["fp32"], None)
 
     next_steps = {}
     if not args.no_next_steps:
@@ -636,7 +647,7 @@ def main():
                    "gemm_frac_measured_peak": round(gemm_tf / mpeak, 4) if mpeak else None,
                    "attention_frac_measured_peak": round(attn_tf / mpeak, 4) if mpeak else None},
         "mfma_peak_measured": measured,
-        "one_window": one_window,
+        "configs": configs,
         "roofline": roof,
         "kernels": kern,
         "wall_s_timed": round(wall, 4),

@@ -91,7 +91,10 @@ extern "C" {
 #define WENC_MAX_DEC_LAYERS 64
 #define WENC_MAX_MELS 1024
 
-/* Human-readable text of a status code (static storage; never NULL). */
+/* Human-readable text of a status code (static storage; never NULL).  The pages report
+ * errors as text (inferencelayer WhisperEncoderGpu::forward returns Result with ensure!
+ * messages; turbospark-runtime encode returns Result<(), String>); a C ABI returns the code and
+ * offers its text here. */
 const char* whisper_enc_strerror(int code);
 
 /*
@@ -122,6 +125,9 @@ int whisper_enc_pack_layer(const float* ln1_g, const float* ln1_b, const float* 
                            int ffn_dim, int path, void* dst_layer, void* stream);
 
 /*
+ * The intermediate buffers of one call (inferencelayer WhisperEncoderGpu::forward allocates
+ * them on every call; turbospark-runtime WhisperMetalEngine::new allocates the scratch for a full
+ * window once), here owned by the caller and sized by this call.
  * Workspace bytes a block/stack call needs for `batch` windows of `t` positions: the LN
  * output / attention output [batch*t, d] and the QKV / FFN hidden activations
  * [batch*t, max(3d, ffn)], in the path's operand type; on the Q8 / Q4 paths room for one

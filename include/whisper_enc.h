@@ -54,6 +54,15 @@ extern "C" {
 /* Arithmetic paths: the type of every matrix-multiply operand.  Accumulation, LayerNorm
  * statistics, softmax state and the residual stream are fp32 on every path.
  *   BF16 - bfloat16 MFMA operands (weights rounded to nearest even when packed);
+ *   BF16X2 - layer and stack calls only: bfloat16 weights and MFMA operands, with the LayerNorm
+ *     and GELU outputs (the QKV, fc1 and fc2 activations) carried as two bfloat16 numbers,
+ *     hi = bf16(v) and lo = bf16(v - hi), both multiplied by the same bf16 weight row, so those
+ *     projections see v to ~2^-17 instead of bf16's 2^-9 (twice the MFMA work on them); Q, K, V,
+ *     the probabilities and the attention output stay single bfloat16.  For bf16-valued weights;
+ *   BF16X3 - as BF16X2, with every weight also packed as a bf16 hi / lo pair (twice the blob):
+ *     the projections compute x_hi w_hi + x_lo w_hi + x_hi w_lo (dropping x_lo w_lo, ~2^-18;
+ *     three times the MFMA work; the out-projection x w_hi + x w_lo), for fp32 weights that bf16
+ *     storage would round;
  *   FP32 - fp32 operands and intermediates (fp32 MFMA), the fallback path;
  *   FP16 - IEEE half MFMA operands, same MFMA rate as BF16 with 3 more mantissa bits;
  *   Q8, Q4 - layer and stack calls only (every other entry point rejects them): the packed
@@ -71,6 +80,8 @@ extern "C" {
 #define WENC_PATH_FP16 2
 #define WENC_PATH_Q8 3
 #define WENC_PATH_Q4 4
+#define WENC_PATH_BF16X2 5
+#define WENC_PATH_BF16X3 6
 
 /* Element types of step-level outputs. */
 #define WENC_DTYPE_F32 0
@@ -176,8 +187,9 @@ int whisper_enc_stack_forward(const float* x, float* y, const void* layers, int 
  * hipMalloc).  The workspace is a static device array of WENC_NOALLOC_SCRATCH_BYTES per GPU,
  * held from the first call on that GPU until the process ends; the call itself allocates
  * nothing.  64 MiB hold the workspace of one 1500-position window of every Whisper encoder size
- * (large-v3: 47.6 MiB on the 16-bit paths, 36.6 MiB on fp32, 85.1 MiB on Q8 / Q4, which is
- * rejected).  A shape whose whisper_enc_workspace_bytes() exceeds it returns WENC_ERR_SCRATCH
+ * on the BF16, FP16 and FP32 paths (large-v3: 47.6 MiB on the 16-bit paths, 36.6 MiB on fp32);
+ * larger ones (more windows; large-v3 on Q8 / Q4 with the fp16 copy of its weights, 85.1 MiB, or
+ * on BF16X2 / X3 with hi / lo activations) are rejected.  A shape whose whisper_enc_workspace_bytes() exceeds it returns WENC_ERR_SCRATCH
  * (having enqueued nothing).  The array of the current device is used (the stream must belong to
  * it), so calls that overlap on one GPU (other threads, or other streams) race on it: serialise
  * them.  Other arguments and the result are exactly those of whisper_enc_stack_forward.  The

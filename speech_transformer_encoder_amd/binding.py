@@ -32,6 +32,8 @@ WENC_PATH_FP32 = 1
 WENC_PATH_FP16 = 2
 WENC_PATH_Q8 = 3
 WENC_PATH_Q4 = 4
+WENC_PATH_BF16X2 = 5
+WENC_PATH_BF16X3 = 6
 PATHS = {"bf16": WENC_PATH_BF16, "fp32": WENC_PATH_FP32, "fp16": WENC_PATH_FP16}
 
 WENC_DTYPE_F32 = 0

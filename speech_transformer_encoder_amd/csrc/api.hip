@@ -29,18 +29,42 @@ int path_dtype(int path) {
   return -1;
 }
 
+// BF16X2 / BF16X3: bf16 MFMA operands; the LayerNorm and GELU outputs that feed the QKV, fc1 and
+// fc2 projections are bf16 hi / lo pairs, and on BF16X3 so are the weights.  Each projection then
+// runs over k segments (KMap): x_hi w + x_lo w (X2); x_hi w_hi + x_lo w_hi + x_hi w_lo (X3; the
+// out-projection, whose input is single bf16, x w_hi + x w_lo).
+bool split_acts(int path) { return path == WENC_PATH_BF16X2 || path == WENC_PATH_BF16X3; }
+bool split_weights(int path) { return path == WENC_PATH_BF16X3; }
+int kmul(int path) { return split_acts(path) ? 2 : 1; }
+// k segments of a projection whose activation is a LayerNorm or GELU output (QKV, fc1, fc2) ...
+KMap kmap_split(int path, int kb) {
+  if (split_weights(path)) return KMap{kb, 3, 0b010, 0b100, 2 * kb};
+  if (split_acts(path)) return KMap{kb, 2, 0b10, 0, kb};
+  return KMap{kb, 1, 0, 0, kb};
+}
+// ... and of the out-projection, whose activation (the attention output) is single.
+KMap kmap_single(int path, int kb) {
+  if (split_weights(path)) return KMap{kb, 2, 0, 0b10, 2 * kb};
+  return KMap{kb, 1, 0, 0, kb};
+}
+
 size_t elem_bytes(int path) { return path == WENC_PATH_FP32 ? 4 : 2; }
+bool split_weights(int path);
 
 // Weight storage of the q8 / q4 paths (0 for the others); their activations are fp16.
 int quant_bits(int path) { return path == WENC_PATH_Q8 ? 8 : path == WENC_PATH_Q4 ? 4 : 0; }
 
 // Operand type of a block or stack: the step-level entry points take path_dtype (no q8 / q4).
-int layer_dtype(int path) { return quant_bits(path) ? DT_F16 : path_dtype(path); }
+int layer_dtype(int path) {
+  return quant_bits(path) ? DT_F16 : split_acts(path) ? DT_BF16 : path_dtype(path);
+}
+// Type of the LayerNorm outputs (the QKV and fc1 operands) of a block.
+int ln_dtype(int path) { return split_acts(path) ? DT_BF16X2 : layer_dtype(path); }
 
 // Bytes of one stored [n][k] matrix: codes (int8 or nibbles) for q8 / q4, else operand values.
 size_t matrix_bytes(size_t n, size_t k, int path) {
   const int bits = quant_bits(path);
-  return bits ? n * k * bits / 8 : n * k * elem_bytes(path);
+  return bits ? n * k * bits / 8 : n * k * elem_bytes(path) * (split_weights(path) ? 2 : 1);
 }
 size_t scale_bytes(size_t n, size_t k, int path) { return quant_bits(path) ? n * (k / 32) * 2 : 0; }
 
@@ -120,8 +144,9 @@ size_t dequant_bytes(int d, int f, int path) {
 // fp32 parts of the split-k residual GEMMs of a block (out-projection and fc2, both [M, d]).
 size_t split_bytes(size_t rows, int d, int f, int path) {
   const int dt = layer_dtype(path);
-  const int s = std::max(linear_split((int)rows, d, d, dt, EPI_BIAS_RESIDUAL),
-                         linear_split((int)rows, d, f, dt, EPI_BIAS_RESIDUAL));
+  const KMap ko = kmap_single(path, d), k2 = kmap_split(path, f);
+  const int s = std::max(linear_split((int)rows, d, ko.nseg * d, dt, EPI_BIAS_RESIDUAL),
+                         linear_split((int)rows, d, k2.nseg * f, dt, EPI_BIAS_RESIDUAL));
   return s > 1 ? round_up((size_t)s * rows * d * sizeof(float)) : 0;
 }
 
@@ -137,22 +162,29 @@ size_t scratch_bytes(int batch, int t, int heads, size_t rows, int d, int f, int
 }
 
 // rows: batch * t, or the packed rows of a ragged batch (t = its longest window).
+// Widths (elements per row) of the two activation regions: a holds the LayerNorm outputs (hi /
+// lo pairs on BF16X2) and the attention output; b the QKV projection and the FFN hidden layer.
+size_t width_a(int d, int path) { return (size_t)kmul(path) * d; }
+size_t width_b(int d, int f, int path) {
+  const size_t fh = (size_t)kmul(path) * f;
+  return 3 * (size_t)d > fh ? 3 * (size_t)d : fh;
+}
+
 size_t workspace_size(int batch, int t, int heads, size_t rows, int d, int f, int path) {
   const size_t es = elem_bytes(path);
-  const size_t wb = (size_t)(3 * d > f ? 3 * d : f);
-  return round_up(rows * d * es) + round_up(rows * wb * es) + dequant_bytes(d, f, path) +
-         scratch_bytes(batch, t, heads, rows, d, f, path);
+  return round_up(rows * width_a(d, path) * es) + round_up(rows * width_b(d, f, path) * es) +
+         dequant_bytes(d, f, path) + scratch_bytes(batch, t, heads, rows, d, f, path);
 }
 
 Workspace carve(void* ws, int batch, int t, int heads, size_t rows, int d, int f, int path) {
   Workspace w;
   const size_t es = elem_bytes(path);
-  const size_t wb = (size_t)(3 * d > f ? 3 * d : f);
+  const size_t wa = width_a(d, path), wb = width_b(d, f, path);
   char* p = static_cast<char*>(ws);
   w.a = p;
-  w.b = p + round_up(rows * d * es);
+  w.b = p + round_up(rows * wa * es);
   if (quant_bits(path)) {
-    char* q = p + round_up(rows * d * es) + round_up(rows * wb * es);
+    char* q = p + round_up(rows * wa * es) + round_up(rows * wb * es);
     w.wqkv = reinterpret_cast<uint16_t*>(q);
     q += round_up(2 * 3 * (size_t)d * d);
     w.wo = reinterpret_cast<uint16_t*>(q);
@@ -162,7 +194,7 @@ Workspace carve(void* ws, int batch, int t, int heads, size_t rows, int d, int f
     w.w2 = reinterpret_cast<uint16_t*>(q);
   }
   if (scratch_bytes(batch, t, heads, rows, d, f, path))
-    w.part = reinterpret_cast<float*>(p + round_up(rows * d * es) + round_up(rows * wb * es) +
+    w.part = reinterpret_cast<float*>(p + round_up(rows * wa * es) + round_up(rows * wb * es) +
                                       dequant_bytes(d, f, path));
   return w;
 }
@@ -206,26 +238,33 @@ int run_block(const float* x, float* y, const char* blob, int rows, int t, int b
     w2 = ws.w2;
   }
 
+  // BF16X2 / X3: the LayerNorm and GELU outputs are hi / lo pairs (rows of 2 d / 2 f), and each
+  // projection runs over its k segments (kmap_split / kmap_single).
+  const int lt = ln_dtype(path), km = kmul(path);
+  const KMap kq = kmap_split(path, d), ko = kmap_single(path, d), k1 = kmap_split(path, d),
+             k2 = kmap_split(path, f);
   if (!ln1_ready)
-    WENC_TRY(launch_layernorm(x, fp(L.ln1_g), fp(L.ln1_b), ws.a, rows, d, dt, st));
-  WENC_TRY(launch_linear(ws.a, d, wqkv, fp(L.bqkv), nullptr, qkv, 3 * d, rows, 3 * d, d, dt,
-                         EPI_BIAS, st));
+    WENC_TRY(launch_layernorm(x, fp(L.ln1_g), fp(L.ln1_b), ws.a, rows, d, lt, st));
+  WENC_TRY(launch_linear(ws.a, km * d, wqkv, fp(L.bqkv), nullptr, qkv, 3 * d, rows, 3 * d,
+                         kq.nseg * d, dt, EPI_BIAS, st, nullptr, nullptr, &kq));
   WENC_TRY(launch_attention(qkv, qkv + es * d, qkv + es * 2 * d, 3 * d, ws.a, d, batch, t, heads,
                             0.125f, dt, st, cu, rows, ws.part));
-  if (ws.part && linear_split(rows, d, d, dt, EPI_BIAS_RESIDUAL) > 1) {
-    const LnFuse ln2{fp(L.ln2_g), fp(L.ln2_b), ws.a, dt, true};
-    WENC_TRY(launch_linear(ws.a, d, wo, fp(L.bo), x, y, d, rows, d, d, dt, EPI_BIAS_RESIDUAL, st,
-                           ws.part, &ln2));
+  if (ws.part && linear_split(rows, d, ko.nseg * d, dt, EPI_BIAS_RESIDUAL) > 1) {
+    const LnFuse ln2{fp(L.ln2_g), fp(L.ln2_b), ws.a, lt, true};
+    WENC_TRY(launch_linear(ws.a, d, wo, fp(L.bo), x, y, d, rows, d, ko.nseg * d, dt,
+                           EPI_BIAS_RESIDUAL, st, ws.part, &ln2, &ko));
   } else {
-    WENC_TRY(launch_linear(ws.a, d, wo, fp(L.bo), x, y, d, rows, d, d, dt, EPI_BIAS_RESIDUAL, st,
-                           ws.part));
-    WENC_TRY(launch_layernorm(y, fp(L.ln2_g), fp(L.ln2_b), ws.a, rows, d, dt, st));
+    WENC_TRY(launch_linear(ws.a, d, wo, fp(L.bo), x, y, d, rows, d, ko.nseg * d, dt,
+                           EPI_BIAS_RESIDUAL, st, ws.part, nullptr, &ko));
+    WENC_TRY(launch_layernorm(y, fp(L.ln2_g), fp(L.ln2_b), ws.a, rows, d, lt, st));
   }
-  WENC_TRY(launch_linear(ws.a, d, w1, fp(L.b1), nullptr, ws.b, f, rows, f, d, dt, EPI_BIAS_GELU,
-                         st));
-  const bool fuse_next = next && ws.part && linear_split(rows, d, f, dt, EPI_BIAS_RESIDUAL) > 1;
-  WENC_TRY(launch_linear(ws.b, f, w2, fp(L.b2), y, y, d, rows, d, f, dt, EPI_BIAS_RESIDUAL, st,
-                         ws.part, fuse_next ? next : nullptr));
+  WENC_TRY(launch_linear(ws.a, km * d, w1, fp(L.b1), nullptr, ws.b, km * f, rows, f, k1.nseg * d,
+                         dt, km > 1 ? EPI_BIAS_GELU_X2 : EPI_BIAS_GELU, st, nullptr, nullptr,
+                         &k1));
+  const bool fuse_next =
+      next && ws.part && linear_split(rows, d, k2.nseg * f, dt, EPI_BIAS_RESIDUAL) > 1;
+  WENC_TRY(launch_linear(ws.b, km * f, w2, fp(L.b2), y, y, d, rows, d, k2.nseg * f, dt,
+                         EPI_BIAS_RESIDUAL, st, ws.part, fuse_next ? next : nullptr, &k2));
   *next_done = fuse_next;
   return WENC_OK;
 }
@@ -301,6 +340,16 @@ int whisper_enc_pack_layer(const float* ln1_g, const float* ln1_b, const float* 
     WENC_TRY(launch_quantize(w2, blob + L.w2, blob + L.s2, d, f, bits, st));
     return WENC_OK;
   }
+  if (split_weights(path)) {
+    // BF16X3: every row as a bf16 [hi | lo] pair (rows of 2 n_in)
+    WENC_TRY(launch_convert_split(wq, blob + L.wqkv, d, d, st));
+    WENC_TRY(launch_convert_split(wk, blob + L.wqkv + 2 * es * dd, d, d, st));
+    WENC_TRY(launch_convert_split(wv, blob + L.wqkv + 4 * es * dd, d, d, st));
+    WENC_TRY(launch_convert_split(wo, blob + L.wo, d, d, st));
+    WENC_TRY(launch_convert_split(w1, blob + L.w1, f, d, st));
+    WENC_TRY(launch_convert_split(w2, blob + L.w2, d, f, st));
+    return WENC_OK;
+  }
   WENC_TRY(launch_convert(wq, blob + L.wqkv, dd, dt, st));
   WENC_TRY(launch_convert(wk, blob + L.wqkv + es * dd, dd, dt, st));
   WENC_TRY(launch_convert(wv, blob + L.wqkv + es * 2 * dd, dd, dt, st));
@@ -363,7 +412,7 @@ int stack_impl(const float* x, float* y, const void* layers, int n_layers, const
     if (l + 1 < n_layers) {
       const char* nb = blob + lb;
       next = {reinterpret_cast<const float*>(nb + L.ln1_g),
-              reinterpret_cast<const float*>(nb + L.ln1_b), ws.a, dt, true};
+              reinterpret_cast<const float*>(nb + L.ln1_b), ws.a, ln_dtype(path), true};
     } else if (ln_post_g) {
       next = {ln_post_g, ln_post_b, y, DT_F32, false};
     }

@@ -72,6 +72,16 @@ __device__ __forceinline__ size_t headmajor_offset(int m, int n, int N, int T) {
   return ((size_t)((size_t)b * (N >> 6) + (n >> 6)) * T + i) * 64 + (n & 63);
 }
 
+// The low halves of eight values whose bf16 roundings (hi) are packed in w4: lo = bf16(v - hi),
+// v - hi exact in fp32.
+__device__ __forceinline__ u32x4 split_lo8(float4 v0, float4 v1, u32x4 w4) {
+  auto lo2 = [](float a, float b, uint32_t hw) {
+    return pack2<bf16_t>(a - __uint_as_float(hw << 16), b - __uint_as_float(hw & 0xffff0000u));
+  };
+  return u32x4{lo2(v0.x, v0.y, w4[0]), lo2(v0.z, v0.w, w4[1]), lo2(v1.x, v1.y, w4[2]),
+               lo2(v1.z, v1.w, w4[3])};
+}
+
 constexpr int G_N = 256, G_M = 256, G_K = 64;  // workgroup tile
 constexpr int G_WN = 4, G_WM = 2;              // wavefront grid: n x m
 constexpr int G_TN = G_N / G_WN, G_TM = G_M / G_WM;  // 64 x 128 per wavefront
@@ -100,14 +110,14 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
                                                              const float* __restrict__ bias,
                                                              const float* residual, void* C,
                                                              int ldc, int M, int N, int K,
-                                                             int tiles_lim) {
+                                                             int tiles_lim, KMap km) {
   constexpr bool kResidual = EPI == EPI_BIAS_RESIDUAL || EPI == EPI_BIAS_GELU_RESIDUAL;
   // Head-major rows scatter over windows (64-bit addresses): those stores stay plain, predicated
   // global stores, and the next tile waits for them.
   constexpr bool kBufferOut = EPI != EPI_BIAS_HEADMAJOR;
   // Vector-memory operations of one wavefront's epilogue: 4 row blocks x (8 residual loads + 8
   // stores), or 4 x 4 stores.
-  constexpr int kEpiOps = kResidual ? 64 : 16;
+  constexpr int kEpiOps = kResidual ? 64 : EPI == EPI_BIAS_GELU_X2 ? 32 : 16;
   __shared__ __attribute__((aligned(1024))) uint16_t s0[G_STAGE];
   __shared__ __attribute__((aligned(1024))) uint16_t s1[G_STAGE];
 
@@ -121,7 +131,10 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
   const int t_begin = (int)((long)tiles * xcd / 8), t_end = (int)((long)tiles * (xcd + 1) / 8);
   const int ntile = t_end - t_begin > j ? (t_end - t_begin - j + per_xcd - 1) / per_xcd : 0;
   if (ntile <= 0) return;
-  const int stepW = 64 * K * 2, stepX = 64 * lda * 2;
+  // km: k segments of km.kb (the bf16 hi / lo pairs of the BF16X2 / X3 paths; one segment
+  // otherwise); weight rows of km.wrow elements.
+  const int nkb = km.kb / G_K, kw = km.wrow;
+  const int stepW = 64 * kw * 2, stepX = 64 * lda * 2;
 
   int n0 = 0, m0 = 0;
   u32x4 rW, rX;
@@ -135,7 +148,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
     n0 = tn * G_N;
     m0 = tm * G_M;
     const int wrows = min(N - n0, G_N), xrows = min(M - m0, G_M);
-    rW = buffer_rsrc(W + (size_t)n0 * K, (uint32_t)(wrows * K * 2));
+    rW = buffer_rsrc(W + (size_t)n0 * kw, (uint32_t)(wrows * kw * 2));
     rX = buffer_rsrc(X + (size_t)m0 * lda, (uint32_t)(xrows * lda * 2));
   };
 
@@ -151,13 +164,15 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
     // writing row (l >> 3), slot (l & 7), which holds chunk slot ^ ((row >> 1) & 7).
     const int lrow = 8 * wave + (lane >> 3);
     const int lchunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
-    const int voW = lrow * K * 2 + lchunk * 16, voX = lrow * lda * 2 + lchunk * 16;
+    const int voW = lrow * kw * 2 + lchunk * 16, voX = lrow * lda * 2 + lchunk * 16;
     auto load_tile = [&](int kt, const uint16_t* st) {
-      const int ko = kt * (G_K * 2);
+      const int seg = (kt >= nkb) + (kt >= 2 * nkb), kk = kt - seg * nkb;
+      const int ko = (((km.xmask >> seg) & 1) * nkb + kk) * (G_K * 2);
+      const int kow = (((km.wmask >> seg) & 1) * nkb + kk) * (G_K * 2);
       const uint32_t base = lds_addr(st);
 #pragma unroll
       for (int i = 0; i < G_LPO; ++i)
-        lds_copy16(rW, base + (uint32_t)(i * G_WAVES + wave) * 1024u, voW + i * stepW + ko);
+        lds_copy16(rW, base + (uint32_t)(i * G_WAVES + wave) * 1024u, voW + i * stepW + kow);
 #pragma unroll
       for (int i = 0; i < G_LPO; ++i)
         lds_copy16(rX, base + (uint32_t)(G_N * G_K * 2) + (uint32_t)(i * G_WAVES + wave) * 1024u,
@@ -324,13 +339,18 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
           const int r = (lane >> 3) + 8 * q, c0 = 2 * (lane & 7);
           float4 v0 = *reinterpret_cast<const float4*>(ep + r * 64 + ((c0 ^ (r & 15)) << 2));
           float4 v1 = *reinterpret_cast<const float4*>(ep + r * 64 + (((c0 + 1) ^ (r & 15)) << 2));
-          if constexpr (EPI == EPI_BIAS_GELU) {
+          if constexpr (EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_X2) {
             v0 = make_float4(gelu_erf_as(v0.x), gelu_erf_as(v0.y), gelu_erf_as(v0.z), gelu_erf_as(v0.w));
             v1 = make_float4(gelu_erf_as(v1.x), gelu_erf_as(v1.y), gelu_erf_as(v1.z), gelu_erf_as(v1.w));
           }
           const u32x4 w4 = {pack2<T>(v0.x, v0.y), pack2<T>(v0.z, v0.w), pack2<T>(v1.x, v1.y),
                             pack2<T>(v1.z, v1.w)};
-          if constexpr (kBufferOut) {
+          if constexpr (EPI == EPI_BIAS_GELU_X2) {
+            // lo = bf16(v - hi) N columns to the right (ldc = 2 N)
+            const u32x4 l4 = split_lo8(v0, v1, w4);
+            __builtin_amdgcn_raw_buffer_store_b128(w4, rC, ((rb + r) * ldc + 4 * c0) * 2, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(l4, rC, ((rb + r) * ldc + N + 4 * c0) * 2, 0, 0);
+          } else if constexpr (kBufferOut) {
             __builtin_amdgcn_raw_buffer_store_b128(w4, rC, ((rb + r) * ldc + 4 * c0) * 2, 0, 0);
           } else {
             const int m = em0 + rb + r;
@@ -368,7 +388,7 @@ template <typename T, int EPI, int WM = H_WM, int HM = H_M>
 __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))) void gemm16_small_kernel(
     const uint16_t* __restrict__ X, int lda, const uint16_t* __restrict__ W,
     const float* __restrict__ bias, const float* residual, void* C, int ldc, int M, int N, int K,
-    int ksplit, int big0) {
+    int ksplit, int big0, KMap km) {
   constexpr int HW = H_WN * WM;                            // wavefronts
   constexpr int TM = HM / WM, NB = TM / 32;                // rows per wavefront, 32-row blocks
   constexpr int HLW = H_N / 16 / HW, HLX = HM / 16 / HW;   // 1 KB copies per wavefront and operand
@@ -415,20 +435,24 @@ __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))
   const int kc = K / ksplit, kbyte0 = part * kc * 2;  // this part's first k, in bytes
 
   const int wrows = min(N - n0, H_N), xrows = min(M - m0, HM);
-  const u32x4 rW = buffer_rsrc(W + (size_t)n0 * K, (uint32_t)(wrows * K * 2));
+  const int kw = km.wrow;  // weight row length (k segments: the BF16X2 / X3 hi / lo pairs)
+  const u32x4 rW = buffer_rsrc(W + (size_t)n0 * kw, (uint32_t)(wrows * kw * 2));
   const u32x4 rX = buffer_rsrc(X + (size_t)m0 * lda, (uint32_t)(xrows * lda * 2));
 
   // Copy i of wavefront w fills 1 KB block (i * HW + w) of its operand: 16 rows of 64 bytes,
   // lane l row (l >> 2), slot (l & 3) holding chunk slot ^ ((row >> 2) & 3).
   const int lrow = 16 * wave + (lane >> 2);
   const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
-  const int voW = lrow * K * 2 + lchunk * 16, voX = lrow * lda * 2 + lchunk * 16;
+  const int voW = lrow * kw * 2 + lchunk * 16, voX = lrow * lda * 2 + lchunk * 16;
   auto load_tile = [&](int kt, const uint16_t* st) {
-    const int ko = kbyte0 + kt * (H_K * 2);
+    const int ke = kbyte0 / 2 + kt * H_K;  // first k of the tile
+    const int seg = (ke >= km.kb) + (ke >= 2 * km.kb), kk = ke - seg * km.kb;
+    const int ko = (((km.xmask >> seg) & 1) * km.kb + kk) * 2;
+    const int kow = (((km.wmask >> seg) & 1) * km.kb + kk) * 2;
     const uint32_t base = lds_addr(st);
 #pragma unroll
     for (int i = 0; i < HLW; ++i)
-      lds_copy16(rW, base + (uint32_t)(i * HW + wave) * 1024u, voW + i * 16 * HW * K * 2 + ko);
+      lds_copy16(rW, base + (uint32_t)(i * HW + wave) * 1024u, voW + i * 16 * HW * kw * 2 + kow);
 #pragma unroll
     for (int i = 0; i < HLX; ++i)
       lds_copy16(rX, base + H_N * 64 + (uint32_t)(i * HW + wave) * 1024u,
@@ -562,7 +586,7 @@ __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))
         const int m = mb + r;
         float4 v0 = *reinterpret_cast<const float4*>(ep + r * 64 + ((c0 ^ (r & 15)) << 2));
         float4 v1 = *reinterpret_cast<const float4*>(ep + r * 64 + (((c0 + 1) ^ (r & 15)) << 2));
-        if constexpr (EPI == EPI_BIAS_GELU) {
+        if constexpr (EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_X2) {
           v0 = make_float4(gelu_erf_as(v0.x), gelu_erf_as(v0.y), gelu_erf_as(v0.z), gelu_erf_as(v0.w));
           v1 = make_float4(gelu_erf_as(v1.x), gelu_erf_as(v1.y), gelu_erf_as(v1.z), gelu_erf_as(v1.w));
         }
@@ -571,6 +595,8 @@ __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))
           const size_t off = EPI == EPI_BIAS_HEADMAJOR ? headmajor_offset(m, nw + 4 * c0, N, ldc)
                                                        : (size_t)m * ldc + nw + 4 * c0;
           *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(C) + off) = w4;
+          if constexpr (EPI == EPI_BIAS_GELU_X2)
+            *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(C) + off + N) = split_lo8(v0, v1, w4);
         }
       }
     }
@@ -775,7 +801,7 @@ static int persistent_grid() {
 template <typename T, int EPI>
 static hipError_t launch16_epi(const uint16_t* X, int lda, const uint16_t* W, const float* bias,
                                const float* residual, void* c, int ldc, int m, int n, int k,
-                               hipStream_t st, float* partial, const LnFuse* ln) {
+                               hipStream_t st, float* partial, const LnFuse* ln, KMap kw) {
   const long tiles = (long)((m + G_M - 1) / G_M) * ((n + G_N - 1) / G_N);
   const long small = (long)((m + H_M - 1) / H_M) * ((n + H_N - 1) / H_N);
   int split_rows = H_M;
@@ -790,11 +816,11 @@ static hipError_t launch16_epi(const uint16_t* X, int lda, const uint16_t* W, co
       if (split_rows == 128)
         gemm16_small_kernel<T, EPI_PARTIAL, 4, 128><<<dim3((unsigned)(small2 * split)),
                                                        dim3(H_THREADS), 0, st>>>(
-            X, lda, W, bias, nullptr, partial, n, m, n, k, split, -1);
+            X, lda, W, bias, nullptr, partial, n, m, n, k, split, -1, kw);
       else
         gemm16_small_kernel<T, EPI_PARTIAL><<<dim3((unsigned)(small * split)), dim3(H_THREADS),
                                               0, st>>>(X, lda, W, bias, nullptr, partial, n, m, n,
-                                                       k, split, -1);
+                                                       k, split, -1, kw);
       if (ln)
         return launch_splitk_reduce_ln(partial, split, bias, residual,
                                        ln->keep_x ? static_cast<float*>(c) : nullptr, ln->gamma,
@@ -813,10 +839,10 @@ static hipError_t launch16_epi(const uint16_t* X, int lda, const uint16_t* W, co
     const long whole = tiles / grid * grid, tail = tiles - whole;
     const bool halves = tail > 0 && 2 * tail <= grid;
     gemm16_kernel<T, EPI><<<dim3((unsigned)grid), dim3(G_THREADS), 0, st>>>(
-        X, lda, W, bias, residual, c, ldc, m, n, k, (int)(halves ? whole : tiles));
+        X, lda, W, bias, residual, c, ldc, m, n, k, (int)(halves ? whole : tiles), kw);
     if (halves)
       gemm16_small_kernel<T, EPI><<<dim3((unsigned)(2 * tail)), dim3(H_THREADS), 0, st>>>(
-          X, lda, W, bias, residual, c, ldc, m, n, k, 1, (int)whole);
+          X, lda, W, bias, residual, c, ldc, m, n, k, 1, (int)whole, kw);
   } else if (2 * small < grid) {
     // Fewer 128 x 256 tiles than half the CUs: 128 x 128 tiles, eight wavefronts of 64 x 32, twice
     // as many workgroups.  Measured at M = 1500 (us, 128 x 256 -> 128 x 128 with four wavefronts
@@ -824,10 +850,10 @@ static hipError_t launch16_epi(const uint16_t* X, int lda, const uint16_t* W, co
     // d 512 QKV 10.7 -> 8.8 -> 7.5, fc1 14.0 -> 11.0 -> 9.7; d 768 QKV 14.4 -> 12.0 -> 11.0.  With
     // 144 tiles or more (d 768 fc1, d 1280) the 128 x 256 tiles stay as fast or faster.
     gemm16_small_kernel<T, EPI, 4, 128><<<dim3((unsigned)small2), dim3(H_THREADS), 0, st>>>(
-        X, lda, W, bias, residual, c, ldc, m, n, k, 1, -1);
+        X, lda, W, bias, residual, c, ldc, m, n, k, 1, -1, kw);
   } else {
     gemm16_small_kernel<T, EPI><<<dim3((unsigned)small), dim3(H_THREADS), 0, st>>>(
-        X, lda, W, bias, residual, c, ldc, m, n, k, 1, -1);
+        X, lda, W, bias, residual, c, ldc, m, n, k, 1, -1, kw);
   }
   return hipGetLastError();
 }
@@ -835,24 +861,30 @@ static hipError_t launch16_epi(const uint16_t* X, int lda, const uint16_t* W, co
 template <typename T>
 static hipError_t launch16(const void* a, int lda, const void* w, const float* bias,
                            const float* residual, void* c, int ldc, int m, int n, int k, int epi,
-                           hipStream_t st, float* partial, const LnFuse* ln) {
+                           hipStream_t st, float* partial, const LnFuse* ln, KMap kw) {
   auto X = static_cast<const uint16_t*>(a);
   auto W = static_cast<const uint16_t*>(w);
   switch (epi) {
     case EPI_BIAS:
-      return launch16_epi<T, EPI_BIAS>(X, lda, W, bias, residual, c, ldc, m, n, k, st, partial, ln);
+      return launch16_epi<T, EPI_BIAS>(X, lda, W, bias, residual, c, ldc, m, n, k, st, partial, ln,
+                                       kw);
     case EPI_BIAS_GELU:
       return launch16_epi<T, EPI_BIAS_GELU>(X, lda, W, bias, residual, c, ldc, m, n, k, st,
-                                            partial, ln);
+                                            partial, ln, kw);
     case EPI_BIAS_RESIDUAL:
       return launch16_epi<T, EPI_BIAS_RESIDUAL>(X, lda, W, bias, residual, c, ldc, m, n, k, st,
-                                                partial, ln);
+                                                partial, ln, kw);
     case EPI_BIAS_HEADMAJOR:
       return launch16_epi<T, EPI_BIAS_HEADMAJOR>(X, lda, W, bias, residual, c, ldc, m, n, k, st,
-                                                 partial, ln);
+                                                 partial, ln, kw);
     case EPI_BIAS_GELU_RESIDUAL:
       return launch16_epi<T, EPI_BIAS_GELU_RESIDUAL>(X, lda, W, bias, residual, c, ldc, m, n, k,
-                                                     st, partial, ln);
+                                                     st, partial, ln, kw);
+  }
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (epi == EPI_BIAS_GELU_X2)
+      return launch16_epi<T, EPI_BIAS_GELU_X2>(X, lda, W, bias, residual, c, ldc, m, n, k, st,
+                                               partial, ln, kw);
   }
   return hipErrorInvalidValue;
 }
@@ -890,15 +922,21 @@ static hipError_t launch32(const void* a, int lda, const void* w, const float* b
 
 hipError_t launch_linear(const void* a, int lda, const void* w, const float* bias,
                          const float* residual, void* c, int ldc, int m, int n, int k, int dtype,
-                         int epilogue, hipStream_t st, float* partial, const LnFuse* ln) {
+                         int epilogue, hipStream_t st, float* partial, const LnFuse* ln,
+                         const KMap* kmap) {
   if (m == 0) return hipSuccess;
+  const KMap kw = kmap ? *kmap : KMap{k, 1, 0, 0, k};
+  const bool plain = kw.nseg == 1 && kw.wrow == kw.kb && kw.xmask == 0 && kw.wmask == 0;
+  if (kmap && (kw.nseg < 1 || kw.nseg > 3 || k != kw.nseg * kw.kb || kw.kb % G_K != 0 ||
+               (kw.wrow != kw.kb && kw.wrow != 2 * kw.kb) || (dtype == DT_F32 && !plain)))
+    return hipErrorInvalidValue;
   switch (dtype) {
     case DT_BF16:
       return launch16<bf16_t>(a, lda, w, bias, residual, c, ldc, m, n, k, epilogue, st, partial,
-                              ln);
+                              ln, kw);
     case DT_F16:
       return launch16<f16_t>(a, lda, w, bias, residual, c, ldc, m, n, k, epilogue, st, partial,
-                             ln);
+                             ln, kw);
     case DT_F32:
       if (ln) return hipErrorInvalidValue;
       return launch32(a, lda, w, bias, residual, c, ldc, m, n, k, epilogue, st);

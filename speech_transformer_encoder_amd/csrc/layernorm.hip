@@ -43,6 +43,20 @@ struct LnStore<NV, f16_t> {
   }
 };
 
+// bf16 hi / lo pair: row stride 2 d, hi in columns 0 .. d - 1, lo = bf16(v - hi) in d .. 2 d - 1.
+struct bf16x2_t {};
+template <int NV>
+struct LnStore<NV, bf16x2_t> {
+  static __device__ __forceinline__ void put(void* y, size_t row, int d, int c, float4 v) {
+    const float h0 = (float)(__bf16)v.x, h1 = (float)(__bf16)v.y, h2 = (float)(__bf16)v.z,
+                h3 = (float)(__bf16)v.w;
+    uint16_t* base = static_cast<uint16_t*>(y) + row * 2 * d + c;
+    *reinterpret_cast<u32x2*>(base) = u32x2{pack2<bf16_t>(h0, h1), pack2<bf16_t>(h2, h3)};
+    *reinterpret_cast<u32x2*>(base + d) =
+        u32x2{pack2<bf16_t>(v.x - h0, v.y - h1), pack2<bf16_t>(v.z - h2, v.w - h3)};
+  }
+};
+
 // Normalises one row held in a wavefront's registers (lane l has columns 4 (l + 64 j) .. + 3 in
 // v[j]; entries past d are ignored) and stores it as OutT.  Both the plain LayerNorm and the fused
 // split-k reduction below end in this routine, so they round identically.
@@ -213,6 +227,9 @@ hipError_t launch_splitk_reduce_ln(const float* part, int ksplit, const float* b
     case DT_F16:
       return launch_reduce_ln_t<f16_t>(part, ksplit, bias, residual, x_out, gamma, beta, y, rows,
                                        d, st);
+    case DT_BF16X2:
+      return launch_reduce_ln_t<bf16x2_t>(part, ksplit, bias, residual, x_out, gamma, beta, y,
+                                          rows, d, st);
   }
   return hipErrorInvalidValue;
 }
@@ -224,6 +241,7 @@ hipError_t launch_layernorm(const float* x, const float* g, const float* b, void
     case DT_F32: return launch_ln_t<float>(x, g, b, y, rows, d, st);
     case DT_BF16: return launch_ln_t<bf16_t>(x, g, b, y, rows, d, st);
     case DT_F16: return launch_ln_t<f16_t>(x, g, b, y, rows, d, st);
+    case DT_BF16X2: return launch_ln_t<bf16x2_t>(x, g, b, y, rows, d, st);
   }
   return hipErrorInvalidValue;
 }

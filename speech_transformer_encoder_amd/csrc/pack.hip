@@ -16,6 +16,19 @@ __global__ void convert16_kernel(const float* __restrict__ src, uint16_t* __rest
     dst[i] = (uint16_t)Cvt<T>::bits(src[i]);
 }
 
+// src [n][k] fp32 -> dst [n][2 k] bf16 rows [hi | lo], hi = bf16(v), lo = bf16(v - hi).
+__global__ void convert_split_kernel(const float* __restrict__ src, uint16_t* __restrict__ dst,
+                                     size_t n, int k) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n * k; i += stride) {
+    const size_t r = i / k, c = i - r * k;
+    const float v = src[i];
+    const float hi = (float)(__bf16)v;
+    dst[r * 2 * k + c] = (uint16_t)Cvt<bf16_t>::bits(hi);
+    dst[r * 2 * k + k + c] = (uint16_t)Cvt<bf16_t>::bits(v - hi);
+  }
+}
+
 __global__ void copy_or_zero_kernel(const float* __restrict__ src, float* __restrict__ dst,
                                     size_t n) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -44,6 +57,12 @@ hipError_t launch_convert(const float* src, void* dst, size_t n, int dtype, hipS
       break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_convert_split(const float* src, void* dst, size_t n, int k, hipStream_t st) {
+  if (n * k == 0) return hipSuccess;
+  convert_split_kernel<<<grid_for(n * k), 256, 0, st>>>(src, static_cast<uint16_t*>(dst), n, k);
   return hipGetLastError();
 }
 

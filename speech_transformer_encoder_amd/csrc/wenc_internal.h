@@ -8,17 +8,22 @@
 
 namespace wenc {
 
-enum DType { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+// DT_BF16X2: a value v carried as two bfloat16 numbers hi = bf16(v), lo = bf16(v - hi), a row of
+// d values stored as [hi_0 .. hi_{d-1} | lo_0 .. lo_{d-1}] (2 d elements); a GEMM whose k runs over
+// both halves while the weight row repeats computes w . hi + w . lo = w . v to ~2^-17.
+enum DType { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_BF16X2 = 3 };
 enum Epilogue {
   EPI_BIAS = 0,
   EPI_BIAS_GELU = 1,
   EPI_BIAS_RESIDUAL = 2,
   EPI_BIAS_HEADMAJOR = 3,
   EPI_BIAS_GELU_RESIDUAL = 4,
-  EPI_PARTIAL = 5  // split-k part: raw fp32 sums (no bias) to partial[split][m][n]
+  EPI_PARTIAL = 5,  // split-k part: raw fp32 sums (no bias) to partial[split][m][n]
+  EPI_BIAS_GELU_X2 = 6  // gelu_erf(. + bias) as a bf16 hi / lo pair: row m = [hi (n) | lo (n)]
 };
 
-// y[rows, d] = LayerNorm(x[rows, d]) * gamma + beta, stored as out_dtype.  d % 4 == 0, d <= 4096.
+// y[rows, d] = LayerNorm(x[rows, d]) * gamma + beta, stored as out_dtype (DT_BF16X2: rows of
+// 2 d, hi then lo).  d % 4 == 0, d <= 4096.
 hipError_t launch_layernorm(const float* x, const float* gamma, const float* beta, void* y,
                             int rows, int d, int out_dtype, hipStream_t st);
 
@@ -54,10 +59,20 @@ struct LnFuse {
 // kernel adds the parts in a fixed order (deterministic), then bias and residual.
 // ln: with a split EPI_BIAS_RESIDUAL GEMM (ldc == n), the second kernel also applies this
 // LayerNorm to the rows it forms (launch_splitk_reduce_ln); anything else with ln is an error.
+// How a GEMM's k range maps onto its operand rows when values are carried as bf16 hi / lo pairs:
+// k runs over nseg segments of kb elements; segment s reads the activation row's half
+// (xmask >> s) & 1 and the weight row's half (wmask >> s) & 1 (half 0: elements 0 .. kb - 1, half
+// 1: kb .. 2 kb - 1); a weight row holds wrow elements (kb, or 2 kb when it is a hi / lo pair).
+// E.g. x = hi + lo against one weight row: {kb, 2, 0b10, 0, kb}; both split, dropping lo . lo:
+// {kb, 3, 0b010, 0b100, 2 kb} (hi.hi + lo.hi + hi.lo).
+struct KMap {
+  int kb, nseg, xmask, wmask, wrow;
+};
+// kmap: nullptr for the plain contraction over k; else k == kmap->nseg * kmap->kb.
 hipError_t launch_linear(const void* a, int lda, const void* w, const float* bias,
                          const float* residual, void* c, int ldc, int m, int n, int k, int dtype,
                          int epilogue, hipStream_t st, float* partial = nullptr,
-                         const LnFuse* ln = nullptr);
+                         const LnFuse* ln = nullptr, const KMap* kmap = nullptr);
 // Number of k parts launch_linear uses with a partial buffer (1: none).  Fixed for a shape,
 // whatever the device, so that workspace sizes are too.
 int linear_split(int m, int n, int k, int dtype, int epilogue);
@@ -79,6 +94,8 @@ int attention_split(int batch, int t, int heads, int dtype);
 
 // dst[i] = round(src[i]) in dtype (or a copy for DT_F32); n elements.
 hipError_t launch_convert(const float* src, void* dst, size_t n, int dtype, hipStream_t st);
+// Rows of src [n][k] fp32 as bf16 hi / lo pairs: dst [n][2 k], row r = [bf16(v) | bf16(v - hi)].
+hipError_t launch_convert_split(const float* src, void* dst, size_t n, int k, hipStream_t st);
 // dst[i] = src ? src[i] : 0 for i < n (fp32).
 hipError_t launch_copy_or_zero(const float* src, float* dst, size_t n, hipStream_t st);
 

@@ -74,6 +74,27 @@ def test_workspace_follows_the_split_plans(lib):
         assert B.whisper_enc_workspace_bytes(1, 1500, d, h, f, P16) == act + 4 * 1500 * d * 4, d
 
 
+def test_bf16x2_path_sizes_and_validation(lib):
+    """BF16X2 packs the same bf16 blob as BF16; its workspace holds the hi / lo activation pairs
+    (LayerNorm outputs [M, 2d], FFN hidden [M, 2 ffn]); the step-level entry points reject it."""
+    P2, P1 = B.WENC_PATH_BF16X2, B.WENC_PATH_BF16
+    for d, f in [(384, 1536), (1280, 5120)]:
+        assert B.whisper_enc_layer_bytes(d, f, P2) == B.whisper_enc_layer_bytes(d, f, P1)
+    M, d, h, f = 16 * 1500, 1280, 20, 5120
+    assert B.whisper_enc_workspace_bytes(16, 1500, d, h, f, P2) >= M * (2 * d + 2 * f) * 2
+    assert B.whisper_enc_workspace_bytes(16, 1500, d, h, f, P2) > \
+        B.whisper_enc_workspace_bytes(16, 1500, d, h, f, P1)
+    assert lib.whisper_enc_linear(FAKE, FAKE, FAKE, None, FAKE, 64, 64, 64, P2,
+                                  B.WENC_EPI_BIAS, None) == B.WENC_ERR_ARG
+    assert lib.whisper_enc_attention(FAKE, FAKE, FAKE, FAKE, 1, 64, 1, 192, 64, P2,
+                                     None) == B.WENC_ERR_ARG
+    # BF16X3: the blob holds every weight as a hi / lo pair
+    P3 = B.WENC_PATH_BF16X3
+    weights = 4 * d * d + 2 * d * f
+    assert B.whisper_enc_layer_bytes(d, f, P3) >= B.whisper_enc_layer_bytes(d, f, P1) + 2 * weights
+    assert B.whisper_enc_workspace_bytes(1, 1500, 1280, 20, 5120, 7) == 0
+
+
 def test_strerror(lib):
     for code in range(6):
         assert B.strerror(code)

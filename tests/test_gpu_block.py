@@ -10,12 +10,17 @@ Acceptance: fp32 path max relative error <= 1e-4; 16-bit paths max relative erro
 mean absolute error <= 1e-3.  The max relative error is taken per element and floored at the
 reference RMS (``oracle.max_rel_error``).
 
-The bf16 instantiation meets the max relative bound on every workload but, by arithmetic, not the
-MAE bound beyond one block: rounding each LayerNorm and GELU output to bf16 (2^-9 relative)
-before a projection leaves ~1e-3 of error per block in the residual stream, which grows with depth
-(1.4e-3 after 6 blocks, 2.8e-3 after 32), and the fp32 weights of the tiny and base workloads lose
-2^-9 more when stored as bf16.  Its MAE is held to 4e-3 there (a ceiling on that growth at 32
-blocks); fp16 operands (3 more mantissa bits, the same MFMA rate) meet both bounds everywhere.
+Paths that meet both 16-bit bounds: fp16 operands on every workload; BF16X3 (bf16 MFMA operands,
+weights and the LayerNorm / GELU outputs carried as bf16 hi + lo pairs) on every workload; BF16X2
+(only the activations split) on the workloads with bf16-valued weights (small, large-v3, batched),
+where its weights are exact -- on the fp32-weight base stack the bf16 rounding of the weights
+alone costs ~1e-3 (measured MAE 1.01e-3), which is what BF16X3 is for.  The literal bf16
+path does NOT meet MAE <= 1e-3 on the base, small, large-v3 and batched workloads: rounding each
+LayerNorm and GELU output to bf16 (2^-9 relative) before a projection leaves ~1e-3 of error per
+block in the residual stream, growing with depth (measured 1.4e-3 after 6 blocks, 2.8e-3 after 32;
+the fp32 weights of the tiny and base workloads lose 2^-9 more when stored as bf16).  Its tests
+there assert the max relative bound, print the MAE, and hold it under BF16_MAE_CEILING only to
+catch a regression of that known miss; the 1e-3 bar itself is asserted on fp16 and BF16X2.
 """
 
 import os
@@ -32,14 +37,19 @@ from tests.gpu_util import PATH_NAMES, errors, host, report, require_gpu
 pytestmark = pytest.mark.gpu
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-PATHS = [B.WENC_PATH_BF16, B.WENC_PATH_FP16, B.WENC_PATH_FP32]
+PATHS = [B.WENC_PATH_BF16, B.WENC_PATH_FP16, B.WENC_PATH_FP32, B.WENC_PATH_BF16X2,
+         B.WENC_PATH_BF16X3]
+# BF16X2 is the path for bf16-valued weights: its full-workload checks run where they are.
+FULL_CASES = [(name, path) for name in synth.CONFIGS for path in PATHS
+              if not (path == B.WENC_PATH_BF16X2 and not synth.CONFIGS[name].bf16_weights)]
+BF16_MAE_CEILING = 4e-3  # regression guard on literal bf16's measured MAE miss (not the bar)
 
 
 def tolerance(path, name=None):
     if path == B.WENC_PATH_FP32:
         return {"max_rel": 1e-4, "mae": None}
     if path == B.WENC_PATH_BF16 and name not in (None, "tiny_block"):
-        return {"max_rel": 2e-2, "mae": 4e-3}
+        return {"max_rel": 2e-2, "mae": BF16_MAE_CEILING}
     return {"max_rel": 2e-2, "mae": 1e-3}
 
 
@@ -172,7 +182,8 @@ def test_window_alone_vs_batched_large_v3():
     report("large-v3 window alone vs batched (mutual)", errors(alone, batched))
 
 
-@pytest.mark.parametrize("path", [B.WENC_PATH_BF16, B.WENC_PATH_FP16, B.WENC_PATH_Q8])
+@pytest.mark.parametrize("path", [B.WENC_PATH_BF16, B.WENC_PATH_FP16, B.WENC_PATH_Q8,
+                                  B.WENC_PATH_BF16X2, B.WENC_PATH_BF16X3])
 def test_stack_equals_chained_blocks(path):
     """A stack call is bit-identical to one block call per layer followed by the final LayerNorm.
 
@@ -242,8 +253,7 @@ def _sampled_block_rows(w, per_window=8):
     return idx, np.concatenate(refs)
 
 
-@pytest.mark.parametrize("path", PATHS)
-@pytest.mark.parametrize("name", list(synth.CONFIGS))
+@pytest.mark.parametrize("name,path", FULL_CASES)
 def test_full_config(name, path):
     cfg = synth.CONFIGS[name]
     w = synth.make_workload(cfg)

@@ -8,6 +8,10 @@ oracle, through the C ABI.
 * Blocks and stacks on the Q8 / Q4 paths against the oracle run on the dequantised weights
   (``oracle.quantized_layer``): the remaining error is the fp16 path's (weights rounded to fp16,
   16-bit activations), so the bar is the block's (max_rel 2e-2, MAE 1e-3).
+* Each block call expands its layer's codes with the kernel behind
+  ``whisper_enc_dequantize_matrix`` and runs the fp16 GEMMs: a Q8 / Q4 stack equals, bit for bit,
+  the fp16 stack on the weights that entry point expands, at one window (split-k parts on the
+  small kernel) and for three batched windows (the persistent kernel).
 """
 
 import numpy as np
@@ -141,3 +145,41 @@ def test_block_quantized_large_v3_batch16(bits):
         rows = np.unique(np.concatenate([[0, cfg.t - 1], r.choice(cfg.t, 6, replace=False)]))
         ref = oracle.encoder_block_rows(w.x[b], p, cfg.heads, rows)
         _check(errors(got[b, rows], ref), f"block q{bits} large window {b}")
+
+
+def _expanded_layers(layers, bits):
+    """Each matrix quantised and expanded back to fp16 by the library's codec (the values the
+    Q8 / Q4 GEMMs multiply), as fp32 arrays in PyTorch layout."""
+    import torch
+    out = []
+    for p in layers:
+        q = dict(p)
+        for name in ("wq", "wk", "wv", "wo", "w1", "w2"):
+            n, k = p[name].shape
+            _, _, codes, scales = _gpu_quantize(p[name], bits)
+            e = torch.empty((n, k), dtype=torch.float16, device="cuda")
+            B.whisper_enc_dequantize_matrix(codes, scales, e, n, k, bits)
+            q[name] = host(e).astype(np.float32)
+        out.append(q)
+    return out
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("name,over", [("base_stack", {"n_layers": 2}),
+                                       ("large_v3_stack", {"n_layers": 1}),
+                                       ("large_v3_batch16_block", {"batch": 3})])
+def test_quantized_equals_fp16_on_expanded_weights(bits, name, over):
+    """Bit-identical to the fp16 path on the expanded weights.  base at one window: out-projection
+    and fc2 as split-k parts with the fused LayerNorms; large-v3 at one window: QKV, fc1 on the
+    128 x 256 tiles, fc2 in 4 parts; three large-v3 windows: 4500 rows on the persistent kernel."""
+    from speech_transformer_encoder_amd.encoder import EncoderStack
+    cfg = synth.CONFIGS[name].with_(**over)
+    w = synth.make_workload(cfg)
+    print(f"[case] q{bits} vs fp16 on expanded weights: {name} {over}", flush=True)
+    x = to_device_input(w.x)
+    got = host(build_from_workload(w, QPATHS[bits]).forward(x))
+    enc16 = EncoderStack(_expanded_layers(w.layers, bits), cfg.d_model, cfg.heads, cfg.ffn_dim,
+                         B.WENC_PATH_FP16, w.ln_post)
+    ref = host(enc16.forward(x))
+    assert np.isfinite(got).all()
+    np.testing.assert_array_equal(got, ref)

@@ -208,37 +208,45 @@ def attention_split_kv(q, k, v, heads: int, chunks: int) -> np.ndarray:
     return _merge_heads(out)
 
 
-def _window_block(x: np.ndarray, p: Dict[str, Optional[np.ndarray]], heads: int) -> np.ndarray:
-    """One pre-LN block on one window ``x [t, d]`` (float64 in, float64 out)."""
-    a = layer_norm(x, p["ln1_g"], p["ln1_b"])
+def _same(a):
+    return a
+
+
+def _window_block(x: np.ndarray, p: Dict[str, Optional[np.ndarray]], heads: int,
+                  act=None) -> np.ndarray:
+    """One pre-LN block on one window ``x [t, d]`` (float64 in, float64 out).  ``act``, when
+    given, replaces the operands of the QKV, fc1 and fc2 products (the LayerNorm outputs and the
+    GELU output) by ``act(operand)`` (``mx_values`` for the MXFP8 form)."""
+    act = act or _same
+    a = act(layer_norm(x, p["ln1_g"], p["ln1_b"]))
     q = linear(a, p["wq"], p["bq"])
     k = linear(a, p["wk"], p.get("bk"))
     v = linear(a, p["wv"], p["bv"])
     o = attention_online(q, k, v, heads)
     x1 = x + linear(o, p["wo"], p["bo"])
-    a2 = layer_norm(x1, p["ln2_g"], p["ln2_b"])
-    hid = gelu_erf(linear(a2, p["w1"], p["b1"]))
+    a2 = act(layer_norm(x1, p["ln2_g"], p["ln2_b"]))
+    hid = act(gelu_erf(linear(a2, p["w1"], p["b1"])))
     return x1 + linear(hid, p["w2"], p["b2"])
 
 
-def encoder_block(x, p: Dict[str, Optional[np.ndarray]], heads: int) -> np.ndarray:
+def encoder_block(x, p: Dict[str, Optional[np.ndarray]], heads: int, act=None) -> np.ndarray:
     """Pre-LN encoder block over ``x`` of shape ``[t, d]`` or ``[batch, t, d]``.
 
     ``x += out(attn(LN1 x))`` then ``x += fc2(gelu(fc1(LN2 x)))``; each window attends only
-    within itself.
+    within itself.  ``act`` as in ``_window_block``.
     """
     x = _f64(x)
     if x.ndim == 2:
-        return _window_block(x, p, heads)
-    return np.stack([_window_block(w, p, heads) for w in x])
+        return _window_block(x, p, heads, act)
+    return np.stack([_window_block(w, p, heads, act) for w in x])
 
 
 def encoder_stack(x, layers: Sequence[Dict[str, Optional[np.ndarray]]], heads: int,
-                  ln_post=None) -> np.ndarray:
+                  ln_post=None, act=None) -> np.ndarray:
     """``len(layers)`` blocks in order, then the final LayerNorm when ``ln_post = (g, b)``."""
     h = _f64(x)
     for p in layers:
-        h = encoder_block(h, p, heads)
+        h = encoder_block(h, p, heads, act)
     if ln_post is not None:
         h = layer_norm(h, ln_post[0], ln_post[1])
     return h
@@ -264,23 +272,25 @@ def encoder_stack_varlen(x_rows, seqlens: Sequence[int],
 
 
 def encoder_block_rows(x_window, p: Dict[str, Optional[np.ndarray]], heads: int,
-                       rows: Sequence[int]) -> np.ndarray:
+                       rows: Sequence[int], act=None) -> np.ndarray:
     """Block output for the selected rows of one window ``[t, d]``.
 
     Same arithmetic as ``encoder_block`` applied to those rows only: every key and value of the
     window is still formed (attention reads all of them), but queries, the residual branch and the
-    FFN run for the selected rows.  Lets a test check sampled outputs of a large batch.
+    FFN run for the selected rows.  Lets a test check sampled outputs of a large batch.  ``act``
+    as in ``_window_block`` (it acts on each row on its own, so taking rows first is the same).
     """
+    act = act or _same
     x = _f64(x_window)
     rows = np.asarray(rows, dtype=np.int64)
-    a = layer_norm(x, p["ln1_g"], p["ln1_b"])
+    a = act(layer_norm(x, p["ln1_g"], p["ln1_b"]))
     k = linear(a, p["wk"], p.get("bk"))
     v = linear(a, p["wv"], p["bv"])
     q = linear(a[rows], p["wq"], p["bq"])
     o = attention_online(q, k, v, heads)
     x1 = x[rows] + linear(o, p["wo"], p["bo"])
-    a2 = layer_norm(x1, p["ln2_g"], p["ln2_b"])
-    return x1 + linear(gelu_erf(linear(a2, p["w1"], p["b1"])), p["w2"], p["b2"])
+    a2 = act(layer_norm(x1, p["ln2_g"], p["ln2_b"]))
+    return x1 + linear(act(gelu_erf(linear(a2, p["w1"], p["b1"]))), p["w2"], p["b2"])
 
 
 def max_rel_error(got, ref) -> float:
@@ -423,4 +433,87 @@ def quantized_layer(p: Dict[str, Optional[np.ndarray]], bits: int) -> Dict[str, 
     out = dict(p)
     for name in QUANT_MATRICES:
         out[name] = deq(*quant(p[name]))
+    return out
+
+
+# ---------------------------------------------------------------- MXFP8 operands
+#
+# The block-scaled fp8 format of gfx950's scaled MFMA (OCP Microscaling Formats (MX) v1.0,
+# MXFP8 with E4M3 elements): blocks of 32 consecutive values along the contraction axis share one
+# power-of-two scale 2^X (an E8M0 byte X + 127), and each value is stored as an E4M3 number
+# (1 sign, 4 exponent bits with bias 7, 3 fraction bits; largest finite magnitude 448, smallest
+# normal 2^-6, subnormal quantum 2^-9) rounded to nearest, ties to even.  The pages do not use fp8;
+# this is the low-precision MFMA form of oxinfer's block-of-32 weights (Precision, make_lin), with
+# the activations quantised the same way because the MFMA takes both operands in the format.
+# Reading of the scale: X is the smallest integer with amax <= 448 2^X, so no element saturates
+# (the MX specification's floor(log2 amax) - 8 differs only when amax's significand exceeds 1.75,
+# where it clamps the block's largest elements to 448 2^X); an all-zero block takes X = -127.
+# Every step below is exact in float64 (powers of two and a rounding to a 4-bit significand).
+
+E4M3_MAX = 448.0
+MX_BLOCK = 32
+
+
+def e4m3_round(y) -> np.ndarray:
+    """Nearest E4M3 value (ties to even) of each |y| <= 448."""
+    y = _f64(y)
+    a = np.abs(y)
+    if np.any(a > E4M3_MAX):
+        raise ValueError("magnitude beyond E4M3's largest finite value")
+    _, ex = np.frexp(a)                       # a = f 2^ex, f in [0.5, 1)
+    e = np.maximum(ex - 1, -6).astype(np.float64)   # exponent of the leading bit; subnormals at -6
+    quantum = np.exp2(e - 3)
+    return np.copysign(np.round(a / quantum) * quantum, y)  # numpy rounds half to even
+
+
+def e4m3_bits(v) -> np.ndarray:
+    """Bit patterns (uint8) of E4M3 values ``v`` (as returned by ``e4m3_round``)."""
+    v = _f64(v)
+    a = np.abs(v)
+    _, ex = np.frexp(a)
+    normal = a >= 2.0 ** -6
+    e = np.where(normal, ex - 1, -6)
+    frac = np.where(normal, a / np.exp2(e) - 1.0, a / 2.0 ** -6) * 8.0
+    field = np.where(normal, e + 7, 0)
+    bits = (np.signbit(v).astype(np.int64) << 7) | (field.astype(np.int64) << 3) | frac.astype(np.int64)
+    return bits.astype(np.uint8)
+
+
+def mx_scale_exponent(amax) -> np.ndarray:
+    """Smallest integer X with ``amax <= 448 2^X`` (X = -127 for amax = 0), clipped to the E8M0
+    range [-127, 127]."""
+    amax = _f64(amax)
+    f, ex = np.frexp(amax)                    # amax = (2 f) 2^(ex - 1), 2 f in [1, 2)
+    x = ex - 9 + (2.0 * f > 1.75)             # 448 = 1.75 2^8
+    return np.clip(np.where(amax > 0, x, -127), -127, 127).astype(np.int64)
+
+
+def mx_quantize(a):
+    """MXFP8 blocks of 32 along the last axis (its length a multiple of 32).
+
+    Returns ``(values, X)``: the dequantised values (float64, ``e4m3 * 2^X``, same shape as ``a``)
+    and the scale exponents, shape ``a.shape[:-1] + (a.shape[-1] / 32,)``."""
+    a = _f64(a)
+    blocks = a.reshape(a.shape[:-1] + (-1, MX_BLOCK))
+    x = mx_scale_exponent(np.max(np.abs(blocks), axis=-1))
+    s = np.exp2(x.astype(np.float64))[..., None]
+    vals = e4m3_round(blocks / s) * s
+    return vals.reshape(a.shape), x
+
+
+def mx_values(a) -> np.ndarray:
+    """``a`` replaced by its MXFP8 values (blocks of 32 along the last axis)."""
+    return mx_quantize(a)[0]
+
+
+MX_MATRICES = ("wq", "wk", "wv", "w1", "w2")
+
+
+def mxfp8_layer(p: Dict[str, Optional[np.ndarray]]) -> Dict[str, Optional[np.ndarray]]:
+    """The block's parameters with the QKV, fc1 and fc2 matrices replaced by their MXFP8 values
+    (blocks of 32 input columns per output row); the output projection, norms and biases
+    unchanged."""
+    out = dict(p)
+    for name in MX_MATRICES:
+        out[name] = mx_values(p[name])
     return out

@@ -9,6 +9,10 @@ seeded recipe in ``speech_transformer_encoder_amd.synth`` on both sides.
 Each ``<config>_rows.npz`` holds ``rows`` (row indices into the single window) and ``y`` (the
 oracle's final output at those rows, float32), plus ``y_rms`` (RMS of the whole output) and
 ``pre_rows`` (the residual stream before the final LayerNorm at the same rows).
+``<config>_mxfp8_rows.npz`` holds the same rows of the oracle's MXFP8 form of the stack
+(``oracle.mxfp8_layer`` weights, ``act=oracle.mx_values`` on the QKV, fc1 and fc2 operands).
+
+    python tests/golden/make_golden.py --mxfp8 [config ...]
 """
 
 import os
@@ -49,6 +53,23 @@ def make(name: str) -> str:
     return out
 
 
+def make_mx(name: str) -> str:
+    cfg = synth.CONFIGS[name]
+    assert cfg.batch == 1
+    w = synth.make_workload(cfg)
+    t0 = time.time()
+    layers = [oracle.mxfp8_layer(p) for p in w.layers]
+    y = oracle.encoder_stack(w.x[0], layers, cfg.heads, w.ln_post, act=oracle.mx_values)
+    rows = sample_rows(cfg.t, cfg.seed)
+    out = os.path.join(HERE, f"{name}_mxfp8_rows.npz")
+    np.savez_compressed(out, rows=rows, y=y[rows].astype(np.float32))
+    print(f"{name} (MXFP8): oracle {time.time() - t0:.1f} s -> {out}", flush=True)
+    return out
+
+
 if __name__ == "__main__":
-    for n in (sys.argv[1:] or ["small_stack", "large_v3_stack"]):
-        make(n)
+    args = sys.argv[1:]
+    mx = "--mxfp8" in args
+    names = [a for a in args if a != "--mxfp8"] or ["small_stack", "large_v3_stack"]
+    for n in names:
+        (make_mx if mx else make)(n)

@@ -413,8 +413,8 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
     elif mutation == "drop_residual":
         real_block = orc._window_block
 
-        def blk(x, p, heads):
-            return real_block(x, p, heads) - x
+        def blk(x, p, heads, act=None):
+            return real_block(x, p, heads, act) - x
         monkeypatch.setattr(orc, "_window_block", blk)
     assert _hf_check() > 1e-6
 
@@ -684,3 +684,114 @@ def test_planted_quantizer_mistakes_are_caught(monkeypatch, mutation):
         plant("dequantize_q4", lambda c, s: real_dq4(c, s) + s.astype(np.float64).repeat(32, axis=1))
     assert not _quant_pins_hold()
     del real_q8, real_q4
+
+
+# ---------------------------------------------------------------- MXFP8 (E4M3 values, E8M0 scales)
+
+
+def _e4m3_table():
+    """Every finite E4M3 value, decoded by torch's float8_e4m3fn (an implementation independent of
+    the oracle): codes 0 .. 126 and 128 .. 254 (0x7f and 0xff are NaN)."""
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    vals = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return codes, vals
+
+
+def test_e4m3_round_matches_torch_and_round_trips():
+    """On float32 inputs of every magnitude up to 448, the oracle's rounding equals torch's
+    float8_e4m3fn cast (value and bit pattern); every finite E4M3 value rounds to itself."""
+    rng = np.random.default_rng(41)
+    y = (rng.standard_normal(200_000) * np.exp2(rng.integers(-14, 9, 200_000))).astype(np.float32)
+    y = y[np.abs(y) <= 448]
+    t = torch.from_numpy(y.copy()).to(torch.float8_e4m3fn)
+    r = orc.e4m3_round(y.astype(np.float64))
+    np.testing.assert_array_equal(r, t.to(torch.float64).numpy())
+    np.testing.assert_array_equal(orc.e4m3_bits(r), t.view(torch.uint8).numpy())
+    codes, vals = _e4m3_table()
+    np.testing.assert_array_equal(orc.e4m3_round(vals), vals)
+    np.testing.assert_array_equal(orc.e4m3_bits(vals), codes)
+
+
+def test_e4m3_ties_go_to_the_even_code():
+    """The midpoint of two neighbouring non-negative values rounds to the one whose code is even."""
+    codes, vals = _e4m3_table()
+    pos = vals[codes < 0x80]
+    pc = codes[codes < 0x80]
+    order = np.argsort(pos)
+    pos, pc = pos[order], pc[order]
+    mid = (pos[:-1] + pos[1:]) / 2
+    got = orc.e4m3_bits(orc.e4m3_round(mid))
+    want = np.where(pc[:-1] % 2 == 0, pc[:-1], pc[1:])
+    np.testing.assert_array_equal(got, want)
+    with pytest.raises(ValueError):
+        orc.e4m3_round(np.array([448.5]))
+
+
+def test_mx_scale_exponent_closed_forms():
+    """X is the smallest integer with amax <= 448 2^X: 448 2^j -> j, just above -> j + 1,
+    2^j -> j - 8 (2^j <= 1.75 2^j), 1.75 2^j -> j - 8, zero -> -127, clipped to [-127, 127]."""
+    j = np.arange(-100, 100)
+    p = np.exp2(j.astype(np.float64))
+    np.testing.assert_array_equal(orc.mx_scale_exponent(448 * p), j)
+    np.testing.assert_array_equal(orc.mx_scale_exponent(np.nextafter(448 * p, np.inf)), j + 1)
+    np.testing.assert_array_equal(orc.mx_scale_exponent(p), j - 8)
+    np.testing.assert_array_equal(orc.mx_scale_exponent(1.75 * p), j - 8)
+    np.testing.assert_array_equal(orc.mx_scale_exponent(np.nextafter(1.75 * p, np.inf)), j - 7)
+    assert orc.mx_scale_exponent(np.array([0.0]))[0] == -127
+    assert orc.mx_scale_exponent(np.array([1e-300]))[0] == -127
+    assert orc.mx_scale_exponent(np.array([3e38]))[0] == 120
+
+
+def test_mx_quantize_is_the_nearest_scaled_value():
+    """Brute force over the 253 finite E4M3 values: each element becomes the nearest of
+    {value 2^X} (ties to the even code) with X its block's exponent, which is the smallest that
+    keeps the block's largest magnitude within 448 2^X; nothing saturates."""
+    codes, vals = _e4m3_table()
+    rng = np.random.default_rng(43)
+    a = rng.standard_normal((6, 64)) * np.exp2(rng.integers(-20, 20, (6, 1)))
+    a[0, :32] = 0.0
+    a[1, :32] *= 1e-3
+    a[2, 5] = 448.0 * 2.0 ** 3 * 1.0000001  # a largest magnitude just above a scale boundary
+    got, x = orc.mx_quantize(a)
+    assert x.shape == (6, 2)
+    for r in range(6):
+        for b in range(2):
+            blk = a[r, 32 * b:32 * b + 32]
+            amax = np.max(np.abs(blk))
+            X = int(x[r, b])
+            if amax == 0:
+                assert X == -127 and np.all(got[r, 32 * b:32 * b + 32] == 0)
+                continue
+            assert amax <= 448 * 2.0 ** X and amax > 448 * 2.0 ** (X - 1)
+            grid = vals * 2.0 ** X
+            for i, v in enumerate(blk):
+                dist = np.abs(grid - v)
+                best = np.flatnonzero(dist == dist.min())
+                cand = grid[best]
+                if len(set(cand)) > 1:  # a tie: the even code
+                    cand = grid[best[codes[best] % 2 == 0]]
+                assert got[r, 32 * b + i] == cand[0] or (v == 0 and got[r, 32 * b + i] == 0)
+
+
+def test_mxfp8_layer_and_block_operands():
+    """mxfp8_layer quantises Wq, Wk, Wv, W1 and W2 along their input columns and leaves the
+    out-projection, norms and biases alone; the block applies `act` to exactly three operands,
+    LN1(x) and LN2(x1) ([t, d]) and the GELU output ([t, f]), and an identity act changes
+    nothing."""
+    cfg = synth.CONFIGS["tiny_block"].with_(t=40)
+    w = synth.make_workload(cfg)
+    p = w.layers[0]
+    q = orc.mxfp8_layer(p)
+    for n in ("wq", "wk", "wv", "w1", "w2"):
+        np.testing.assert_array_equal(q[n], orc.mx_values(p[n]))
+        assert not np.array_equal(q[n], p[n])
+    for n in ("wo", "bo", "bq", "bv", "b1", "b2", "ln1_g", "ln2_b"):
+        np.testing.assert_array_equal(q[n], p[n])
+    seen = []
+
+    def act(a):
+        seen.append(a.shape)
+        return a
+    out = orc.encoder_block(w.x, p, cfg.heads, act=act)
+    assert seen == [(40, 384), (40, 384), (40, 1536)]
+    np.testing.assert_array_equal(out, orc.encoder_block(w.x, p, cfg.heads))

@@ -23,7 +23,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "encoder frames/sec per 1500-frame window + attention/GEMM TFLOP/s (% MFMA peak)"
-PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
+# Dense MFMA peaks of the operand types (MXFP8 runs at the fp8 rate; BF16X2 / X3 at bf16's).
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3, "bf16x2": 2500.0, "bf16x3": 2500.0,
+               "q8": 2500.0, "q4": 2500.0, "mxfp8": 5000.0}
 PEAK_HBM_GBS = 8000.0
 COLD_FLUSH_BYTES = 512 << 20  # twice the 256 MB Infinity Cache
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -37,8 +39,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="large_v3_batch16_block")
     ap.add_argument("--path", default="fp16", choices=["bf16", "fp16", "fp32"])
-    ap.add_argument("--compare-paths", default="bf16",
-                    help="comma-separated other paths timed the same way (reported, not value)")
+    ap.add_argument("--compare-paths", default="bf16,bf16x3,mxfp8",
+                    help="comma-separated other paths timed the same way (reported, not value): "
+                         "bf16, bf16x2, bf16x3, mxfp8, fp32")
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-windows", type=int, default=16)
@@ -156,6 +159,57 @@ def make_kernels(cfg, path_name):
                                                            B.WENC_EPI_BIAS_RESIDUAL), "mfma",
                               2.0 * M * d * f),
     }
+
+
+def mx_kernel_breakdown(cfg, reps):
+    """The MXFP8 path's own kernels at the workload's shapes: the LayerNorm writing MXFP8, and
+    the QKV, fc1 + GELU (MXFP8 out) and fc2 + residual projections on MXFP8 operands (operands
+    quantised on the GPU from random fp32).  Attention and the out-projection are the fp16
+    kernels.  Rates against the dense fp8 MFMA peak."""
+    import torch
+    from speech_transformer_encoder_amd import binding as B
+    M, d, f = cfg.batch * cfg.t, cfg.d_model, cfg.ffn_dim
+    g = torch.Generator(device="cuda").manual_seed(0)
+    rnd = lambda *s: torch.randn(*s, device="cuda", generator=g)  # noqa: E731
+
+    def mx(rows, k, scale=1.0):
+        out = torch.empty(B.whisper_enc_mx_bytes(rows, k), dtype=torch.uint8, device="cuda")
+        B.whisper_enc_mx_quantize(rnd(rows, k) * scale, out, rows, k)
+        return out
+    a, h = mx(M, d), mx(M, f)
+    wqkv, w1, w2 = mx(3 * d, d, 0.02), mx(f, d, 0.02), mx(d, f, 0.02)
+    x = rnd(M, d)
+    y = x.clone()
+    ones, zeros = torch.ones(d, device="cuda"), torch.zeros(d, device="cuda")
+    b3, bf = torch.zeros(3 * d, device="cuda"), torch.zeros(f, device="cuda")
+    qkv = torch.empty(M, 3 * d, dtype=torch.float16, device="cuda")
+    hid = torch.empty(B.whisper_enc_mx_bytes(M, f), dtype=torch.uint8, device="cuda")
+    ln_out = torch.empty(B.whisper_enc_mx_bytes(M, d), dtype=torch.uint8, device="cuda")
+    P = B.WENC_PATH_MXFP8
+    kernels = {
+        "ln": (lambda: B.whisper_enc_layernorm(x, ones, zeros, ln_out, M, d, B.WENC_DTYPE_MXFP8),
+               "hbm", M * d * 4 + B.whisper_enc_mx_bytes(M, d) + 2 * d * 4),
+        "gemm_qkv": (lambda: B.whisper_enc_linear(a, wqkv, b3, None, qkv, M, 3 * d, d, P,
+                                                  B.WENC_EPI_BIAS), "mfma", 2.0 * M * 3 * d * d),
+        "gemm_fc1_gelu": (lambda: B.whisper_enc_linear(a, w1, bf, None, hid, M, f, d, P,
+                                                       B.WENC_EPI_BIAS_GELU), "mfma", 2.0 * M * f * d),
+        "gemm_fc2_residual": (lambda: B.whisper_enc_linear(h, w2, zeros, y, y, M, d, f, P,
+                                                           B.WENC_EPI_BIAS_RESIDUAL), "mfma",
+                              2.0 * M * d * f),
+    }
+    st = torch.cuda.current_stream()
+    out = {}
+    for name, (fn, bound, work) in kernels.items():
+        ms = time_events(fn, reps, st)
+        if bound == "hbm":
+            ach, peak, unit = work / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+        else:
+            ach, peak, unit = work / (ms * 1e-3) / 1e12, PEAK_TFLOPS["mxfp8"], "TFLOP/s"
+        out[name] = {"ms": round(ms, 5), "achieved": round(ach, 1), "unit": unit, "peak": peak,
+                     "frac": round(ach / peak, 4)}
+    del a, h, wqkv, w1, w2, hid, ln_out, qkv
+    torch.cuda.empty_cache()
+    return out
 
 
 def mfma_peak(path_name):
@@ -573,6 +627,12 @@ def main():
     for pn in [p for p in args.compare_paths.split(",") if p and p != args.path]:
         oms, _ = time_forward(build_from_workload(w, B.PATHS[pn]))
         others[pn] = {"value": round(cfg.batch * cfg.t / (oms * 1e-3), 1), "ms_per_step": round(oms, 4)}
+        if pn == "mxfp8":
+            others[pn]["kernels"] = mx_kernel_breakdown(cfg, args.kernel_reps)
+            if not args.no_other_configs and cfg.name != "large_v3_stack":
+                others[pn]["large_v3_stack"] = time_config("large_v3_stack", "mxfp8",
+                                                           args.kernel_reps, PEAK_TFLOPS["mxfp8"],
+                                                           None)
     frames = cfg.batch * cfg.t
     flops = cfg.flops()
 

@@ -74,7 +74,18 @@ extern "C" {
  *       Q4: m = first element of largest magnitude, d = m / -8,
  *           code = min(15, floor(x / d + 8.5)) in [0, 15], value = (code - 8) * d;
  *     (fp32 arithmetic, x times the correctly rounded fp32 1 / d; d stored as fp16).  Each block
- *     call expands its layer's matrices to fp16 in the workspace and runs the FP16 path. */
+ *     call expands its layer's matrices to fp16 in the workspace and runs the FP16 path;
+ *   MXFP8 - gfx950's block-scaled fp8 arithmetic for oxinfer's blocks of 32 (Precision,
+ *     make_lin): the QKV, fc1 and fc2 projections run on MXFP8 operands (OCP Microscaling
+ *     Formats v1.0: E4M3 values, one power-of-two E8M0 scale 2^X per 32 consecutive input
+ *     columns of a row, X the smallest integer with amax <= 448 * 2^X, values rounded to nearest
+ *     even) with fp32 accumulation: their weights are quantised when packed, and their
+ *     activations (the two LayerNorm outputs and the GELU output) by the kernels that produce
+ *     them.  Attention and the out-projection stay FP16.  A different numerical method: the
+ *     operands carry 4 significant bits, so outputs differ from the fp32 model by about 1 % of
+ *     their RMS per block; it is not held to the FP16 path's error bounds.  Layer and stack
+ *     calls, whisper_enc_linear and whisper_enc_layernorm (WENC_DTYPE_MXFP8) accept it; the
+ *     attention, front-end and cross K/V calls do not. */
 #define WENC_PATH_BF16 0
 #define WENC_PATH_FP32 1
 #define WENC_PATH_FP16 2
@@ -82,11 +93,13 @@ extern "C" {
 #define WENC_PATH_Q4 4
 #define WENC_PATH_BF16X2 5
 #define WENC_PATH_BF16X3 6
+#define WENC_PATH_MXFP8 7
 
 /* Element types of step-level outputs. */
 #define WENC_DTYPE_F32 0
 #define WENC_DTYPE_BF16 1
 #define WENC_DTYPE_F16 2
+#define WENC_DTYPE_MXFP8 3 /* an MXFP8 matrix, laid out as whisper_enc_mx_quantize writes it */
 
 /* Projection epilogues (whisper_enc_linear). */
 #define WENC_EPI_BIAS 0          /* c = a w^T + bias                        (path dtype) */
@@ -206,7 +219,9 @@ int whisper_enc_stack_forward_noalloc(const float* x, float* y, const void* laye
 /*
  * y[rows, d] = (x - mean) / sqrt(var + 1e-5) * gamma + beta per row, two-pass biased variance
  * (inferencelayer LN_SRC).  x fp32; y in out_dtype (WENC_DTYPE_*); d % 64 == 0, 64 <= d <= 4096.
- * y == x is allowed only for WENC_DTYPE_F32.
+ * y may equal x for WENC_DTYPE_F32 and must not otherwise overlap it.  WENC_DTYPE_MXFP8 writes
+ * whisper_enc_mx_bytes(rows, d) bytes at y, each block of 32 columns scaled as
+ * whisper_enc_mx_quantize does.
  */
 int whisper_enc_layernorm(const float* x, const float* gamma, const float* beta, void* y,
                           int rows, int d, int out_dtype, void* stream);
@@ -217,7 +232,10 @@ int whisper_enc_layernorm(const float* x, const float* gamma, const float* beta,
  * in the operand type; WENC_EPI_BIAS_RESIDUAL writes fp32 c = residual + a w^T + bias and
  * WENC_EPI_BIAS_GELU_RESIDUAL fp32 c = residual + gelu_erf(a w^T + bias) (the conv front end's
  * second convolution plus positions), with residual [m, n] fp32 (c == residual allowed).
- * n % 64 == 0, k % 64 == 0.
+ * n % 64 == 0, k % 64 == 0.  WENC_PATH_MXFP8: a and w are MXFP8 matrices of m and n rows of k
+ * (whisper_enc_mx_quantize layout; m * k and n * k below 2^31, else WENC_ERR_UNSUPPORTED);
+ * WENC_EPI_BIAS writes fp16 c [m, n], WENC_EPI_BIAS_GELU an MXFP8 matrix of m rows of n
+ * (whisper_enc_mx_bytes(m, n) bytes at c).
  */
 int whisper_enc_linear(const void* a, const void* w, const float* bias, const float* residual,
                        void* c, int m, int n, int k, int path, int epilogue, void* stream);
@@ -250,6 +268,21 @@ int whisper_enc_quantize_matrix(const float* w, void* codes, void* scales, int n
  */
 int whisper_enc_dequantize_matrix(const void* codes, const void* scales, void* dst, int n, int k,
                                   int bits, void* stream);
+
+/*
+ * MXFP8 matrices (WENC_PATH_MXFP8).  A matrix of `rows` rows of k values (k % 32 == 0) is
+ * rows * k E4M3 codes (row-major, one byte each: sign, 4 exponent bits with bias 7, 3 fraction
+ * bits) followed, at byte offset rows * k rounded up to a multiple of 256, by k / 32 planes of
+ * rows rounded up to a multiple of 16 bytes: byte r of plane j is X + 127 for block j (columns
+ * 32 j .. 32 j + 31) of row r, whose values are code * 2^X.  whisper_enc_mx_bytes gives the total
+ * (0 for invalid sizes).  whisper_enc_mx_quantize writes the MXFP8 form of src [rows, k] (device
+ * fp32, 16-byte aligned, values finite) to dst (device, 16-byte aligned, whisper_enc_mx_bytes
+ * bytes, not overlapping src): X is the smallest integer with the block's largest magnitude
+ * <= 448 * 2^X (-127 for an all-zero block), and each code the E4M3 value nearest to v * 2^-X,
+ * ties to even; no value saturates.  Asynchronous on `stream`.
+ */
+size_t whisper_enc_mx_bytes(int rows, int k);
+int whisper_enc_mx_quantize(const float* src, void* dst, int rows, int k, void* stream);
 
 /* ---- Ragged batches: windows of different lengths packed back to back. ---- */
 

@@ -34,11 +34,15 @@ WENC_PATH_Q8 = 3
 WENC_PATH_Q4 = 4
 WENC_PATH_BF16X2 = 5
 WENC_PATH_BF16X3 = 6
-PATHS = {"bf16": WENC_PATH_BF16, "fp32": WENC_PATH_FP32, "fp16": WENC_PATH_FP16}
+WENC_PATH_MXFP8 = 7
+PATHS = {"bf16": WENC_PATH_BF16, "fp32": WENC_PATH_FP32, "fp16": WENC_PATH_FP16,
+         "q8": WENC_PATH_Q8, "q4": WENC_PATH_Q4, "bf16x2": WENC_PATH_BF16X2,
+         "bf16x3": WENC_PATH_BF16X3, "mxfp8": WENC_PATH_MXFP8}
 
 WENC_DTYPE_F32 = 0
 WENC_DTYPE_BF16 = 1
 WENC_DTYPE_F16 = 2
+WENC_DTYPE_MXFP8 = 3
 
 WENC_EPI_BIAS = 0
 WENC_EPI_BIAS_GELU = 1
@@ -65,7 +69,7 @@ EXPORTS = (
     "whisper_enc_stem_forward",
     "whisper_enc_varlen_workspace_bytes", "whisper_enc_stack_forward_varlen",
     "whisper_enc_attention_varlen", "whisper_enc_quantize_matrix", "whisper_enc_dequantize_matrix",
-    "whisper_enc_stack_forward_noalloc",
+    "whisper_enc_stack_forward_noalloc", "whisper_enc_mx_bytes", "whisper_enc_mx_quantize",
 )
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -112,6 +116,8 @@ def load() -> ctypes.CDLL:
         "whisper_enc_quantize_matrix": (I, [P, P, P, I, I, I, P]),
         "whisper_enc_dequantize_matrix": (I, [P, P, P, I, I, I, P]),
         "whisper_enc_stack_forward_noalloc": (I, [P, P, P, I, P, P, I, I, I, I, I, I, P]),
+        "whisper_enc_mx_bytes": (Z, [I, I]),
+        "whisper_enc_mx_quantize": (I, [P, P, I, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -285,6 +291,15 @@ def whisper_enc_attention_varlen(q, k, v, o, cu_seqlens, batch, total_rows, max_
 def whisper_enc_quantize_matrix(w, codes, scales, n, k, bits, stream=None) -> None:
     _check(load().whisper_enc_quantize_matrix(_ptr(w), _ptr(codes), _ptr(scales), n, k, bits,
                                               _stream(stream)), "whisper_enc_quantize_matrix")
+
+
+def whisper_enc_mx_bytes(rows, k) -> int:
+    return int(load().whisper_enc_mx_bytes(rows, k))
+
+
+def whisper_enc_mx_quantize(src, dst, rows, k, stream=None) -> None:
+    _check(load().whisper_enc_mx_quantize(_ptr(src), _ptr(dst), rows, k, _stream(stream)),
+           "whisper_enc_mx_quantize")
 
 
 def whisper_enc_dequantize_matrix(codes, scales, dst, n, k, bits, stream=None) -> None:

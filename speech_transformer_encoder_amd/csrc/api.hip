@@ -25,9 +25,17 @@ int path_dtype(int path) {
     case WENC_PATH_BF16: return DT_BF16;
     case WENC_PATH_FP16: return DT_F16;
     case WENC_PATH_FP32: return DT_F32;
+    case WENC_PATH_MXFP8: return DT_MX8;
   }
   return -1;
 }
+// Operand type of the steps that have no MXFP8 form (attention, the conv front end, cross K/V).
+int plain_dtype(int path) { return path == WENC_PATH_MXFP8 ? -1 : path_dtype(path); }
+
+// MXFP8: the QKV, fc1 and fc2 projections on MXFP8 operands (weights quantised at pack time, the
+// LayerNorm and GELU outputs by the kernels that produce them); attention and the
+// out-projection, whose input is the attention output, stay fp16.
+bool mx_path(int path) { return path == WENC_PATH_MXFP8; }
 
 // BF16X2 / BF16X3: bf16 MFMA operands; the LayerNorm and GELU outputs that feed the QKV, fc1 and
 // fc2 projections are bf16 hi / lo pairs, and on BF16X3 so are the weights.  Each projection then
@@ -49,7 +57,6 @@ KMap kmap_single(int path, int kb) {
 }
 
 size_t elem_bytes(int path) { return path == WENC_PATH_FP32 ? 4 : 2; }
-bool split_weights(int path);
 
 // Weight storage of the q8 / q4 paths (0 for the others); their activations are fp16.
 int quant_bits(int path) { return path == WENC_PATH_Q8 ? 8 : path == WENC_PATH_Q4 ? 4 : 0; }
@@ -60,10 +67,14 @@ int layer_dtype(int path) {
 }
 // Type of the LayerNorm outputs (the QKV and fc1 operands) of a block.
 int ln_dtype(int path) { return split_acts(path) ? DT_BF16X2 : layer_dtype(path); }
+// Operand type of attention and of the out-projection.
+int attn_dtype(int path) { return mx_path(path) ? DT_F16 : layer_dtype(path); }
 
-// Bytes of one stored [n][k] matrix: codes (int8 or nibbles) for q8 / q4, else operand values.
+// Bytes of one stored [n][k] matrix: codes (int8 or nibbles) for q8 / q4, codes and scale planes
+// for MXFP8, else operand values.
 size_t matrix_bytes(size_t n, size_t k, int path) {
   const int bits = quant_bits(path);
+  if (mx_path(path)) return mx_matrix_bytes(n, k);
   return bits ? n * k * bits / 8 : n * k * elem_bytes(path) * (split_weights(path) ? 2 : 1);
 }
 size_t scale_bytes(size_t n, size_t k, int path) { return quant_bits(path) ? n * (k / 32) * 2 : 0; }
@@ -94,7 +105,7 @@ LayerLayout layer_layout(int d, int f, int path) {
   L.b1 = take(4 * (size_t)f);
   L.b2 = take(4 * (size_t)d);
   L.wqkv = take(matrix_bytes(3 * (size_t)d, d, path));
-  L.wo = take(matrix_bytes(d, d, path));
+  L.wo = take(mx_path(path) ? 2 * (size_t)d * d : matrix_bytes(d, d, path));  // MXFP8: fp16
   L.w1 = take(matrix_bytes(f, d, path));
   L.w2 = take(matrix_bytes(d, f, path));
   L.sqkv = take(scale_bytes(3 * (size_t)d, d, path));
@@ -143,16 +154,16 @@ size_t dequant_bytes(int d, int f, int path) {
 
 // fp32 parts of the split-k residual GEMMs of a block (out-projection and fc2, both [M, d]).
 size_t split_bytes(size_t rows, int d, int f, int path) {
-  const int dt = layer_dtype(path);
   const KMap ko = kmap_single(path, d), k2 = kmap_split(path, f);
-  const int s = std::max(linear_split((int)rows, d, ko.nseg * d, dt, EPI_BIAS_RESIDUAL),
-                         linear_split((int)rows, d, k2.nseg * f, dt, EPI_BIAS_RESIDUAL));
+  const int s = std::max(
+      linear_split((int)rows, d, ko.nseg * d, attn_dtype(path), EPI_BIAS_RESIDUAL),
+      linear_split((int)rows, d, k2.nseg * f, layer_dtype(path), EPI_BIAS_RESIDUAL));
   return s > 1 ? round_up((size_t)s * rows * d * sizeof(float)) : 0;
 }
 
 // fp32 (O, m, l) of both key halves when attention splits its keys (few query blocks).
 size_t attn_split_bytes(int batch, int t, int heads, size_t rows, int path) {
-  if (attention_split(batch, t, heads, layer_dtype(path)) < 2) return 0;
+  if (attention_split(batch, t, heads, attn_dtype(path)) < 2) return 0;
   return round_up(2 * rows * (size_t)heads * 66 * sizeof(float));
 }
 
@@ -170,21 +181,30 @@ size_t width_b(int d, int f, int path) {
   return 3 * (size_t)d > fh ? 3 * (size_t)d : fh;
 }
 
+// Bytes of the two activation regions (MXFP8: also room for the MXFP8 LayerNorm output in a and
+// the MXFP8 hidden layer in b, which are at most a few scale planes larger than the fp16 ones).
+size_t region_a_bytes(size_t rows, int d, int path) {
+  const size_t b = round_up(rows * width_a(d, path) * elem_bytes(path));
+  return mx_path(path) ? std::max(b, mx_matrix_bytes(rows, d)) : b;
+}
+size_t region_b_bytes(size_t rows, int d, int f, int path) {
+  const size_t b = round_up(rows * width_b(d, f, path) * elem_bytes(path));
+  return mx_path(path) ? std::max(b, mx_matrix_bytes(rows, f)) : b;
+}
+
 size_t workspace_size(int batch, int t, int heads, size_t rows, int d, int f, int path) {
-  const size_t es = elem_bytes(path);
-  return round_up(rows * width_a(d, path) * es) + round_up(rows * width_b(d, f, path) * es) +
+  return region_a_bytes(rows, d, path) + region_b_bytes(rows, d, f, path) +
          dequant_bytes(d, f, path) + scratch_bytes(batch, t, heads, rows, d, f, path);
 }
 
 Workspace carve(void* ws, int batch, int t, int heads, size_t rows, int d, int f, int path) {
   Workspace w;
-  const size_t es = elem_bytes(path);
-  const size_t wa = width_a(d, path), wb = width_b(d, f, path);
+  const size_t ra = region_a_bytes(rows, d, path), rb = region_b_bytes(rows, d, f, path);
   char* p = static_cast<char*>(ws);
   w.a = p;
-  w.b = p + round_up(rows * wa * es);
+  w.b = p + ra;
   if (quant_bits(path)) {
-    char* q = p + round_up(rows * wa * es) + round_up(rows * wb * es);
+    char* q = p + ra + rb;
     w.wqkv = reinterpret_cast<uint16_t*>(q);
     q += round_up(2 * 3 * (size_t)d * d);
     w.wo = reinterpret_cast<uint16_t*>(q);
@@ -194,8 +214,7 @@ Workspace carve(void* ws, int batch, int t, int heads, size_t rows, int d, int f
     w.w2 = reinterpret_cast<uint16_t*>(q);
   }
   if (scratch_bytes(batch, t, heads, rows, d, f, path))
-    w.part = reinterpret_cast<float*>(p + round_up(rows * wa * es) + round_up(rows * wb * es) +
-                                      dequant_bytes(d, f, path));
+    w.part = reinterpret_cast<float*>(p + ra + rb + dequant_bytes(d, f, path));
   return w;
 }
 
@@ -214,7 +233,7 @@ int run_block(const float* x, float* y, const char* blob, int rows, int t, int b
               bool ln1_ready, const LnFuse* next, bool* next_done) {
   *next_done = false;
   const LayerLayout L = layer_layout(d, f, path);
-  const int dt = layer_dtype(path);
+  const int dt = layer_dtype(path), da = attn_dtype(path);  // projections fed by LN / GELU; the rest
   const size_t es = elem_bytes(path);
   auto fp = [&](size_t off) { return reinterpret_cast<const float*>(blob + off); };
   const void* wqkv = blob + L.wqkv;
@@ -248,13 +267,13 @@ int run_block(const float* x, float* y, const char* blob, int rows, int t, int b
   WENC_TRY(launch_linear(ws.a, km * d, wqkv, fp(L.bqkv), nullptr, qkv, 3 * d, rows, 3 * d,
                          kq.nseg * d, dt, EPI_BIAS, st, nullptr, nullptr, &kq));
   WENC_TRY(launch_attention(qkv, qkv + es * d, qkv + es * 2 * d, 3 * d, ws.a, d, batch, t, heads,
-                            0.125f, dt, st, cu, rows, ws.part));
-  if (ws.part && linear_split(rows, d, ko.nseg * d, dt, EPI_BIAS_RESIDUAL) > 1) {
+                            0.125f, da, st, cu, rows, ws.part));
+  if (ws.part && linear_split(rows, d, ko.nseg * d, da, EPI_BIAS_RESIDUAL) > 1) {
     const LnFuse ln2{fp(L.ln2_g), fp(L.ln2_b), ws.a, lt, true};
-    WENC_TRY(launch_linear(ws.a, d, wo, fp(L.bo), x, y, d, rows, d, ko.nseg * d, dt,
+    WENC_TRY(launch_linear(ws.a, d, wo, fp(L.bo), x, y, d, rows, d, ko.nseg * d, da,
                            EPI_BIAS_RESIDUAL, st, ws.part, &ln2, &ko));
   } else {
-    WENC_TRY(launch_linear(ws.a, d, wo, fp(L.bo), x, y, d, rows, d, ko.nseg * d, dt,
+    WENC_TRY(launch_linear(ws.a, d, wo, fp(L.bo), x, y, d, rows, d, ko.nseg * d, da,
                            EPI_BIAS_RESIDUAL, st, ws.part, nullptr, &ko));
     WENC_TRY(launch_layernorm(y, fp(L.ln2_g), fp(L.ln2_b), ws.a, rows, d, lt, st));
   }
@@ -267,6 +286,11 @@ int run_block(const float* x, float* y, const char* blob, int rows, int t, int b
                          EPI_BIAS_RESIDUAL, st, ws.part, fuse_next ? next : nullptr, &k2));
   *next_done = fuse_next;
   return WENC_OK;
+}
+
+bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  return pa < pb + bbytes && pb < pa + abytes;
 }
 
 bool overlaps_partially(const void* a, const void* b, size_t bytes) {
@@ -338,6 +362,17 @@ int whisper_enc_pack_layer(const float* ln1_g, const float* ln1_b, const float* 
     WENC_TRY(launch_quantize(wo, blob + L.wo, blob + L.so, d, d, bits, st));
     WENC_TRY(launch_quantize(w1, blob + L.w1, blob + L.s1, f, d, bits, st));
     WENC_TRY(launch_quantize(w2, blob + L.w2, blob + L.s2, d, f, bits, st));
+    return WENC_OK;
+  }
+  if (mx_path(path)) {
+    // MXFP8 codes and scale planes; Q, K and V fill rows 0, d and 2d of the fused [3d][d]; the
+    // out-projection in fp16.
+    for (int i = 0; i < 3; ++i)
+      WENC_TRY(launch_mx_quantize(i == 0 ? wq : i == 1 ? wk : wv, blob + L.wqkv, d, d, i * d, 3 * d,
+                                  st));
+    WENC_TRY(launch_convert(wo, blob + L.wo, dd, DT_F16, st));
+    WENC_TRY(launch_mx_quantize(w1, blob + L.w1, f, d, 0, f, st));
+    WENC_TRY(launch_mx_quantize(w2, blob + L.w2, d, f, 0, d, st));
     return WENC_OK;
   }
   if (split_weights(path)) {
@@ -552,17 +587,26 @@ int whisper_enc_layernorm(const float* x, const float* gamma, const float* beta,
                           int rows, int d, int out_dtype, void* stream) {
   if (rows < 0 || rows > WENC_MAX_ROWS) return WENC_ERR_ARG;
   if (d < 64 || d > WENC_MAX_D_MODEL || d % 64 != 0) return WENC_ERR_ARG;
-  if (out_dtype != WENC_DTYPE_F32 && out_dtype != WENC_DTYPE_BF16 && out_dtype != WENC_DTYPE_F16)
+  if (out_dtype != WENC_DTYPE_F32 && out_dtype != WENC_DTYPE_BF16 && out_dtype != WENC_DTYPE_F16 &&
+      out_dtype != WENC_DTYPE_MXFP8)
     return WENC_ERR_ARG;
   if (rows == 0) return WENC_OK;
   if (!x || !gamma || !beta || !y) return WENC_ERR_ARG;
   if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(beta, 16) || !aligned(y, 16))
     return WENC_ERR_ARG;
-  if (out_dtype != WENC_DTYPE_F32 &&
-      overlaps_partially(x, y, (size_t)rows * d * sizeof(float)))
-    return WENC_ERR_ARG;
-  if (out_dtype != WENC_DTYPE_F32 && x == (const void*)y) return WENC_ERR_ARG;
-  const int dt = out_dtype == WENC_DTYPE_F32 ? DT_F32 : out_dtype == WENC_DTYPE_BF16 ? DT_BF16 : DT_F16;
+  const size_t xbytes = (size_t)rows * d * sizeof(float);
+  if (out_dtype == WENC_DTYPE_F32) {
+    if (overlaps_partially(x, y, xbytes)) return WENC_ERR_ARG;  // in place (y == x) is allowed
+  } else {
+    // A 16-bit or MXFP8 y must not overlap x at all.
+    const size_t ybytes = out_dtype == WENC_DTYPE_MXFP8 ? mx_matrix_bytes(rows, d)
+                                                         : (size_t)rows * d * 2;
+    if (overlaps(x, xbytes, y, ybytes)) return WENC_ERR_ARG;
+  }
+  const int dt = out_dtype == WENC_DTYPE_F32    ? DT_F32
+                 : out_dtype == WENC_DTYPE_BF16 ? DT_BF16
+                 : out_dtype == WENC_DTYPE_F16  ? DT_F16
+                                                : DT_MX8;
   WENC_TRY(launch_layernorm(x, gamma, beta, y, rows, d, dt, static_cast<hipStream_t>(stream)));
   return WENC_OK;
 }
@@ -586,6 +630,8 @@ int whisper_enc_linear(const void* a, const void* w, const float* bias, const fl
     return WENC_ERR_ARG;
   if (fp32_out && overlaps_partially(residual, c, (size_t)m * n * sizeof(float)))
     return WENC_ERR_ARG;
+  if (dt == DT_MX8 && ((size_t)m * k > (size_t)INT32_MAX || (size_t)n * k > (size_t)INT32_MAX))
+    return WENC_ERR_UNSUPPORTED;  // 32-bit buffer offsets of the operand rows
   const int epi = epilogue == WENC_EPI_BIAS        ? EPI_BIAS
                   : epilogue == WENC_EPI_BIAS_GELU ? EPI_BIAS_GELU
                   : epilogue == WENC_EPI_BIAS_RESIDUAL ? EPI_BIAS_RESIDUAL
@@ -597,7 +643,7 @@ int whisper_enc_linear(const void* a, const void* w, const float* bias, const fl
 
 int whisper_enc_attention(const void* q, const void* k, const void* v, void* o, int batch, int t,
                           int heads, int ld_qkv, int ld_o, int path, void* stream) {
-  const int dt = path_dtype(path);
+  const int dt = plain_dtype(path);
   if (dt < 0) return WENC_ERR_ARG;
   if (batch < 0 || t < 0 || heads <= 0 || (long long)batch * t > WENC_MAX_ROWS) return WENC_ERR_ARG;
   if (heads * WENC_HEAD_DIM > WENC_MAX_FFN_DIM) return WENC_ERR_ARG;
@@ -615,7 +661,7 @@ int whisper_enc_attention(const void* q, const void* k, const void* v, void* o, 
 int whisper_enc_attention_varlen(const void* q, const void* k, const void* v, void* o,
                                  const int* cu_seqlens, int batch, int total_rows, int max_t,
                                  int heads, int ld_qkv, int ld_o, int path, void* stream) {
-  const int dt = path_dtype(path);
+  const int dt = plain_dtype(path);
   if (dt < 0) return WENC_ERR_ARG;
   if (batch < 0 || total_rows < 0 || max_t < 0 || heads <= 0 || total_rows > WENC_MAX_ROWS)
     return WENC_ERR_ARG;
@@ -656,7 +702,7 @@ CrossLayout cross_layout(int d, int n_layers, int path) {
 }
 
 bool valid_cross(int d, int n_layers, int path) {
-  return path_dtype(path) >= 0 && d >= 64 && d <= WENC_MAX_D_MODEL && d % 64 == 0 &&
+  return plain_dtype(path) >= 0 && d >= 64 && d <= WENC_MAX_D_MODEL && d % 64 == 0 &&
          n_layers >= 1 && n_layers <= WENC_MAX_DEC_LAYERS;
 }
 
@@ -676,7 +722,7 @@ int whisper_enc_pack_cross_kv(const float* const* wk, const float* const* wv,
   if (!wk || !wv || !bv || !dst || !aligned(dst, kAlign)) return WENC_ERR_ARG;
   for (int l = 0; l < n_dec_layers; ++l)
     if (!wk[l] || !wv[l] || !bv[l]) return WENC_ERR_ARG;
-  const int d = d_model, dt = path_dtype(path);
+  const int d = d_model, dt = plain_dtype(path);
   const size_t dd = (size_t)d * d, es = elem_bytes(path);
   const CrossLayout L = cross_layout(d, n_dec_layers, path);
   char* blob = static_cast<char*>(dst);
@@ -692,7 +738,7 @@ int whisper_enc_pack_cross_kv(const float* const* wk, const float* const* wv,
 }
 
 size_t whisper_enc_cross_kv_workspace_bytes(int batch, int t, int d_model, int path) {
-  if (path_dtype(path) < 0 || batch < 0 || t < 0 || (long long)batch * t > WENC_MAX_ROWS ||
+  if (plain_dtype(path) < 0 || batch < 0 || t < 0 || (long long)batch * t > WENC_MAX_ROWS ||
       d_model < 64 || d_model > WENC_MAX_D_MODEL || d_model % 64)
     return 0;
   if (path == WENC_PATH_FP32) return kAlign;  // the fp32 path reads y directly
@@ -713,7 +759,7 @@ int whisper_enc_cross_kv(const float* y, void* kv, const void* wkv, int n_dec_la
     return WENC_ERR_ARG;
   if (workspace_bytes < whisper_enc_cross_kv_workspace_bytes(batch, t, d_model, path))
     return WENC_ERR_WORKSPACE;
-  const int d = d_model, dt = path_dtype(path);
+  const int d = d_model, dt = plain_dtype(path);
   const int n = 2 * n_dec_layers * d;
   const CrossLayout L = cross_layout(d, n_dec_layers, path);
   const char* blob = static_cast<const char*>(wkv);
@@ -760,7 +806,7 @@ StemLayout stem_layout(int n_mels, int d, int n_pos, int path) {
 }
 
 bool valid_stem(int n_mels, int d, int n_pos, int path) {
-  return path_dtype(path) >= 0 && n_mels >= 1 && n_mels <= WENC_MAX_MELS && d >= 64 &&
+  return plain_dtype(path) >= 0 && n_mels >= 1 && n_mels <= WENC_MAX_MELS && d >= 64 &&
          d <= WENC_MAX_D_MODEL && d % 64 == 0 && n_pos >= 1 && n_pos <= WENC_MAX_ROWS;
 }
 
@@ -801,7 +847,7 @@ int whisper_enc_pack_stem(const float* conv1_w, const float* conv1_b, const floa
   if (!valid_stem(n_mels, d_model, n_pos, path)) return WENC_ERR_ARG;
   if (!conv1_w || !conv1_b || !conv2_w || !conv2_b || !pos) return WENC_ERR_ARG;
   if (!dst || !aligned(dst, kAlign)) return WENC_ERR_ARG;
-  const int d = d_model, dt = path_dtype(path);
+  const int d = d_model, dt = plain_dtype(path);
   const StemLayout L = stem_layout(n_mels, d, n_pos, path);
   char* blob = static_cast<char*>(dst);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -839,7 +885,7 @@ int whisper_enc_stem_forward(const float* mel, float* x, const void* stem, int b
   }
   const StemWorkspace w = stem_workspace(workspace, (size_t)batch, t_mel, n_mels, d_model, path);
   if (workspace_bytes < w.total) return WENC_ERR_WORKSPACE;
-  const int d = d_model, dt = path_dtype(path), k1 = stem_k1(n_mels);
+  const int d = d_model, dt = plain_dtype(path), k1 = stem_k1(n_mels);
   const StemLayout L = stem_layout(n_mels, d, n_pos, path);
   const char* blob = static_cast<const char*>(stem);
   auto fp = [&](size_t off) { return reinterpret_cast<const float*>(blob + off); };
@@ -869,6 +915,22 @@ int whisper_enc_quantize_matrix(const float* w, void* codes, void* scales, int n
   if ((size_t)n * k == 0) return WENC_OK;
   if (!w || !codes || !scales || !aligned(scales, 2)) return WENC_ERR_ARG;
   WENC_TRY(launch_quantize(w, codes, scales, n, k, bits, static_cast<hipStream_t>(stream)));
+  return WENC_OK;
+}
+
+size_t whisper_enc_mx_bytes(int rows, int k) {
+  if (rows < 0 || rows > WENC_MAX_ROWS || k < 32 || k % 32 != 0 || k > WENC_MAX_FFN_DIM) return 0;
+  return mx_matrix_bytes((size_t)rows, (size_t)k);
+}
+
+int whisper_enc_mx_quantize(const float* src, void* dst, int rows, int k, void* stream) {
+  if (rows < 0 || rows > WENC_MAX_ROWS || k < 32 || k % 32 != 0 || k > WENC_MAX_FFN_DIM)
+    return WENC_ERR_ARG;
+  if (rows == 0) return WENC_OK;
+  if (!src || !dst || !aligned(src, 16) || !aligned(dst, 16)) return WENC_ERR_ARG;
+  if (overlaps(src, (size_t)rows * k * sizeof(float), dst, mx_matrix_bytes(rows, k)))
+    return WENC_ERR_ARG;
+  WENC_TRY(launch_mx_quantize(src, dst, rows, k, 0, rows, static_cast<hipStream_t>(stream)));
   return WENC_OK;
 }
 

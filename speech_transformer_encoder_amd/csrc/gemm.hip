@@ -45,24 +45,6 @@ __device__ __forceinline__ float gelu_erf(float z) {
   return 0.5f * z * (1.0f + erff(z * 0.7071067811865476f));
 }
 
-// erf-GELU for the 16-bit paths, whose output is rounded to 8 or 11 significant bits: the
-// complementary error function from Abramowitz & Stegun, Handbook of Mathematical Functions,
-// formula 7.1.26 (Hastings' rational approximation, absolute error <= 1.5e-7):
-//   erfc(a) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-a^2),  t = 1 / (1 + p a),  a >= 0.
-// With a = |z| / sqrt 2 and w = 1 - erfc(a) = erf(a):  gelu(z) = z/2 (1 + erf(z/sqrt 2))
-// = (z + |z| w) / 2 for both signs of z.  13 VALU operations (two of them transcendental).
-__device__ __forceinline__ float gelu_erf_as(float z) {
-  const float az = fabsf(z);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.7071067811865476f, az, 1.0f));
-  float q = fmaf(t, 1.061405429f, -1.453152027f);
-  q = fmaf(t, q, 1.421413741f);
-  q = fmaf(t, q, -0.284496736f);
-  q = fmaf(t, q, 0.254829592f);
-  const float e = __builtin_amdgcn_exp2f(z * (z * (-0.5f * 1.4426950408889634f)));  // exp(-a^2)
-  const float w = fmaf(-(q * t), e, 1.0f);
-  return 0.5f * fmaf(az, w, z);
-}
-
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Element offset of (row m, column n) in the head-major layout of EPI_BIAS_HEADMAJOR: rows are
@@ -375,7 +357,7 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
 constexpr int H_N = 128, H_M = 256, H_K = 32;
 constexpr int H_WN = 2, H_WM = 4;
 constexpr int H_TN = H_N / H_WN, H_TM = H_M / H_WM;  // 64 x 64 per wavefront
-constexpr int H_NA = H_TN / 32, H_NB = H_TM / 32;     // 2 x 2
+constexpr int H_NA = H_TN / 32;                       // 2 MFMA blocks along n
 constexpr int H_WAVES = H_WN * H_WM;
 constexpr int H_THREADS = 64 * H_WAVES;
 
@@ -384,18 +366,31 @@ constexpr int H_THREADS = 64 * H_WAVES;
 // a tiny-, base- or small-shaped window), (4, 128): 128 x 128 tiles of eight wavefronts of 64 x 32.
 // (2, 128), four wavefronts of 64 x 64, is kept as a shape the kernel supports.  Every output is
 // the same k-ordered MFMA chain whatever the tile, so all shapes give identical results.
+//
+// T = mx8_t: MXFP8 operands (codes and E8M0 scale planes, see mx_planes_offset) on
+// v_mfma_scale_f32_32x32x64_f8f6f4.  A 64-byte LDS row then holds 64 k values (one MFMA deep),
+// in the same layout and with the same copies; per k tile, wavefront 0 also copies the tile's two
+// 32-k scale blocks of its 128 W rows and wavefront 1 those of its X rows into a 2 KB window after
+// the stage's operand rows.  EPI_BIAS writes fp16; EPI_BIAS_GELU writes MXFP8 (mx.c).
 template <typename T, int EPI, int WM = H_WM, int HM = H_M>
 __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))) void gemm16_small_kernel(
     const uint16_t* __restrict__ X, int lda, const uint16_t* __restrict__ W,
     const float* __restrict__ bias, const float* residual, void* C, int ldc, int M, int N, int K,
-    int ksplit, int big0, KMap km) {
+    int ksplit, int big0, KMap km, MxPlanes mx) {
+  constexpr bool MX = std::is_same<T, mx8_t>::value;
+  using OutT = typename std::conditional<MX, f16_t, T>::type;  // type of 16-bit outputs
+  constexpr int EB = MX ? 1 : 2;                           // operand bytes per k value
+  constexpr int KT = 64 / EB;                              // k values per 64-byte LDS row
   constexpr int HW = H_WN * WM;                            // wavefronts
   constexpr int TM = HM / WM, NB = TM / 32;                // rows per wavefront, 32-row blocks
   constexpr int HLW = H_N / 16 / HW, HLX = HM / 16 / HW;   // 1 KB copies per wavefront and operand
-  constexpr int HSTAGE = (H_N + HM) * H_K;                 // 16-bit elements per stage
+  // 16-bit elements per stage: the operand rows (+ the MXFP8 scale window, 2 KB).
+  constexpr int HSTAGE = (H_N + HM) * H_K + (MX ? 1024 : 0);
+  constexpr int SCALE_OFF = (H_N + HM) * 64;              // byte offset of the scale window
   // Three stages, or the epilogue's 8 KB (4096 16-bit elements) per wavefront if that is more.
   constexpr int LDS_ELEMS = 3 * HSTAGE > HW * 4096 ? 3 * HSTAGE : HW * 4096;
   static_assert((WM == 4 && (HM == 256 || HM == 128)) || (WM == 2 && HM == 128), "tile shapes");
+  static_assert(!MX || (EPI != EPI_BIAS_HEADMAJOR && EPI != EPI_BIAS_GELU_X2), "MXFP8 epilogues");
   // One array for the three stages: the copies are inline assembly, invisible to the compiler's
   // wait insertion, so separate arrays buy nothing; the epilogue reuses it (8 KB per wavefront).
   __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
@@ -432,31 +427,52 @@ __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))
     m0 = (first_m + (tb % group) % gm) * G_M;
     if (n0 >= N) return;  // the second half of a last tile only 64 columns wide
   }
-  const int kc = K / ksplit, kbyte0 = part * kc * 2;  // this part's first k, in bytes
+  const int kc = K / ksplit, kbyte0 = part * kc * EB;  // this part's first k, in bytes
 
   const int wrows = min(N - n0, H_N), xrows = min(M - m0, HM);
   const int kw = km.wrow;  // weight row length (k segments: the BF16X2 / X3 hi / lo pairs)
-  const u32x4 rW = buffer_rsrc(W + (size_t)n0 * kw, (uint32_t)(wrows * kw * 2));
-  const u32x4 rX = buffer_rsrc(X + (size_t)m0 * lda, (uint32_t)(xrows * lda * 2));
+  const char* const Wb = reinterpret_cast<const char*>(W);
+  const char* const Xb = reinterpret_cast<const char*>(X);
+  const u32x4 rW = buffer_rsrc(Wb + (size_t)n0 * kw * EB, (uint32_t)(wrows * kw * EB));
+  const u32x4 rX = buffer_rsrc(Xb + (size_t)m0 * lda * EB, (uint32_t)(xrows * lda * EB));
+  // MXFP8 scale planes (K / 32 planes each); reads past the last plane return zeros.
+  const u32x4 rWs = buffer_rsrc(mx.w, MX ? (uint32_t)((K / 32) * mx.w_stride) : 0u);
+  const u32x4 rXs = buffer_rsrc(mx.x, MX ? (uint32_t)((K / 32) * mx.x_stride) : 0u);
 
   // Copy i of wavefront w fills 1 KB block (i * HW + w) of its operand: 16 rows of 64 bytes,
   // lane l row (l >> 2), slot (l & 3) holding chunk slot ^ ((row >> 2) & 3).
   const int lrow = 16 * wave + (lane >> 2);
   const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
-  const int voW = lrow * kw * 2 + lchunk * 16, voX = lrow * lda * 2 + lchunk * 16;
+  const int voW = lrow * kw * EB + lchunk * 16, voX = lrow * lda * EB + lchunk * 16;
+  // Scale copies: lane l of wavefront 0 (1) copies 16 scale bytes of the tile's W (X) rows, block
+  // l / L of the tile's two, rows 16 (l % L) ..; lanes past 2 L read out of range (zeros) into
+  // the rest of the 1 KB window.  The window holds byte [block][row] at block * rows + row.
+  constexpr int XL = HM / 16;
+  const int sc_off = wave == 0 ? (lane < 16 ? (lane >> 3) * mx.w_stride + n0 + (lane & 7) * 16 : -1)
+                               : (lane < 2 * XL ? (lane / XL) * mx.x_stride + m0 + (lane % XL) * 16 : -1);
   auto load_tile = [&](int kt, const uint16_t* st) {
-    const int ke = kbyte0 / 2 + kt * H_K;  // first k of the tile
-    const int seg = (ke >= km.kb) + (ke >= 2 * km.kb), kk = ke - seg * km.kb;
-    const int ko = (((km.xmask >> seg) & 1) * km.kb + kk) * 2;
-    const int kow = (((km.wmask >> seg) & 1) * km.kb + kk) * 2;
     const uint32_t base = lds_addr(st);
+    int ko, kow;
+    if constexpr (MX) {
+      ko = kow = kbyte0 + kt * 64;
+      const int blk = ko >> 5;  // first 32-k block of the tile
+      if (wave == 0)
+        lds_copy16(rWs, base + SCALE_OFF, sc_off < 0 ? 0x7ffffff0 : sc_off + blk * mx.w_stride);
+      else if (wave == 1)
+        lds_copy16(rXs, base + SCALE_OFF + 1024u, sc_off < 0 ? 0x7ffffff0 : sc_off + blk * mx.x_stride);
+    } else {
+      const int ke = kbyte0 / 2 + kt * H_K;  // first k of the tile
+      const int seg = (ke >= km.kb) + (ke >= 2 * km.kb), kk = ke - seg * km.kb;
+      ko = (((km.xmask >> seg) & 1) * km.kb + kk) * 2;
+      kow = (((km.wmask >> seg) & 1) * km.kb + kk) * 2;
+    }
 #pragma unroll
     for (int i = 0; i < HLW; ++i)
-      lds_copy16(rW, base + (uint32_t)(i * HW + wave) * 1024u, voW + i * 16 * HW * kw * 2 + kow);
+      lds_copy16(rW, base + (uint32_t)(i * HW + wave) * 1024u, voW + i * 16 * HW * kw * EB + kow);
 #pragma unroll
     for (int i = 0; i < HLX; ++i)
       lds_copy16(rX, base + H_N * 64 + (uint32_t)(i * HW + wave) * 1024u,
-                 voX + i * 16 * HW * lda * 2 + ko);
+                 voX + i * 16 * HW * lda * EB + ko);
   };
 
   const int rowA = (wn * H_TN + frow) * 64;
@@ -486,7 +502,7 @@ __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))
 #pragma unroll
     for (int a = 0; a < H_NA; ++a)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) acc[a][b] = mfma32x32x16<T>(fa[a], fb[b], acc[a][b]);
+      for (int b = 0; b < NB; ++b) acc[a][b] = mfma32x32x16<OutT>(fa[a], fb[b], acc[a][b]);
   };
   auto sched = [&]() {
     constexpr int R = H_NA + NB, MF = H_NA * NB, P = R < MF ? R : MF;  // reads, MFMAs, pairs
@@ -499,33 +515,90 @@ __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))
     if constexpr (R > P) __builtin_amdgcn_sched_group_barrier(0x100, R - P, 0);
   };
 
-  constexpr int LT = HLW + HLX;  // copies per wavefront and tile
-  const int nk = kc / H_K;
-  u32x4 fa0[H_NA], fb0[NB], fa1[H_NA], fb1[NB];
-  load_tile(0, s0);
-  if (nk > 1) load_tile(1, s1);
-  if (nk > 1) __builtin_amdgcn_s_waitcnt(0x0F70 | LT); else __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  read_frags(s0, 0, fa0, fb0);
-
-  // k tile kt from `cur`; tile kt + 2 goes to `ahead` (the stage of tile kt - 1, which every
-  // wavefront finished reading before the barrier of body(kt - 1)).
-  auto body = [&](int kt, const uint16_t* cur, const uint16_t* nxt, const uint16_t* ahead) {
-    const bool loads = kt + 2 < nk, next = kt + 1 < nk;
-    if (loads) load_tile(kt + 2, ahead);
-    read_frags(cur, 1, fa1, fb1); mm(fa0, fb0); sched();
-    if (next) {
-      if (loads) __builtin_amdgcn_s_waitcnt(0x0F70 | LT);
-      else __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();  // tile kt + 1 landed everywhere; tile kt no longer read after this step
-      read_frags(nxt, 0, fa0, fb0);
-    }
-    mm(fa1, fb1);
+  constexpr int LT = HLW + HLX;  // copies per wavefront and tile (MXFP8: +1 on wavefronts 0, 1)
+  // Wait until this wavefront's copies of the next tile have landed, with those of the tile after
+  // it (`ahead`) still allowed in flight.
+  auto wait_copies = [&](bool ahead) {
+    if (!ahead) __builtin_amdgcn_s_waitcnt(0x0F70);
+    else if (MX && wave < 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (LT + 1));
+    else __builtin_amdgcn_s_waitcnt(0x0F70 | LT);
   };
-  for (int kt = 0; kt < nk; kt += 3) {
-    body(kt, s0, s1, s2);
-    if (kt + 1 < nk) body(kt + 1, s1, s2, s0);
-    if (kt + 2 < nk) body(kt + 2, s2, s0, s1);
+  const int nk = kc / KT;
+  if constexpr (MX) {
+    // Per k tile each fragment is chunks g and g + 2 of its LDS row (k 16 g .. and 32 + 16 g ..:
+    // the MFMA's 32 bytes per lane, bytes 0 .. 15 in 32-k block 0 and 16 .. 31 in block 1, block
+    // b scaled by the register of lane row + 32 b), and the lane's scale byte is that of block g.
+    // The fragments of tile kt + 1 are read after the barrier that follows tile kt's MFMAs
+    // (the compiler gives alternate tiles their own registers, so those reads overlap the MFMAs
+    // still running; an explicit second register set measured no faster and cost 27 VGPRs).
+    auto read_scales = [&](const uint16_t* st, int (&sa)[H_NA], int (&sb)[NB]) {
+      const uint8_t* w = reinterpret_cast<const uint8_t*>(st) + SCALE_OFF;
+#pragma unroll
+      for (int a = 0; a < H_NA; ++a) sa[a] = w[g * H_N + wn * H_TN + a * 32 + frow];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) sb[b] = w[1024 + g * HM + wm * TM + b * 32 + frow];
+    };
+    u32x4 A0[H_NA], B0[NB], A1[H_NA], B1[NB];
+    int SA[H_NA], SB[NB];
+    auto mm_row = [&](int a) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        acc[a][b] = mfma_mx8(A0[a], A1[a], B0[b], B1[b], SA[a], SB[b], acc[a][b]);
+    };
+    load_tile(0, s0);
+    if (nk > 1) load_tile(1, s1);
+    wait_copies(nk > 1);
+    __syncthreads();
+    read_frags(s0, 0, A0, B0);
+    read_frags(s0, 1, A1, B1);
+    read_scales(s0, SA, SB);
+    auto body = [&](int kt, const uint16_t* nxt, const uint16_t* ahead) {
+      const bool loads = kt + 2 < nk, next = kt + 1 < nk;
+      if (loads) load_tile(kt + 2, ahead);
+#pragma unroll
+      for (int a = 0; a < H_NA; ++a) mm_row(a);
+      if (next) {
+        wait_copies(loads);
+        // Tile kt + 1 landed everywhere, and every wavefront's reads of tile kt are complete (the
+        // barrier waits for them), so tile kt's stage may take tile kt + 3 in body(kt + 1).
+        __syncthreads();
+        read_frags(nxt, 0, A0, B0);
+        read_frags(nxt, 1, A1, B1);
+        read_scales(nxt, SA, SB);
+      }
+    };
+    for (int kt = 0; kt < nk; kt += 3) {
+      body(kt, s1, s2);
+      if (kt + 1 < nk) body(kt + 1, s2, s0);
+      if (kt + 2 < nk) body(kt + 2, s0, s1);
+    }
+  } else {
+    u32x4 fa0[H_NA], fb0[NB], fa1[H_NA], fb1[NB];
+    load_tile(0, s0);
+    if (nk > 1) load_tile(1, s1);
+    if (nk > 1) __builtin_amdgcn_s_waitcnt(0x0F70 | LT); else __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    read_frags(s0, 0, fa0, fb0);
+
+    // k tile kt from `cur`; tile kt + 2 goes to `ahead` (the stage of tile kt - 1, which every
+    // wavefront finished reading before the barrier of body(kt - 1)).
+    auto body = [&](int kt, const uint16_t* cur, const uint16_t* nxt, const uint16_t* ahead) {
+      const bool loads = kt + 2 < nk, next = kt + 1 < nk;
+      if (loads) load_tile(kt + 2, ahead);
+      read_frags(cur, 1, fa1, fb1); mm(fa0, fb0); sched();
+      if (next) {
+        if (loads) __builtin_amdgcn_s_waitcnt(0x0F70 | LT);
+        else __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();  // tile kt + 1 landed everywhere; tile kt no longer read after this step
+        read_frags(nxt, 0, fa0, fb0);
+      }
+      mm(fa1, fb1);
+    };
+    for (int kt = 0; kt < nk; kt += 3) {
+      body(kt, s0, s1, s2);
+      if (kt + 1 < nk) body(kt + 1, s1, s2, s0);
+      if (kt + 2 < nk) body(kt + 2, s2, s0, s1);
+    }
   }
 
   // Epilogue as in the persistent kernel: 32-row blocks staged through the wavefront's own 8 KB of
@@ -590,7 +663,25 @@ __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))
           v0 = make_float4(gelu_erf_as(v0.x), gelu_erf_as(v0.y), gelu_erf_as(v0.z), gelu_erf_as(v0.w));
           v1 = make_float4(gelu_erf_as(v1.x), gelu_erf_as(v1.y), gelu_erf_as(v1.z), gelu_erf_as(v1.w));
         }
-        const u32x4 w4 = {pack2<T>(v0.x, v0.y), pack2<T>(v0.z, v0.w), pack2<T>(v1.x, v1.y), pack2<T>(v1.z, v1.w)};
+        if constexpr (MX && EPI == EPI_BIAS_GELU) {
+          // MXFP8 output: a 32-column block of row m is held by the four lanes 4 j .. 4 j + 3 (eight
+          // columns each); its scale byte goes to plane (column / 32), position m.
+          float amax = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
+                             fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
+          amax = fmaxf(amax, __shfl_xor(amax, 1));
+          amax = fmaxf(amax, __shfl_xor(amax, 2));
+          const int xe = mx_exponent(amax);
+          const float sc = mx_inv_scale(xe);
+          const u32x2 w2 = {mx_pack4(v0, sc), mx_pack4(v1, sc)};
+          if (m < M) {
+            *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(C) + (size_t)m * ldc + nw + 4 * c0) = w2;
+            if ((lane & 3) == 0)
+              mx.c[(size_t)((nw + 4 * c0) >> 5) * mx.c_stride + m] = (uint8_t)(xe + 127);
+          }
+          continue;
+        }
+        const u32x4 w4 = {pack2<OutT>(v0.x, v0.y), pack2<OutT>(v0.z, v0.w), pack2<OutT>(v1.x, v1.y),
+                          pack2<OutT>(v1.z, v1.w)};
         if (m < M) {
           const size_t off = EPI == EPI_BIAS_HEADMAJOR ? headmajor_offset(m, nw + 4 * c0, N, ldc)
                                                        : (size_t)m * ldc + nw + 4 * c0;
@@ -764,13 +855,14 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int ksplit,
 // (4 parts of 320 -> 2 of 640), d 512 fc2 19.9 -> 17.2 us (8 of 256 -> 4 of 512); with parts of
 // 768 k or more (d 768 and d 1280 fc2) the 128 x 256 tiles stay faster.  Fewer 128 x 256 tiles
 // than half the CUs also take 128 x 128 tiles.
-static int split_plan(int m, int n, int k, int* tile_rows) {
+// kt: the k values per k tile (32 for 16-bit operands, 64 for MXFP8); every part is whole tiles.
+static int split_plan(int m, int n, int k, int* tile_rows, int kt = H_K) {
   *tile_rows = H_M;
   const long big = (long)((m + G_M - 1) / G_M) * ((n + G_N - 1) / G_N);
   if (big >= 256) return 1;
   const long small = (long)((m + H_M - 1) / H_M) * ((n + H_N - 1) / H_N);
   int s = 1;
-  while (s < 8 && small * s * 2 <= 256 && k % (s * 2 * H_K) == 0 && k / (s * 2) >= 256) s *= 2;
+  while (s < 8 && small * s * 2 <= 256 && k % (s * 2 * kt) == 0 && k / (s * 2) >= 256) s *= 2;
   if (2 * small * s < 256) {
     *tile_rows = 128;
   } else if (s >= 4 && k / s < 512) {
@@ -784,7 +876,7 @@ int linear_split(int m, int n, int k, int dtype, int epilogue) {
   if (dtype == DT_F32 || (epilogue != EPI_BIAS_RESIDUAL && epilogue != EPI_BIAS_GELU_RESIDUAL))
     return 1;
   int rows;
-  return split_plan(m, n, k, &rows);
+  return split_plan(m, n, k, &rows, dtype == DT_MX8 ? 64 : H_K);
 }
 
 // Workgroups of the persistent kernel: the current device's CU count, rounded down to a multiple
@@ -816,11 +908,11 @@ static hipError_t launch16_epi(const uint16_t* X, int lda, const uint16_t* W, co
       if (split_rows == 128)
         gemm16_small_kernel<T, EPI_PARTIAL, 4, 128><<<dim3((unsigned)(small2 * split)),
                                                        dim3(H_THREADS), 0, st>>>(
-            X, lda, W, bias, nullptr, partial, n, m, n, k, split, -1, kw);
+            X, lda, W, bias, nullptr, partial, n, m, n, k, split, -1, kw, MxPlanes{});
       else
         gemm16_small_kernel<T, EPI_PARTIAL><<<dim3((unsigned)(small * split)), dim3(H_THREADS),
                                               0, st>>>(X, lda, W, bias, nullptr, partial, n, m, n,
-                                                       k, split, -1, kw);
+                                                       k, split, -1, kw, MxPlanes{});
       if (ln)
         return launch_splitk_reduce_ln(partial, split, bias, residual,
                                        ln->keep_x ? static_cast<float*>(c) : nullptr, ln->gamma,
@@ -842,7 +934,7 @@ static hipError_t launch16_epi(const uint16_t* X, int lda, const uint16_t* W, co
         X, lda, W, bias, residual, c, ldc, m, n, k, (int)(halves ? whole : tiles), kw);
     if (halves)
       gemm16_small_kernel<T, EPI><<<dim3((unsigned)(2 * tail)), dim3(H_THREADS), 0, st>>>(
-          X, lda, W, bias, residual, c, ldc, m, n, k, 1, (int)whole, kw);
+          X, lda, W, bias, residual, c, ldc, m, n, k, 1, (int)whole, kw, MxPlanes{});
   } else if (2 * small < grid) {
     // Fewer 128 x 256 tiles than half the CUs: 128 x 128 tiles, eight wavefronts of 64 x 32, twice
     // as many workgroups.  Measured at M = 1500 (us, 128 x 256 -> 128 x 128 with four wavefronts
@@ -850,10 +942,10 @@ static hipError_t launch16_epi(const uint16_t* X, int lda, const uint16_t* W, co
     // d 512 QKV 10.7 -> 8.8 -> 7.5, fc1 14.0 -> 11.0 -> 9.7; d 768 QKV 14.4 -> 12.0 -> 11.0.  With
     // 144 tiles or more (d 768 fc1, d 1280) the 128 x 256 tiles stay as fast or faster.
     gemm16_small_kernel<T, EPI, 4, 128><<<dim3((unsigned)small2), dim3(H_THREADS), 0, st>>>(
-        X, lda, W, bias, residual, c, ldc, m, n, k, 1, -1, kw);
+        X, lda, W, bias, residual, c, ldc, m, n, k, 1, -1, kw, MxPlanes{});
   } else {
     gemm16_small_kernel<T, EPI><<<dim3((unsigned)small), dim3(H_THREADS), 0, st>>>(
-        X, lda, W, bias, residual, c, ldc, m, n, k, 1, -1, kw);
+        X, lda, W, bias, residual, c, ldc, m, n, k, 1, -1, kw, MxPlanes{});
   }
   return hipGetLastError();
 }
@@ -885,6 +977,77 @@ static hipError_t launch16(const void* a, int lda, const void* w, const float* b
     if (epi == EPI_BIAS_GELU_X2)
       return launch16_epi<T, EPI_BIAS_GELU_X2>(X, lda, W, bias, residual, c, ldc, m, n, k, st,
                                                partial, ln, kw);
+  }
+  return hipErrorInvalidValue;
+}
+
+// MXFP8 operands: always the small kernel (128 x 256 tiles, or 128 x 128 where those would
+// leave more than half the CUs idle), with the same split-k rule as the 16-bit operands.
+template <int EPI>
+static hipError_t launch_mx_epi(const uint16_t* X, const uint16_t* W, const float* bias,
+                                const float* residual, void* c, int ldc, int m, int n, int k,
+                                hipStream_t st, float* partial, const LnFuse* ln,
+                                const MxPlanes& mx) {
+  const KMap kw{k, 1, 0, 0, k};
+  const long small = (long)((m + H_M - 1) / H_M) * ((n + H_N - 1) / H_N);
+  const long small2 = (long)((m + 127) / 128) * ((n + H_N - 1) / H_N);
+  int split_rows = H_M;
+  const int split = partial ? linear_split(m, n, k, DT_MX8, EPI) : 1;
+  if (split > 1) split_plan(m, n, k, &split_rows, 64);
+  if (ln && (EPI != EPI_BIAS_RESIDUAL || split < 2 || ldc != n)) return hipErrorInvalidValue;
+  if constexpr (EPI == EPI_BIAS_RESIDUAL || EPI == EPI_BIAS_GELU_RESIDUAL) {
+    if (split > 1) {
+      if (split_rows == 128)
+        gemm16_small_kernel<mx8_t, EPI_PARTIAL, 4, 128><<<dim3((unsigned)(small2 * split)),
+                                                           dim3(H_THREADS), 0, st>>>(
+            X, k, W, bias, nullptr, partial, n, m, n, k, split, -1, kw, mx);
+      else
+        gemm16_small_kernel<mx8_t, EPI_PARTIAL><<<dim3((unsigned)(small * split)),
+                                                  dim3(H_THREADS), 0, st>>>(
+            X, k, W, bias, nullptr, partial, n, m, n, k, split, -1, kw, mx);
+      if (ln)
+        return launch_splitk_reduce_ln(partial, split, bias, residual,
+                                       ln->keep_x ? static_cast<float*>(c) : nullptr, ln->gamma,
+                                       ln->beta, ln->y, ln->y_dtype, m, n, st);
+      const unsigned g = (unsigned)std::min(m, 16384);
+      splitk_reduce_kernel<EPI == EPI_BIAS_GELU_RESIDUAL><<<g, 256, 0, st>>>(
+          partial, split, bias, residual, static_cast<float*>(c), ldc, m, n);
+      return hipGetLastError();
+    }
+  }
+  if (2 * small < persistent_grid())
+    gemm16_small_kernel<mx8_t, EPI, 4, 128><<<dim3((unsigned)small2), dim3(H_THREADS), 0, st>>>(
+        X, k, W, bias, residual, c, ldc, m, n, k, 1, -1, kw, mx);
+  else
+    gemm16_small_kernel<mx8_t, EPI><<<dim3((unsigned)small), dim3(H_THREADS), 0, st>>>(
+        X, k, W, bias, residual, c, ldc, m, n, k, 1, -1, kw, mx);
+  return hipGetLastError();
+}
+
+static hipError_t launch_mx(const void* a, int lda, const void* w, const float* bias,
+                            const float* residual, void* c, int ldc, int m, int n, int k, int epi,
+                            hipStream_t st, float* partial, const LnFuse* ln) {
+  if (lda != k || k % 64 != 0) return hipErrorInvalidValue;
+  MxPlanes mx{static_cast<const uint8_t*>(a) + mx_planes_offset(m, k), (int)mx_plane_stride(m),
+              static_cast<const uint8_t*>(w) + mx_planes_offset(n, k), (int)mx_plane_stride(n),
+              nullptr, 0};
+  auto X = static_cast<const uint16_t*>(a);
+  auto W = static_cast<const uint16_t*>(w);
+  switch (epi) {
+    case EPI_BIAS:
+      return launch_mx_epi<EPI_BIAS>(X, W, bias, residual, c, ldc, m, n, k, st, partial, ln, mx);
+    case EPI_BIAS_GELU:
+      if (ldc != n) return hipErrorInvalidValue;
+      mx.c = static_cast<uint8_t*>(c) + mx_planes_offset(m, n);
+      mx.c_stride = (int)mx_plane_stride(m);
+      return launch_mx_epi<EPI_BIAS_GELU>(X, W, bias, residual, c, ldc, m, n, k, st, partial, ln,
+                                          mx);
+    case EPI_BIAS_RESIDUAL:
+      return launch_mx_epi<EPI_BIAS_RESIDUAL>(X, W, bias, residual, c, ldc, m, n, k, st, partial,
+                                              ln, mx);
+    case EPI_BIAS_GELU_RESIDUAL:
+      return launch_mx_epi<EPI_BIAS_GELU_RESIDUAL>(X, W, bias, residual, c, ldc, m, n, k, st,
+                                                   partial, ln, mx);
   }
   return hipErrorInvalidValue;
 }
@@ -940,6 +1103,9 @@ hipError_t launch_linear(const void* a, int lda, const void* w, const float* bia
     case DT_F32:
       if (ln) return hipErrorInvalidValue;
       return launch32(a, lda, w, bias, residual, c, ldc, m, n, k, epilogue, st);
+    case DT_MX8:
+      if (!plain) return hipErrorInvalidValue;
+      return launch_mx(a, lda, w, bias, residual, c, ldc, m, n, k, epilogue, st, partial, ln);
   }
   return hipErrorInvalidValue;
 }

@@ -8,8 +8,9 @@
 // The pages' shader runs one 256-thread workgroup per row with shared-memory tree reductions.
 // Here a 64-lane wavefront owns a row: it loads the whole row into registers with 16-byte
 // loads (d <= 4096), reduces with cross-lane shuffles, and writes the normalised row in the
-// GEMM operand type (bf16 / fp16) or fp32.  Four rows per 256-thread workgroup.  The pass is
-// HBM-bound: 4 bytes read and 2 (or 4) bytes written per element.
+// GEMM operand type (bf16 / fp16, or MXFP8 codes with their scale planes) or fp32.  Four rows
+// per 256-thread workgroup.  The pass is HBM-bound: 4 bytes read and 1, 2 or 4 bytes written per
+// element.
 //
 // When the residual GEMM before a LayerNorm splits k (one window), the GEMM's second pass and the
 // LayerNorm are one kernel here (splitk_reduce_ln_rows): the row is formed from the parts in
@@ -24,20 +25,20 @@ struct LnStore;
 
 template <int NV>
 struct LnStore<NV, float> {
-  static __device__ __forceinline__ void put(void* y, size_t row, int d, int c, float4 v) {
+  static __device__ __forceinline__ void put(void* y, size_t row, int d, int c, float4 v, int) {
     *reinterpret_cast<float4*>(static_cast<float*>(y) + row * d + c) = v;
   }
 };
 template <int NV>
 struct LnStore<NV, bf16_t> {
-  static __device__ __forceinline__ void put(void* y, size_t row, int d, int c, float4 v) {
+  static __device__ __forceinline__ void put(void* y, size_t row, int d, int c, float4 v, int) {
     u32x2 w = {pack2<bf16_t>(v.x, v.y), pack2<bf16_t>(v.z, v.w)};
     *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(y) + row * d + c) = w;
   }
 };
 template <int NV>
 struct LnStore<NV, f16_t> {
-  static __device__ __forceinline__ void put(void* y, size_t row, int d, int c, float4 v) {
+  static __device__ __forceinline__ void put(void* y, size_t row, int d, int c, float4 v, int) {
     u32x2 w = {pack2<f16_t>(v.x, v.y), pack2<f16_t>(v.z, v.w)};
     *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(y) + row * d + c) = w;
   }
@@ -47,7 +48,7 @@ struct LnStore<NV, f16_t> {
 struct bf16x2_t {};
 template <int NV>
 struct LnStore<NV, bf16x2_t> {
-  static __device__ __forceinline__ void put(void* y, size_t row, int d, int c, float4 v) {
+  static __device__ __forceinline__ void put(void* y, size_t row, int d, int c, float4 v, int) {
     const float h0 = (float)(__bf16)v.x, h1 = (float)(__bf16)v.y, h2 = (float)(__bf16)v.z,
                 h3 = (float)(__bf16)v.w;
     uint16_t* base = static_cast<uint16_t*>(y) + row * 2 * d + c;
@@ -57,13 +58,32 @@ struct LnStore<NV, bf16x2_t> {
   }
 };
 
+// MXFP8 rows (codes [rows][d], then the scale planes): the 32 columns of a block are held by
+// eight consecutive lanes (four each), which share the block's largest magnitude; the first of
+// them stores the scale byte.  Called by every lane of those eight (d is a multiple of 64).
+template <int NV>
+struct LnStore<NV, mx8_t> {
+  static __device__ __forceinline__ void put(void* y, size_t row, int d, int c, float4 v, int rows) {
+    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    amax = fmaxf(amax, __shfl_xor(amax, 4));
+    const int xe = mx_exponent(amax);
+    uint8_t* base = static_cast<uint8_t*>(y);
+    *reinterpret_cast<uint32_t*>(base + row * d + c) = mx_pack4(v, mx_inv_scale(xe));
+    if ((c & 31) == 0)
+      base[mx_planes_offset(rows, d) + (size_t)(c >> 5) * mx_plane_stride(rows) + row] =
+          (uint8_t)(xe + 127);
+  }
+};
+
 // Normalises one row held in a wavefront's registers (lane l has columns 4 (l + 64 j) .. + 3 in
 // v[j]; entries past d are ignored) and stores it as OutT.  Both the plain LayerNorm and the fused
 // split-k reduction below end in this routine, so they round identically.
 template <int NV, typename OutT>
 __device__ __forceinline__ void ln_row(float4 (&v)[NV], int lane, const float* __restrict__ gamma,
                                        const float* __restrict__ beta, void* y, size_t row, int d,
-                                       float eps) {
+                                       float eps, int rows) {
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
@@ -94,7 +114,7 @@ __device__ __forceinline__ void ln_row(float4 (&v)[NV], int lane, const float* _
       o.y = v[j].y * inv * g.y + b.y;
       o.z = v[j].z * inv * g.z + b.z;
       o.w = v[j].w * inv * g.w + b.w;
-      LnStore<NV, OutT>::put(y, row, d, c, o);
+      LnStore<NV, OutT>::put(y, row, d, c, o, rows);
     }
   }
 }
@@ -115,7 +135,7 @@ __global__ __launch_bounds__(256) void layernorm_rows(const float* __restrict__ 
     const int c = (lane + 64 * j) * 4;
     v[j] = c < d ? *reinterpret_cast<const float4*>(xr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  ln_row<NV, OutT>(v, lane, gamma, beta, y, row, d, eps);
+  ln_row<NV, OutT>(v, lane, gamma, beta, y, row, d, eps, rows);
 }
 
 // Second pass of a split-k residual GEMM fused with the LayerNorm that reads its output: per row,
@@ -167,7 +187,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_ln_rows(
       if (c < d) *reinterpret_cast<float4*>(x_out + row * d + c) = v[j];
     }
   }
-  ln_row<NV, OutT>(v, lane, gamma, beta, y, row, d, eps);
+  ln_row<NV, OutT>(v, lane, gamma, beta, y, row, d, eps, rows);
 }
 
 template <typename OutT>
@@ -230,6 +250,9 @@ hipError_t launch_splitk_reduce_ln(const float* part, int ksplit, const float* b
     case DT_BF16X2:
       return launch_reduce_ln_t<bf16x2_t>(part, ksplit, bias, residual, x_out, gamma, beta, y,
                                           rows, d, st);
+    case DT_MX8:
+      return launch_reduce_ln_t<mx8_t>(part, ksplit, bias, residual, x_out, gamma, beta, y, rows,
+                                       d, st);
   }
   return hipErrorInvalidValue;
 }
@@ -242,6 +265,7 @@ hipError_t launch_layernorm(const float* x, const float* g, const float* b, void
     case DT_BF16: return launch_ln_t<bf16_t>(x, g, b, y, rows, d, st);
     case DT_F16: return launch_ln_t<f16_t>(x, g, b, y, rows, d, st);
     case DT_BF16X2: return launch_ln_t<bf16x2_t>(x, g, b, y, rows, d, st);
+    case DT_MX8: return launch_ln_t<mx8_t>(x, g, b, y, rows, d, st);
   }
   return hipErrorInvalidValue;
 }

@@ -141,4 +141,43 @@ hipError_t launch_dequant(const DequantSegments& seg, int bits, hipStream_t st) 
   return hipGetLastError();
 }
 
+// MXFP8 weights (the operands of the scaled-MFMA GEMMs): rows r0 .. r0 + n - 1 of an MXFP8 matrix
+// of `total` rows and k columns at dst (codes, then the scale planes), from fp32 src [n][k].  One
+// thread per (row, block of 32): the block's largest magnitude fixes X (mx_exponent), the codes
+// are the E4M3 roundings of v 2^-X (exact scaling by a power of two, then round to nearest even).
+__global__ void mx_quantize_kernel(const float* __restrict__ src, uint8_t* __restrict__ dst,
+                                   int n, int k, int r0, int total) {
+  const int nb = k / 32;
+  const size_t blocks = (size_t)n * nb;
+  uint8_t* planes = dst + mx_planes_offset(total, k);
+  const size_t pstride = mx_plane_stride(total);
+  for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < blocks;
+       e += (size_t)gridDim.x * blockDim.x) {
+    const int row = (int)(e / nb), blk = (int)(e % nb);
+    const float4* s4 = reinterpret_cast<const float4*>(src + (size_t)row * k + blk * 32);
+    float4 v[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] = s4[i];
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+    }
+    const int xe = mx_exponent(amax);
+    const float sc = mx_inv_scale(xe);
+    u32x4* out = reinterpret_cast<u32x4*>(dst + (size_t)(r0 + row) * k + blk * 32);
+    out[0] = u32x4{mx_pack4(v[0], sc), mx_pack4(v[1], sc), mx_pack4(v[2], sc), mx_pack4(v[3], sc)};
+    out[1] = u32x4{mx_pack4(v[4], sc), mx_pack4(v[5], sc), mx_pack4(v[6], sc), mx_pack4(v[7], sc)};
+    planes[(size_t)blk * pstride + r0 + row] = (uint8_t)(xe + 127);
+  }
+}
+
+hipError_t launch_mx_quantize(const float* src, void* dst, int n, int k, int r0, int total,
+                              hipStream_t st) {
+  const size_t blocks = (size_t)n * (k / 32);
+  if (blocks == 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<size_t>((blocks + 255) / 256, 8192);
+  mx_quantize_kernel<<<grid, 256, 0, st>>>(src, static_cast<uint8_t*>(dst), n, k, r0, total);
+  return hipGetLastError();
+}
+
 }  // namespace wenc

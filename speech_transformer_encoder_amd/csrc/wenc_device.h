@@ -65,6 +65,25 @@ __device__ __forceinline__ f32x16 mfma32x32x16<f16_t>(u32x4 a, u32x4 b, f32x16 c
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// MXFP8 operand tag (E4M3 codes with E8M0 scale planes; layout: mx_planes_offset).
+struct mx8_t {};
+
+// D(32x32) += A(32x64) * B(64x32) with E4M3 operands and E8M0 block scales
+// (v_mfma_scale_f32_32x32x64_f8f6f4).  Lane l supplies 32 bytes of row l % 32 of A (and of
+// column l % 32 of B): bytes 0 .. 15 hold 16 k values of 32-k block 0 and bytes 16 .. 31 16 of
+// block 1, the two halves of the wavefront covering each block together; block b of row r is
+// scaled by 2^(s - 127) with s the low byte of the scale register of lane r + 32 b (measured with
+// exact small-integer products on gfx950).  D has the layout of the 16-bit form.
+__device__ __forceinline__ f32x16 mfma_mx8(u32x4 a_lo, u32x4 a_hi, u32x4 b_lo, u32x4 b_hi, int sa,
+                                           int sb, f32x16 c) {
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  const i32x8 a = {(int)a_lo[0], (int)a_lo[1], (int)a_lo[2], (int)a_lo[3],
+                   (int)a_hi[0], (int)a_hi[1], (int)a_hi[2], (int)a_hi[3]};
+  const i32x8 b = {(int)b_lo[0], (int)b_lo[1], (int)b_lo[2], (int)b_lo[3],
+                   (int)b_hi[0], (int)b_hi[1], (int)b_hi[2], (int)b_hi[3]};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
 // D(32x32) += A(32x2) * B(2x32) in fp32.  Lane l supplies A[row l%32][k l/32] and
 // B[k l/32][col l%32]; D has the same layout as the 16-bit form.
 __device__ __forceinline__ f32x16 mfma32x32x2_f32(float a, float b, f32x16 c) {
@@ -91,6 +110,44 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- MXFP8 (OCP Microscaling Formats v1.0, E4M3 elements, E8M0 scale per 32 values) ----
+// (matrix layout: mx_planes_offset in wenc_internal.h)
+
+// Scale exponent of a block whose largest magnitude is amax: the smallest X with
+// amax <= 448 * 2^X (448 = 1.75 * 2^8, E4M3's largest finite value), so no element saturates;
+// -127 for amax = 0 (or below the normal range), which the E8M0 range also bounds.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  const int x = (int)(b >> 23) - 127 - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
+  return x < -127 ? -127 : x;
+}
+// 2^-X as a float (X in [-127, 120]: a normal number).
+__device__ __forceinline__ float mx_inv_scale(int x) { return __uint_as_float((uint32_t)(127 - x) << 23); }
+// Four values times s -> four E4M3 codes (round to nearest even; every |v s| <= 448) in one word,
+// value i in byte i.
+__device__ __forceinline__ uint32_t mx_pack4(float4 v, float s) {
+  uint32_t r = __builtin_amdgcn_cvt_pk_fp8_f32(v.x * s, v.y * s, 0u, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(v.z * s, v.w * s, r, true);
+}
+
+// erf-GELU for outputs rounded to 16 bits or fewer: the complementary error function from
+// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26 (Hastings' rational
+// approximation, absolute error <= 1.5e-7):
+//   erfc(a) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-a^2),  t = 1 / (1 + p a),  a >= 0.
+// With a = |z| / sqrt 2 and w = 1 - erfc(a) = erf(a):  gelu(z) = z/2 (1 + erf(z/sqrt 2))
+// = (z + |z| w) / 2 for both signs of z.  13 VALU operations (two of them transcendental).
+__device__ __forceinline__ float gelu_erf_as(float z) {
+  const float az = fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.7071067811865476f, az, 1.0f));
+  float q = fmaf(t, 1.061405429f, -1.453152027f);
+  q = fmaf(t, q, 1.421413741f);
+  q = fmaf(t, q, -0.284496736f);
+  q = fmaf(t, q, 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(z * (z * (-0.5f * 1.4426950408889634f)));  // exp(-a^2)
+  const float w = fmaf(-(q * t), e, 1.0f);
+  return 0.5f * fmaf(az, w, z);
+}
 
 // Workgroups of a 1-D grid are dispatched round-robin over the eight XCDs (id % 8).  This
 // bijective renumbering gives each XCD a contiguous range of virtual ids, so workgroups that

@@ -11,7 +11,21 @@ namespace wenc {
 // DT_BF16X2: a value v carried as two bfloat16 numbers hi = bf16(v), lo = bf16(v - hi), a row of
 // d values stored as [hi_0 .. hi_{d-1} | lo_0 .. lo_{d-1}] (2 d elements); a GEMM whose k runs over
 // both halves while the weight row repeats computes w . hi + w . lo = w . v to ~2^-17.
-enum DType { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_BF16X2 = 3 };
+// MXFP8 matrix (OCP Microscaling Formats v1.0, MXFP8: E4M3 values with one E8M0 scale per block
+// of 32 consecutive values of a row): `rows` rows of k values are stored as codes [rows][k] (one
+// E4M3 byte each) followed, at byte offset mx_planes_offset(rows, k), by k / 32 scale planes of
+// mx_plane_stride(rows) bytes: the byte X + 127 of block j of row r at plane j, position r.
+// Value = code * 2^X.
+__host__ __device__ inline size_t mx_planes_offset(size_t rows, size_t k) {
+  return (rows * k + 255) / 256 * 256;
+}
+__host__ __device__ inline size_t mx_plane_stride(size_t rows) { return (rows + 15) / 16 * 16; }
+__host__ __device__ inline size_t mx_matrix_bytes(size_t rows, size_t k) {
+  return mx_planes_offset(rows, k) + ((k / 32) * mx_plane_stride(rows) + 255) / 256 * 256;
+}
+
+// DT_MX8: an MXFP8 matrix (above).
+enum DType { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_BF16X2 = 3, DT_MX8 = 4 };
 enum Epilogue {
   EPI_BIAS = 0,
   EPI_BIAS_GELU = 1,
@@ -23,7 +37,7 @@ enum Epilogue {
 };
 
 // y[rows, d] = LayerNorm(x[rows, d]) * gamma + beta, stored as out_dtype (DT_BF16X2: rows of
-// 2 d, hi then lo).  d % 4 == 0, d <= 4096.
+// 2 d, hi then lo; DT_MX8: an MXFP8 matrix of rows x d, d % 64 == 0).  d % 4 == 0, d <= 4096.
 hipError_t launch_layernorm(const float* x, const float* gamma, const float* beta, void* y,
                             int rows, int d, int out_dtype, hipStream_t st);
 
@@ -68,7 +82,20 @@ struct LnFuse {
 struct KMap {
   int kb, nseg, xmask, wmask, wrow;
 };
+// Scale planes of the MXFP8 operands of one GEMM (x: the activation rows, w: the weight rows,
+// c: the MXFP8 output of EPI_BIAS_GELU), each plane's stride in bytes.
+struct MxPlanes {
+  const uint8_t* x;
+  int x_stride;
+  const uint8_t* w;
+  int w_stride;
+  uint8_t* c;
+  int c_stride;
+};
 // kmap: nullptr for the plain contraction over k; else k == kmap->nseg * kmap->kb.
+// DT_MX8: a and w are MXFP8 matrices ([m][k] and [n][k] codes, lda == k, followed by their scale
+// planes); EPI_BIAS writes fp16, EPI_BIAS_GELU an MXFP8 [m][n] matrix (ldc == n), the residual
+// epilogues fp32; no kmap, no EPI_BIAS_HEADMAJOR.
 hipError_t launch_linear(const void* a, int lda, const void* w, const float* bias,
                          const float* residual, void* c, int ldc, int m, int n, int k, int dtype,
                          int epilogue, hipStream_t st, float* partial = nullptr,
@@ -112,6 +139,10 @@ struct DequantSegments {
 hipError_t launch_quantize(const float* w, void* codes, void* scales, int n, int k, int bits,
                            hipStream_t st);
 hipError_t launch_dequant(const DequantSegments& seg, int bits, hipStream_t st);
+// MXFP8: src [n][k] fp32 (16-byte aligned rows, k % 32 == 0) -> rows r0 .. r0 + n - 1 of the
+// MXFP8 matrix of `total` rows at dst (codes and scale planes; mx_planes_offset).
+hipError_t launch_mx_quantize(const float* src, void* dst, int n, int k, int r0, int total,
+                              hipStream_t st);
 
 // Conv front end rearrangements (stem.hip).  dst[o][j * cin + i] = w[o][i][j] (zero past 3 cin,
 // kp columns); unfold_s1: out[b t + i][j c + q] = src[b][i + j - 1][q] (fp32 src, kp columns);

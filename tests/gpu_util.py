@@ -16,7 +16,7 @@ from speech_transformer_encoder_amd import binding as B  # noqa: E402
 
 PATH_NAMES = {B.WENC_PATH_BF16: "bf16", B.WENC_PATH_FP16: "fp16", B.WENC_PATH_FP32: "fp32",
               B.WENC_PATH_BF16X2: "bf16x2", B.WENC_PATH_BF16X3: "bf16x3", B.WENC_PATH_Q8: "q8",
-              B.WENC_PATH_Q4: "q4"}
+              B.WENC_PATH_Q4: "q4", B.WENC_PATH_MXFP8: "mxfp8"}
 
 
 def require_gpu():

@@ -52,7 +52,7 @@ def test_sizes():
     assert bf >= 12 * 1280 * 1280 * 2 and f32 >= 12 * 1280 * 1280 * 4
     assert bf % 256 == 0 and f32 % 256 == 0
     assert B.whisper_enc_layer_bytes(100, 5120, 0) == 0
-    assert B.whisper_enc_layer_bytes(1280, 5120, 7) == 0
+    assert B.whisper_enc_layer_bytes(1280, 5120, 8) == 0
     ws = B.whisper_enc_workspace_bytes(16, 1500, 1280, 20, 5120, B.WENC_PATH_BF16)
     assert ws >= 16 * 1500 * (1280 + 5120) * 2
     assert B.whisper_enc_workspace_bytes(1, 1500, 1280, 16, 5120, 0) == 0  # head_dim 80
@@ -92,7 +92,7 @@ def test_bf16x2_path_sizes_and_validation(lib):
     P3 = B.WENC_PATH_BF16X3
     weights = 4 * d * d + 2 * d * f
     assert B.whisper_enc_layer_bytes(d, f, P3) >= B.whisper_enc_layer_bytes(d, f, P1) + 2 * weights
-    assert B.whisper_enc_workspace_bytes(1, 1500, 1280, 20, 5120, 7) == 0
+    assert B.whisper_enc_workspace_bytes(1, 1500, 1280, 20, 5120, 8) == 0
 
 
 def test_strerror(lib):
@@ -115,7 +115,7 @@ def test_block_validation(lib):
     assert _block(lib, heads=5) == B.WENC_ERR_ARG              # d % heads != 0
     assert _block(lib, d=100, heads=1) == B.WENC_ERR_ARG
     assert _block(lib, f=100) == B.WENC_ERR_ARG
-    assert _block(lib, path=7) == B.WENC_ERR_ARG
+    assert _block(lib, path=8) == B.WENC_ERR_ARG
     assert _block(lib, batch=-1) == B.WENC_ERR_ARG
     assert _block(lib, x=None) == B.WENC_ERR_ARG
     assert _block(lib, layer=None) == B.WENC_ERR_ARG
@@ -312,3 +312,43 @@ def test_quantized_paths_sizes_and_validation(lib):
     dq = lambda *a: lib.whisper_enc_dequantize_matrix(*a)  # noqa: E731
     assert dq(FAKE + 8, FAKE, FAKE, 4, 64, 8, None) == B.WENC_ERR_ARG
     assert dq(FAKE, FAKE, None, 4, 64, 4, None) == B.WENC_ERR_ARG
+
+
+def test_mxfp8_sizes_and_validation(lib):
+    """MXFP8 matrices: rows * k code bytes rounded up to 256, then k / 32 scale planes of rows
+    rounded up to 16 bytes, the planes rounded up to 256.  An MXFP8 layer holds QKV, fc1 and fc2
+    as MXFP8 matrices and the out-projection as fp16; its workspace is the fp16 path's (every
+    MXFP8 activation fits the fp16 region it replaces).  The attention, front-end and cross K/V
+    entry points do not take the MXFP8 path."""
+    MX = B.WENC_PATH_MXFP8
+    assert B.whisper_enc_mx_bytes(5, 32) == 256 + 256
+    assert B.whisper_enc_mx_bytes(1500, 1280) == 1500 * 1280 + 40 * 1504  # both multiples of 256
+    assert B.whisper_enc_mx_bytes(16, 64) == 1024 + 256
+    for bad in [(-1, 64), (4, 48), (4, 0), (4, 1 << 17)]:
+        assert B.whisper_enc_mx_bytes(*bad) == 0
+    mxb = lambda r, k: B.whisper_enc_mx_bytes(r, k)  # noqa: E731
+    rnd = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    for d, f in [(384, 1536), (1280, 5120), (512, 2048)]:
+        fp32_sections = rnd(4 * d) * 6 + rnd(4 * 3 * d) + rnd(4 * f)  # LN, biases
+        want = fp32_sections + mxb(3 * d, d) + rnd(2 * d * d) + mxb(f, d) + mxb(d, f)
+        assert B.whisper_enc_layer_bytes(d, f, MX) == want, d
+    for args in [(16, 1500, 1280, 20, 5120), (1, 1500, 384, 6, 1536), (3, 77, 512, 8, 2048)]:
+        assert B.whisper_enc_workspace_bytes(*args, MX) == \
+            B.whisper_enc_workspace_bytes(*args, B.WENC_PATH_FP16)
+    assert lib.whisper_enc_attention(FAKE, FAKE, FAKE, FAKE, 1, 64, 1, 192, 64, MX, None) == \
+        B.WENC_ERR_ARG
+    assert B.whisper_enc_stem_bytes(80, 384, 1500, MX) == 0
+    assert B.whisper_enc_cross_kv_bytes(384, 4, MX) == 0
+    mq = lambda *a: lib.whisper_enc_mx_quantize(*a)  # noqa: E731
+    assert mq(FAKE, FAKE + (1 << 24), 4, 48, None) == B.WENC_ERR_ARG      # k % 32
+    assert mq(FAKE + 8, FAKE + (1 << 24), 4, 64, None) == B.WENC_ERR_ARG  # alignment
+    assert mq(FAKE, FAKE + 256, 4, 64, None) == B.WENC_ERR_ARG            # dst overlaps src
+    assert mq(None, FAKE, 4, 64, None) == B.WENC_ERR_ARG
+    assert mq(None, None, 0, 64, None) == B.WENC_OK
+    ln = lambda *a: lib.whisper_enc_layernorm(*a)  # noqa: E731
+    assert ln(FAKE, FAKE, FAKE, FAKE + 512, 4, 64, B.WENC_DTYPE_MXFP8, None) == B.WENC_ERR_ARG
+    assert ln(FAKE, FAKE, FAKE, FAKE, 4, 64, 4, None) == B.WENC_ERR_ARG  # no such dtype
+    lin = lambda *a: lib.whisper_enc_linear(*a)  # noqa: E731
+    assert lin(FAKE, FAKE, FAKE, None, FAKE, 64, 64, 48, MX, B.WENC_EPI_BIAS, None) == B.WENC_ERR_ARG
+    assert lin(FAKE, FAKE, FAKE, None, FAKE, 1 << 24, 64, 256, MX, B.WENC_EPI_BIAS, None) == \
+        B.WENC_ERR_UNSUPPORTED  # m * k >= 2^31

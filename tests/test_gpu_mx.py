@@ -1,0 +1,327 @@
+"""The MXFP8 path (gfx950's block-scaled fp8 MFMA) on the GPU against the CPU oracle, through the
+C ABI.
+
+* Quantiser: codes and scale bytes are integers decided by exact operations (scaling by a power
+  of two, one rounding to E4M3) on the same fp32 inputs on both sides: compared exactly.
+* LayerNorm with MXFP8 output: the GPU quantises its fp32 LayerNorm values, the oracle the
+  float64 values rounded to fp32.  The two fp32 values differ by a few units in the last place,
+  so a value lying that close to a rounding boundary (or a block maximum that close to a scale
+  boundary) can round the other way: at most 1e-4 of the codes may differ, each by one step.
+* Projections: MXFP8 operands written from the oracle's quantiser, the GPU's products against the
+  exact float64 products of the same values, within the error model of the scaled MFMA measured
+  on gfx950 (inside a 32-k block, products cut toward zero to 2^-13 of the block's largest; see
+  _hw_bound) plus fp32 accumulation and the rounding of an fp16 output (2^-11 relative); the
+  GELU output is MXFP8 again and must be the rounding of a value within that bound.
+* Blocks and stacks: against the oracle of the same method (``oracle.mxfp8_layer`` weights and
+  ``act=oracle.mx_values`` on the QKV, fc1 and fc2 operands), with the exact float64 block beside
+  it; the bars are stated above the block tests.
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from speech_transformer_encoder_amd import binding as B
+from speech_transformer_encoder_amd import synth
+from speech_transformer_encoder_amd.encoder import build_from_workload, to_device_input
+from tests import mx_util
+from tests.gpu_util import dev, errors, host, report, require_gpu
+
+pytestmark = pytest.mark.gpu
+MX = B.WENC_PATH_MXFP8
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _to_gpu_bytes(buf):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(buf)).cuda()
+
+
+def _from_gpu_bytes(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _matrix(seed, rows, k):
+    """N(0, 1) rows at magnitudes from 2^-30 to 2^30, with special blocks: all zero, exact E4M3
+    values times a power of two, exact midpoints between neighbours (ties), a largest magnitude
+    of exactly 448 2^X and one just above it, and values in E4M3's subnormal range."""
+    r = np.random.default_rng([seed, 91])
+    a = r.standard_normal((rows, k)).astype(np.float32)
+    a *= np.exp2(r.integers(-30, 31, (rows, 1))).astype(np.float32)
+    grid = np.array([m * 2.0 ** e for e in range(-6, 9) for m in (1, 1.125, 1.25, 1.375, 1.5,
+                                                                   1.625, 1.75, 1.875)])
+    grid = grid[grid <= 448]
+    if rows > 0:
+        a[0, :32] = 0.0
+    if rows > 1:
+        a[1, :32] = r.choice(grid, 32) * np.sign(r.standard_normal(32)) * 2.0 ** -20
+    if rows > 2:  # ties: midpoints of neighbouring E4M3 values, with amax 448 fixing X = 0
+        i = r.integers(0, len(grid) - 1, 32)
+        a[2, :32] = (grid[i] + grid[i + 1]) / 2
+        a[2, 0] = 448.0
+    if rows > 3:
+        a[3, :32] = r.standard_normal(32)
+        a[3, 5] = np.nextafter(np.float32(448.0), np.float32(1e9))  # just above 448: X = 1
+    if rows > 4:
+        a[4, :32] = r.standard_normal(32) * 2.0 ** -14  # many in E4M3's subnormal range
+        a[4, 0] = 300.0 * 2.0 ** -10
+    return a.astype(np.float32)
+
+
+@pytest.mark.parametrize("rows,k", [(5, 32), (64, 1280), (1280, 5120), (3, 96), (1499, 128)])
+def test_mx_quantize_exact(rows, k):
+    import torch
+    a = _matrix(rows + k, rows, k)
+    print(f"[case] mx quantize rows={rows} k={k}", flush=True)
+    out = torch.zeros(B.whisper_enc_mx_bytes(rows, k), dtype=torch.uint8, device="cuda")
+    B.whisper_enc_mx_quantize(dev(a), out, rows, k)
+    codes, sbytes, _ = mx_util.decode(_from_gpu_bytes(out), rows, k)
+    ref = mx_util.oracle_bytes(a)[0]
+    rcodes, rsbytes, _ = mx_util.decode(ref, rows, k)
+    np.testing.assert_array_equal(sbytes, rsbytes)
+    np.testing.assert_array_equal(codes, rcodes)
+
+
+def _step(vals, sbytes):
+    """E4M3 quantisation step at each value under its block's scale 2^X: 2^(e - 3) for a value
+    of binade e, and the subnormal step 2^(X - 9) below 2^(X - 6)."""
+    x = np.repeat(sbytes.astype(np.float64) - 127, 32, axis=1)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.abs(vals)))
+    return np.exp2(np.maximum(e, x - 6) - 3)
+
+
+def _near_equal_codes(got_vals, got_s, ref_vals, ref_s, frac=1e-4):
+    """At most `frac` of the values (and of the scales) differ, each value by one quantisation
+    step and each scale by one."""
+    dv = got_vals != ref_vals
+    ds = got_s != ref_s
+    print(f"[mx] differing values {int(dv.sum())} of {got_vals.size}, scales {int(ds.sum())} of "
+          f"{got_s.size}", flush=True)
+    assert dv.sum() <= max(2, frac * got_vals.size)
+    assert ds.sum() <= max(1, frac * got_s.size)
+    assert np.all(np.abs(got_s.astype(int) - ref_s.astype(int)) <= 1)
+    step = np.maximum(_step(got_vals, got_s), _step(ref_vals, ref_s))
+    assert np.all(np.abs(got_vals - ref_vals) <= step * (1 + 1e-12)), \
+        (got_vals[dv][:8], ref_vals[dv][:8])
+
+
+@pytest.mark.parametrize("rows,d", [(4, 64), (300, 384), (1500, 1280), (517, 512)])
+def test_layernorm_mx(rows, d):
+    import torch
+    r = np.random.default_rng([rows, d, 5])
+    x = (r.standard_normal((rows, d)) * np.exp2(r.integers(-3, 6, (rows, 1)))).astype(np.float32)
+    g = (1 + 0.1 * r.standard_normal(d)).astype(np.float32)
+    b = (0.1 * r.standard_normal(d)).astype(np.float32)
+    print(f"[case] layernorm mx rows={rows} d={d}", flush=True)
+    out = torch.zeros(B.whisper_enc_mx_bytes(rows, d), dtype=torch.uint8, device="cuda")
+    B.whisper_enc_layernorm(dev(x), dev(g), dev(b), out, rows, d, B.WENC_DTYPE_MXFP8)
+    _, s, vals = mx_util.decode(_from_gpu_bytes(out), rows, d)
+    ln32 = oracle.layer_norm(x, g, b).astype(np.float32)
+    _, rs, rvals = mx_util.decode(mx_util.oracle_bytes(ln32)[0], rows, d)
+    _near_equal_codes(vals, s, rvals, rs)
+
+
+def _block_max(v):
+    """Largest magnitude of each 32-column block of each row: [rows, k / 32]."""
+    return np.abs(v).reshape(v.shape[0], -1, 32).max(axis=2)
+
+
+def _hw_bound(av, wv):
+    """Error bound of the scaled-MFMA products against the exact sums of the same MXFP8 values.
+
+    Measured on gfx950 (exact small-integer cases): inside each 32-k block the products are
+    aligned to the block's largest one and cut toward zero to multiples of 2^(E - 13), E the
+    binade of that product (a product 2^-14 of it is dropped), and the block sums are then added
+    in fp32.  So per block at most 32 * 2^-13 * max|p| <= 2^-8 * max|a| * max|w| of the block,
+    plus fp32 rounding of the K / 32 additions."""
+    k = av.shape[1]
+    return (2.0 ** -8 * (_block_max(av) @ _block_max(wv).T)
+            + 2.0 ** -24 * (k // 32 + 2) * (np.abs(av) @ np.abs(wv).T))
+
+
+@pytest.mark.parametrize("m,n,k", [(300, 192, 256), (1500, 1280, 5120), (1499, 3840, 1280),
+                                   (64, 64, 64)])
+@pytest.mark.parametrize("epi", [B.WENC_EPI_BIAS, B.WENC_EPI_BIAS_RESIDUAL, B.WENC_EPI_BIAS_GELU])
+def test_linear_mx(m, n, k, epi):
+    import torch
+    r = np.random.default_rng([m, n, k, 17])
+    a = r.standard_normal((m, k)).astype(np.float32)
+    w = (r.standard_normal((n, k)) * 0.02).astype(np.float32)
+    w[:, :32] *= 50.0  # blocks of one row at different scales
+    bias = (r.standard_normal(n) * 0.1).astype(np.float32)
+    res = r.standard_normal((m, n)).astype(np.float32)
+    abytes, av = mx_util.oracle_bytes(a)
+    wbytes, wv = mx_util.oracle_bytes(w)
+    print(f"[case] linear mx m={m} n={n} k={k} epi={epi}", flush=True)
+    ga, gw = _to_gpu_bytes(abytes), _to_gpu_bytes(wbytes)
+    exact = av @ wv.T + bias.astype(np.float64)
+    hw = _hw_bound(av, wv)
+    if epi == B.WENC_EPI_BIAS:
+        c = torch.empty((m, n), dtype=torch.float16, device="cuda")
+        B.whisper_enc_linear(ga, gw, dev(bias), None, c, m, n, k, MX, epi)
+        err = np.abs(host(c) - exact)
+        print(f"[mx] fp16 out: max |err| / bound = {np.max(err / (hw + 2.0 ** -11 * np.abs(exact))):.3f}",
+              flush=True)
+        assert np.all(err <= hw + 2.0 ** -11 * np.abs(exact) + 2.0 ** -24), err.max()
+    elif epi == B.WENC_EPI_BIAS_RESIDUAL:
+        c = dev(res)
+        B.whisper_enc_linear(ga, gw, dev(bias), c, c, m, n, k, MX, epi)
+        ref = res.astype(np.float64) + exact
+        err = np.abs(host(c) - ref)
+        print(f"[mx] fp32 out: max |err| / bound = {np.max(err / hw):.3f}", flush=True)
+        assert np.all(err <= hw + 2.0 ** -23 * (np.abs(ref) + np.abs(res) + np.abs(bias))), err.max()
+    else:
+        # MXFP8 output: each value is the E4M3 rounding (under its block's scale) of gelu of a sum
+        # within the bound above of the exact one; gelu's slope is at most 1.13 in magnitude, and
+        # its A&S 7.1.26 evaluation adds at most 2^-20 |z|.  Scales match the oracle's except
+        # where a block maximum lies that close to a scale boundary.
+        c = torch.zeros(B.whisper_enc_mx_bytes(m, n), dtype=torch.uint8, device="cuda")
+        B.whisper_enc_linear(ga, gw, dev(bias), None, c, m, n, k, MX, epi)
+        _, s, vals = mx_util.decode(_from_gpu_bytes(c), m, n)
+        g = oracle.gelu_erf(exact)
+        _, rs, rvals = mx_util.decode(mx_util.oracle_bytes(g)[0], m, n)
+        ds = s != rs
+        print(f"[mx] gelu out: codes differing from the oracle's rounding "
+              f"{int((vals != rvals).sum())} of {vals.size}, scales {int(ds.sum())}", flush=True)
+        assert ds.sum() <= max(1, 1e-3 * s.size)
+        assert np.all(np.abs(s.astype(int) - rs.astype(int)) <= 1)
+        step = np.maximum(_step(vals, s), _step(g, s))
+        tol = 0.5 * step + 1.13 * hw + 2.0 ** -20 * np.abs(exact) + 2.0 ** -40
+        assert np.all(np.abs(vals - g) <= tol), np.max(np.abs(vals - g) / tol)
+
+
+# ------------------------------------------------------------------ blocks and stacks
+#
+# Bars.  One block from identical inputs: against the MXFP8 oracle, the block's bar (max_rel 2e-2,
+# MAE 1e-3; measured 1.1e-2 / 7e-5 on the tiny block).  Several blocks (or a batch with outlier
+# rows): each quantiser turns the last-bit differences of the fp16 attention and fp32 arithmetic
+# into whole-step flips that later blocks amplify, so the GPU and the oracle follow nearby but
+# distinct trajectories of the same method (measured GPU-vs-MXFP8-oracle MAE 1.0e-2 after 6 base
+# blocks, against the method's own 2.3e-2).  There the bar is that the GPU adds no error of its
+# own: its distance from the exact block is within 10 % (MAE) and 25 % (max_rel) of the MXFP8
+# oracle's (measured ratios 1.00 and 0.99 on the base stack, 1.00 and 1.04 on two large-v3
+# blocks).  A wrong scale, layout or dropped block moves the GPU result by the size of the
+# method's error or more and fails it.
+
+BLOCK_BAR = {"max_rel": 2e-2, "mae": 1e-3}
+REL_MAE, REL_MAX = 1.10, 1.25
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _assert_mx(tag, got, mx_ref, exact, single_block):
+    e_mx, e_gx, e_m = errors(got, mx_ref), errors(got, exact), errors(mx_ref, exact)
+    report(f"{tag} [mxfp8] vs the MXFP8 oracle", e_mx)
+    report(f"{tag} [mxfp8] vs the exact oracle", e_gx)
+    report(f"{tag} MXFP8 oracle vs the exact oracle (the method's own error)", e_m)
+    assert e_mx["finite"] and e_gx["finite"], tag
+    if single_block:
+        assert e_mx["max_rel"] <= BLOCK_BAR["max_rel"] and e_mx["mae"] <= BLOCK_BAR["mae"], (tag, e_mx)
+    assert e_gx["mae"] <= REL_MAE * e_m["mae"], (tag, e_gx, e_m)
+    assert e_gx["max_rel"] <= REL_MAX * e_m["max_rel"], (tag, e_gx, e_m)
+
+
+def _check_mx(got, w, tag, n_layers=None, ln_post=True, single_block=False):
+    cfg = w.cfg
+    layers = [oracle.mxfp8_layer(p) for p in w.layers[:n_layers]]
+    post = w.ln_post if ln_post else None
+    ref = oracle.encoder_stack(w.x, layers, cfg.heads, post, act=oracle.mx_values)
+    exact = oracle.encoder_stack(w.x, w.layers[:n_layers], cfg.heads, post)
+    _assert_mx(tag, got, ref, exact, single_block)
+
+
+def test_block_mx_small_ragged():
+    cfg = synth.CONFIGS["tiny_block"].with_(batch=2, t=200)
+    w = synth.make_workload(cfg)
+    print("[case] block mx small", flush=True)
+    enc = build_from_workload(w, MX)
+    got = host(enc.forward(to_device_input(w.x), final_norm=False))
+    _check_mx(got, w, "tiny block b2 t200", ln_post=False, single_block=True)
+
+
+def test_block_mx_tiny_full():
+    w = synth.make_workload(synth.CONFIGS["tiny_block"])
+    print("[case] block mx tiny full", flush=True)
+    enc = build_from_workload(w, MX)
+    got = host(enc.forward(to_device_input(w.x), final_norm=False))
+    _check_mx(got, w, "tiny_block", ln_post=False, single_block=True)
+
+
+def test_stack_mx_base():
+    w = synth.make_workload(synth.CONFIGS["base_stack"])
+    print("[case] stack mx base", flush=True)
+    enc = build_from_workload(w, MX)
+    got = host(enc.forward(to_device_input(w.x)))
+    _check_mx(got, w, "base_stack")
+
+
+def test_stack_mx_large_v3_two_blocks():
+    w = synth.make_workload(synth.CONFIGS["large_v3_stack"], n_layers=2)
+    print("[case] stack mx large-v3 2 blocks", flush=True)
+    enc = build_from_workload(w, MX)
+    got = host(enc.forward(to_device_input(w.x)))
+    _check_mx(got, w, "large-v3 2 blocks")
+
+
+@pytest.mark.parametrize("name", ["small_stack", "large_v3_stack"])
+def test_stack_mx_full_depth(name):
+    """The full 12- and 32-block stacks: sampled rows of the exact oracle and of the MXFP8
+    oracle, both stored by tests/golden/make_golden.py."""
+    cfg = synth.CONFIGS[name]
+    w = synth.make_workload(cfg)
+    print(f"[case] stack mx full depth {name}", flush=True)
+    enc = build_from_workload(w, MX)
+    got = host(enc.forward(to_device_input(w.x)))[0]
+    g = np.load(os.path.join(GOLDEN, f"{name}_rows.npz"))
+    m = np.load(os.path.join(GOLDEN, f"{name}_mxfp8_rows.npz"))
+    np.testing.assert_array_equal(g["rows"], m["rows"])
+    _assert_mx(name, got[g["rows"]], m["y"], g["y"], single_block=False)
+
+
+def test_block_mx_batched_sampled():
+    """The batched large-v3 block (5 % of the rows x20) on sampled rows of four windows."""
+    cfg = synth.CONFIGS["large_v3_batch16_block"]
+    w = synth.make_workload(cfg)
+    print("[case] block mx batched large-v3", flush=True)
+    enc = build_from_workload(w, MX)
+    got = host(enc.forward(to_device_input(w.x), final_norm=False))
+    p = oracle.mxfp8_layer(w.layers[0])
+    g, r, x = [], [], []
+    for b in range(0, cfg.batch, 5):
+        big = np.where(np.abs(w.x[b]).max(axis=1) > 10)[0][:2]
+        rows = np.unique(np.concatenate([[0, 1, 777, cfg.t - 1], big]))
+        r.append(oracle.encoder_block_rows(w.x[b], p, cfg.heads, rows, act=oracle.mx_values))
+        x.append(oracle.encoder_block_rows(w.x[b], w.layers[0], cfg.heads, rows))
+        g.append(got[b][rows])
+    _assert_mx("batched large-v3 sampled", np.concatenate(g), np.concatenate(r),
+               np.concatenate(x), single_block=False)
+
+
+def test_stack_mx_equals_chained_blocks():
+    """As for the other paths: the stack call (LayerNorms fused into the split-k reductions,
+    writing MXFP8) equals one block call per layer plus the final LayerNorm, bit for bit."""
+    import torch
+    cfg = synth.CONFIGS["base_stack"].with_(n_layers=3)
+    w = synth.make_workload(cfg)
+    enc = build_from_workload(w, MX)
+    x = to_device_input(w.x)
+    print("[case] mx stack vs chained blocks", flush=True)
+    stacked = host(enc.forward(x))
+    batch, t, d = x.shape
+    ws = enc.workspace(batch, t)
+    cur, nxt = x.clone(), torch.empty_like(x)
+    for l in range(cfg.n_layers):
+        B.whisper_enc_block_forward(cur, nxt, enc.blob.data_ptr() + l * enc.layer_bytes, batch, t,
+                                    d, cfg.heads, cfg.ffn_dim, MX, ws, ws.numel())
+        cur, nxt = nxt, cur
+    g, b = enc.ln_post
+    B.whisper_enc_layernorm(cur, g, b, nxt, batch * t, d, B.WENC_DTYPE_F32)
+    np.testing.assert_array_equal(stacked, host(nxt))

@@ -85,6 +85,11 @@ constexpr int G_STAGE = (G_N + G_M) * G_K;  // 16-bit elements per stage
 // alone, not for the stores.
 // tiles_lim: the first tiles_lim tiles of the grouped order (the rest, when the tiles do not
 // divide into whole rounds, go to gemm16_small_kernel as half tiles).
+//
+// T = mx8_t: MXFP8 operands on v_mfma_scale_f32_32x32x64_f8f6f4.  A 128-byte LDS row then holds
+// 128 k values, two MFMA steps of 64 (the 16-bit steps 0, 1 and 2, 3 by their chunks); per k tile
+// wavefront 0 copies the tile's four 32-k scale blocks of the 256 W rows and wavefront 1 those of
+// the X rows into a 2 KB window after the stage.  EPI_BIAS writes fp16, EPI_BIAS_GELU MXFP8.
 template <typename T, int EPI>
 __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __restrict__ X,
                                                              int lda,
@@ -92,22 +97,28 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
                                                              const float* __restrict__ bias,
                                                              const float* residual, void* C,
                                                              int ldc, int M, int N, int K,
-                                                             int tiles_lim, KMap km) {
+                                                             int tiles_lim, KMap km, MxPlanes mx) {
+  constexpr bool MX = std::is_same<T, mx8_t>::value;
+  using OutT = typename std::conditional<MX, f16_t, T>::type;  // type of 16-bit outputs
+  constexpr int EB = MX ? 1 : 2;                                // operand bytes per k value
+  constexpr bool kMxOut = MX && EPI == EPI_BIAS_GELU;
+  static_assert(!MX || (EPI != EPI_BIAS_HEADMAJOR && EPI != EPI_BIAS_GELU_X2), "MXFP8 epilogues");
   constexpr bool kResidual = EPI == EPI_BIAS_RESIDUAL || EPI == EPI_BIAS_GELU_RESIDUAL;
   // Head-major rows scatter over windows (64-bit addresses): those stores stay plain, predicated
   // global stores, and the next tile waits for them.
   constexpr bool kBufferOut = EPI != EPI_BIAS_HEADMAJOR;
   // Vector-memory operations of one wavefront's epilogue: 4 row blocks x (8 residual loads + 8
-  // stores), or 4 x 4 stores.
-  constexpr int kEpiOps = kResidual ? 64 : EPI == EPI_BIAS_GELU_X2 ? 32 : 16;
-  __shared__ __attribute__((aligned(1024))) uint16_t s0[G_STAGE];
-  __shared__ __attribute__((aligned(1024))) uint16_t s1[G_STAGE];
+  // stores), or 4 x 4 stores (MXFP8 output: 4 x (4 code + 4 scale stores)).
+  constexpr int kEpiOps = kResidual ? 64 : (EPI == EPI_BIAS_GELU_X2 || kMxOut) ? 32 : 16;
+  constexpr int kStage = G_STAGE + (MX ? 1024 : 0);  // + the MXFP8 scale window (2 KB)
+  __shared__ __attribute__((aligned(1024))) uint16_t s0[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t s1[kStage];
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave / G_WM, wm = wave % G_WM;
   const int tiles_m = (M + G_M - 1) / G_M, tiles_n = (N + G_N - 1) / G_N;
   const int tiles = min(tiles_m * tiles_n, tiles_lim);
-  const int nk = K / G_K;
+  const int nk = K / (G_K * 2 / EB);  // k tiles of 128 bytes per row
   const int per_xcd = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
   const int t_begin = (int)((long)tiles * xcd / 8), t_end = (int)((long)tiles * (xcd + 1) / 8);
@@ -116,7 +127,11 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
   // km: k segments of km.kb (the bf16 hi / lo pairs of the BF16X2 / X3 paths; one segment
   // otherwise); weight rows of km.wrow elements.
   const int nkb = km.kb / G_K, kw = km.wrow;
-  const int stepW = 64 * kw * 2, stepX = 64 * lda * 2;
+  const int stepW = 64 * kw * EB, stepX = 64 * lda * EB;
+  // Copies per wavefront and k tile (MXFP8: one more on wavefronts 0 and 1, the scale blocks).
+  const int LT = 2 * G_LPO + ((MX && wave < 2) ? 1 : 0);
+  const u32x4 rWs = buffer_rsrc(mx.w, MX ? (uint32_t)((K / 32) * mx.w_stride) : 0u);
+  const u32x4 rXs = buffer_rsrc(mx.x, MX ? (uint32_t)((K / 32) * mx.x_stride) : 0u);
 
   int n0 = 0, m0 = 0;
   u32x4 rW, rX;
@@ -130,8 +145,10 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
     n0 = tn * G_N;
     m0 = tm * G_M;
     const int wrows = min(N - n0, G_N), xrows = min(M - m0, G_M);
-    rW = buffer_rsrc(W + (size_t)n0 * kw, (uint32_t)(wrows * kw * 2));
-    rX = buffer_rsrc(X + (size_t)m0 * lda, (uint32_t)(xrows * lda * 2));
+    rW = buffer_rsrc(reinterpret_cast<const char*>(W) + (size_t)n0 * kw * EB,
+                     (uint32_t)(wrows * kw * EB));
+    rX = buffer_rsrc(reinterpret_cast<const char*>(X) + (size_t)m0 * lda * EB,
+                     (uint32_t)(xrows * lda * EB));
   };
 
   f32x16 acc[G_NA][G_NB];
@@ -146,12 +163,24 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
     // writing row (l >> 3), slot (l & 7), which holds chunk slot ^ ((row >> 1) & 7).
     const int lrow = 8 * wave + (lane >> 3);
     const int lchunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
-    const int voW = lrow * kw * 2 + lchunk * 16, voX = lrow * lda * 2 + lchunk * 16;
+    const int voW = lrow * kw * EB + lchunk * 16, voX = lrow * lda * EB + lchunk * 16;
     auto load_tile = [&](int kt, const uint16_t* st) {
-      const int seg = (kt >= nkb) + (kt >= 2 * nkb), kk = kt - seg * nkb;
-      const int ko = (((km.xmask >> seg) & 1) * nkb + kk) * (G_K * 2);
-      const int kow = (((km.wmask >> seg) & 1) * nkb + kk) * (G_K * 2);
+      int ko, kow;
       const uint32_t base = lds_addr(st);
+      if constexpr (MX) {
+        ko = kow = kt * 128;
+        // Scale window: lane l copies plane 4 kt + (l >> 4), rows 16 (l & 15) .. of the tile
+        // (byte [plane][row] at plane * 256 + row).
+        const int pl = 4 * kt + (lane >> 4), r16 = (lane & 15) * 16;
+        if (wave == 0)
+          lds_copy16(rWs, base + G_STAGE * 2, pl * mx.w_stride + n0 + r16);
+        else if (wave == 1)
+          lds_copy16(rXs, base + G_STAGE * 2 + 1024u, pl * mx.x_stride + m0 + r16);
+      } else {
+        const int seg = (kt >= nkb) + (kt >= 2 * nkb), kk = kt - seg * nkb;
+        ko = (((km.xmask >> seg) & 1) * nkb + kk) * (G_K * 2);
+        kow = (((km.wmask >> seg) & 1) * nkb + kk) * (G_K * 2);
+      }
 #pragma unroll
       for (int i = 0; i < G_LPO; ++i)
         lds_copy16(rW, base + (uint32_t)(i * G_WAVES + wave) * 1024u, voW + i * stepW + kow);
@@ -182,7 +211,42 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
 #pragma unroll
       for (int a = 0; a < G_NA; ++a)
 #pragma unroll
-        for (int b = 0; b < G_NB; ++b) acc[a][b] = mfma32x32x16<T>(fa[a], fb[b], acc[a][b]);
+        for (int b = 0; b < G_NB; ++b) acc[a][b] = mfma32x32x16<OutT>(fa[a], fb[b], acc[a][b]);
+    };
+    // MXFP8 step s of a tile (k 64 s .. 64 s + 63): the fragments of the 16-bit steps 2 s and
+    // 2 s + 1 (lo, hi) and each lane's scale byte of 32-k block 2 s + g.
+    auto read_scales = [&](const uint16_t* st, int s, int (&sa)[G_NA], int (&sb)[G_NB]) {
+      const uint8_t* w = reinterpret_cast<const uint8_t*>(st) + G_STAGE * 2 + (2 * s + g) * 256;
+#pragma unroll
+      for (int a = 0; a < G_NA; ++a) sa[a] = w[wn * G_TN + a * 32 + frow];
+#pragma unroll
+      for (int b = 0; b < G_NB; ++b) sb[b] = w[1024 + wm * G_TM + b * 32 + frow];
+    };
+    auto frag_a = [&](const uint16_t* st, int s, int a) {
+      const char* base = reinterpret_cast<const char*>(st) + rowA + a * 4096;
+      return lds_frag8(base + xo[2 * s], base + xo[2 * s + 1]);
+    };
+    auto frag_b = [&](const uint16_t* st, int s, int b) {
+      const char* base = reinterpret_cast<const char*>(st) + rowB + b * 4096;
+      return lds_frag8(base + xo[2 * s], base + xo[2 * s + 1]);
+    };
+    // MXFP8 step s of a k tile: its fragments and scale bytes, then its MFMAs.  The scheduling
+    // barriers keep each step's reads after the previous step's MFMAs, so that one set of
+    // fragment registers serves (the accumulators take half the register file).
+    auto step_mx = [&](const uint16_t* st, int s) {
+      u32x8 fa[G_NA], fb[G_NB];
+      int sa[G_NA], sb[G_NB];
+#pragma unroll
+      for (int a = 0; a < G_NA; ++a) fa[a] = frag_a(st, s, a);
+#pragma unroll
+      for (int b = 0; b < G_NB; ++b) fb[b] = frag_b(st, s, b);
+      read_scales(st, s, sa, sb);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = 0; b < G_NB; ++b)
+#pragma unroll
+        for (int a = 0; a < G_NA; ++a) acc[a][b] = mfma_mx8(fa[a], fb[b], sa[a], sb[b], acc[a][b]);
+      __builtin_amdgcn_sched_barrier(0);
     };
     // Interleave the next step's fragment reads with the current step's MFMAs.
     auto sched = [&]() {
@@ -210,18 +274,20 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
       // k tile 0 has landed.  Still allowed in flight: k tile 1 and, after the first tile, the
       // previous epilogue's operations, which were issued after k tile 0.
       if (it == 0 || !kBufferOut) {
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * G_LPO));  // vmcnt(8)
-      } else if constexpr (kEpiOps + 2 * G_LPO >= 63) {
+        if (LT > 2 * G_LPO) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * G_LPO + 1));  // vmcnt(9)
+        else __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * G_LPO));  // vmcnt(8)
+      } else if constexpr (kEpiOps + 2 * G_LPO + (MX ? 1 : 0) >= 63) {
         __builtin_amdgcn_s_waitcnt(0xCF7F);  // vmcnt(63): waits a little more than needed
       } else {
-        constexpr int n = kEpiOps + 2 * G_LPO;
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+        constexpr int n = kEpiOps + 2 * G_LPO, n1 = n + 1;
+        if (LT > 2 * G_LPO) __builtin_amdgcn_s_waitcnt(0x0F70 | (n1 & 15) | ((n1 >> 4) << 14));
+        else __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
       }
     } else {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     }
     __syncthreads();
-    read_frags(s0, 0, fa0, fb0);
+    if constexpr (!MX) read_frags(s0, 0, fa0, fb0);
 
     // One k tile.  `loads` / `next` are compile-time flags so that the loop body has no branch
     // (the scheduling barriers only act inside one basic block).
@@ -240,13 +306,30 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
       mm(fa1, fb1);
       if constexpr (decltype(next)::value) sched();
     };
-    int kt = 0;
-    for (; kt + 2 < nk; ++kt) body(kt, std::true_type{}, std::true_type{});
-    if (kt + 1 < nk) {
-      body(kt, std::false_type{}, std::true_type{});
-      ++kt;
+    if constexpr (MX) {
+      // One k tile = two MXFP8 steps.  One set of fragment registers (the accumulators take half
+      // the register file): each step's reads follow the previous step's MFMAs, and the other
+      // wavefront of the SIMD covers their latency.  A plain loop (one copy of the body) keeps
+      // the register assignment simple.
+      for (int kt = 0; kt < nk; ++kt) {
+        const uint16_t* cur = (kt & 1) ? s1 : s0;
+        step_mx(cur, 0);
+        step_mx(cur, 1);
+        if (kt + 1 < nk) {
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // this wavefront's loads of tile kt + 1 have landed
+          __syncthreads();                     // ... everyone's, and tile kt is no longer read
+          if (kt + 2 < nk) load_tile(kt + 2, cur);
+        }
+      }
+    } else {
+      int kt = 0;
+      for (; kt + 2 < nk; ++kt) body(kt, std::true_type{}, std::true_type{});
+      if (kt + 1 < nk) {
+        body(kt, std::false_type{}, std::true_type{});
+        ++kt;
+      }
+      body(kt, std::false_type{}, std::false_type{});
     }
-    body(kt, std::false_type{}, std::false_type{});
 
     // Epilogue, one 32-row block of the wavefront at a time: (acc + bias) as fp32 into the
     // wavefront's 8 KB of stage 1 (row r, 16-byte chunk c at slot c ^ (r & 15)), then read back
@@ -272,10 +355,13 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
     // Output (and residual) rows of the tile from the wavefront's first column; the range covers
     // the tile's rows below M, or nothing when the wavefront's columns are past N.
     const size_t row0 = (size_t)em0 * ldc + nw;
-    constexpr int esz = kResidual ? 4 : 2;
+    constexpr int esz = kResidual ? 4 : kMxOut ? 1 : 2;
     const int nrec = cols_ok ? min(M - em0, G_M) * ldc * esz : 0;
     const __amdgpu_buffer_rsrc_t rC = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<char*>(C) + row0 * esz, (short)0, nrec, 0x00020000);
+    // MXFP8 output: the scale planes (N / 32 planes of mx.c_stride bytes).
+    const __amdgpu_buffer_rsrc_t rS = __builtin_amdgcn_make_buffer_rsrc(
+        mx.c, (short)0, kMxOut ? (N / 32) * mx.c_stride : 0, 0x00020000);
 #pragma unroll
     for (int b = 0; b < G_NB; ++b) {
 #pragma unroll
@@ -325,8 +411,27 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
             v0 = make_float4(gelu_erf_as(v0.x), gelu_erf_as(v0.y), gelu_erf_as(v0.z), gelu_erf_as(v0.w));
             v1 = make_float4(gelu_erf_as(v1.x), gelu_erf_as(v1.y), gelu_erf_as(v1.z), gelu_erf_as(v1.w));
           }
-          const u32x4 w4 = {pack2<T>(v0.x, v0.y), pack2<T>(v0.z, v0.w), pack2<T>(v1.x, v1.y),
-                            pack2<T>(v1.z, v1.w)};
+          if constexpr (kMxOut) {
+            // MXFP8 output: the four lanes 4 j .. 4 j + 3 hold a row's 32-column block (eight
+            // columns each); its scale byte goes to plane (column / 32), position m.  Both stores
+            // are issued by every lane (the range checks drop rows past M and non-writers), so
+            // the epilogue's operation count stays fixed.
+            float amax = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
+                               fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
+            amax = fmaxf(amax, __shfl_xor(amax, 1));
+            amax = fmaxf(amax, __shfl_xor(amax, 2));
+            const int xe = mx_exponent(amax);
+            const float sc = mx_inv_scale(xe);
+            const u32x2 w2 = {mx_pack4(v0, sc), mx_pack4(v1, sc)};
+            __builtin_amdgcn_raw_buffer_store_b64(w2, rC, (rb + r) * ldc + 4 * c0, 0, 0);
+            const int m = em0 + rb + r;
+            const bool writer = (lane & 3) == 0 && cols_ok && m < M;
+            const int soff = writer ? ((nw + 4 * c0) >> 5) * mx.c_stride + m : 0x7ffffff0;
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(xe + 127), rS, soff, 0, 0);
+            continue;
+          }
+          const u32x4 w4 = {pack2<OutT>(v0.x, v0.y), pack2<OutT>(v0.z, v0.w),
+                            pack2<OutT>(v1.x, v1.y), pack2<OutT>(v1.z, v1.w)};
           if constexpr (EPI == EPI_BIAS_GELU_X2) {
             // lo = bf16(v - hi) N columns to the right (ldc = 2 N)
             const u32x4 l4 = split_lo8(v0, v1, w4);
@@ -538,19 +643,27 @@ __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))
 #pragma unroll
       for (int b = 0; b < NB; ++b) sb[b] = w[1024 + g * HM + wm * TM + b * 32 + frow];
     };
-    u32x4 A0[H_NA], B0[NB], A1[H_NA], B1[NB];
+    u32x8 A[H_NA], Bf[NB];
     int SA[H_NA], SB[NB];
-    auto mm_row = [&](int a) {
+    auto read_mx = [&](const uint16_t* st) {
+      const char* base = reinterpret_cast<const char*>(st);
+      A[0] = lds_frag8(base + rowA + xo[0], base + rowA + xo[1]);
 #pragma unroll
       for (int b = 0; b < NB; ++b)
-        acc[a][b] = mfma_mx8(A0[a], A1[a], B0[b], B1[b], SA[a], SB[b], acc[a][b]);
+        Bf[b] = lds_frag8(base + rowB + b * 2048 + xo[0], base + rowB + b * 2048 + xo[1]);
+#pragma unroll
+      for (int a = 1; a < H_NA; ++a)
+        A[a] = lds_frag8(base + rowA + a * 2048 + xo[0], base + rowA + a * 2048 + xo[1]);
+    };
+    auto mm_row = [&](int a) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[a][b] = mfma_mx8(A[a], Bf[b], SA[a], SB[b], acc[a][b]);
     };
     load_tile(0, s0);
     if (nk > 1) load_tile(1, s1);
     wait_copies(nk > 1);
     __syncthreads();
-    read_frags(s0, 0, A0, B0);
-    read_frags(s0, 1, A1, B1);
+    read_mx(s0);
     read_scales(s0, SA, SB);
     auto body = [&](int kt, const uint16_t* nxt, const uint16_t* ahead) {
       const bool loads = kt + 2 < nk, next = kt + 1 < nk;
@@ -562,8 +675,7 @@ __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))
         // Tile kt + 1 landed everywhere, and every wavefront's reads of tile kt are complete (the
         // barrier waits for them), so tile kt's stage may take tile kt + 3 in body(kt + 1).
         __syncthreads();
-        read_frags(nxt, 0, A0, B0);
-        read_frags(nxt, 1, A1, B1);
+        read_mx(nxt);
         read_scales(nxt, SA, SB);
       }
     };
@@ -931,7 +1043,7 @@ static hipError_t launch16_epi(const uint16_t* X, int lda, const uint16_t* W, co
     const long whole = tiles / grid * grid, tail = tiles - whole;
     const bool halves = tail > 0 && 2 * tail <= grid;
     gemm16_kernel<T, EPI><<<dim3((unsigned)grid), dim3(G_THREADS), 0, st>>>(
-        X, lda, W, bias, residual, c, ldc, m, n, k, (int)(halves ? whole : tiles), kw);
+        X, lda, W, bias, residual, c, ldc, m, n, k, (int)(halves ? whole : tiles), kw, MxPlanes{});
     if (halves)
       gemm16_small_kernel<T, EPI><<<dim3((unsigned)(2 * tail)), dim3(H_THREADS), 0, st>>>(
           X, lda, W, bias, residual, c, ldc, m, n, k, 1, (int)whole, kw, MxPlanes{});
@@ -1015,12 +1127,25 @@ static hipError_t launch_mx_epi(const uint16_t* X, const uint16_t* W, const floa
       return hipGetLastError();
     }
   }
-  if (2 * small < persistent_grid())
+  const int grid = persistent_grid();
+  const long tiles = (long)((m + G_M - 1) / G_M) * ((n + G_N - 1) / G_N);
+  if (tiles >= grid && k % 128 == 0) {
+    // As for 16-bit operands: whole rounds of 256 x 256 tiles on the persistent kernel, a short
+    // last round as 128-column half tiles on the small kernel.
+    const long whole = tiles / grid * grid, tail = tiles - whole;
+    const bool halves = tail > 0 && 2 * tail <= grid;
+    gemm16_kernel<mx8_t, EPI><<<dim3((unsigned)grid), dim3(G_THREADS), 0, st>>>(
+        X, k, W, bias, residual, c, ldc, m, n, k, (int)(halves ? whole : tiles), kw, mx);
+    if (halves)
+      gemm16_small_kernel<mx8_t, EPI><<<dim3((unsigned)(2 * tail)), dim3(H_THREADS), 0, st>>>(
+          X, k, W, bias, residual, c, ldc, m, n, k, 1, (int)whole, kw, mx);
+  } else if (2 * small < grid) {
     gemm16_small_kernel<mx8_t, EPI, 4, 128><<<dim3((unsigned)small2), dim3(H_THREADS), 0, st>>>(
         X, k, W, bias, residual, c, ldc, m, n, k, 1, -1, kw, mx);
-  else
+  } else {
     gemm16_small_kernel<mx8_t, EPI><<<dim3((unsigned)small), dim3(H_THREADS), 0, st>>>(
         X, k, W, bias, residual, c, ldc, m, n, k, 1, -1, kw, mx);
+  }
   return hipGetLastError();
 }
 

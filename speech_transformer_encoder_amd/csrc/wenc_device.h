@@ -74,14 +74,18 @@ struct mx8_t {};
 // block 1, the two halves of the wavefront covering each block together; block b of row r is
 // scaled by 2^(s - 127) with s the low byte of the scale register of lane r + 32 b (measured with
 // exact small-integer products on gfx950).  D has the layout of the 16-bit form.
-__device__ __forceinline__ f32x16 mfma_mx8(u32x4 a_lo, u32x4 a_hi, u32x4 b_lo, u32x4 b_hi, int sa,
-                                           int sb, f32x16 c) {
-  typedef int i32x8 __attribute__((ext_vector_type(8)));
-  const i32x8 a = {(int)a_lo[0], (int)a_lo[1], (int)a_lo[2], (int)a_lo[3],
-                   (int)a_hi[0], (int)a_hi[1], (int)a_hi[2], (int)a_hi[3]};
-  const i32x8 b = {(int)b_lo[0], (int)b_lo[1], (int)b_lo[2], (int)b_lo[3],
-                   (int)b_hi[0], (int)b_hi[1], (int)b_hi[2], (int)b_hi[3]};
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16 mfma_mx8(u32x8 a, u32x8 b, int sa, int sb, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, a),
+                                                         __builtin_bit_cast(i32x8, b), c, 0, 0, 0,
+                                                         sa, 0, sb);
+}
+// An MXFP8 fragment from LDS: bytes 0 .. 15 at lo, 16 .. 31 at hi, read straight into the eight
+// consecutive registers the MFMA takes.
+__device__ __forceinline__ u32x8 lds_frag8(const char* lo, const char* hi) {
+  const u32x4 a = *reinterpret_cast<const u32x4*>(lo), b = *reinterpret_cast<const u32x4*>(hi);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // D(32x32) += A(32x2) * B(2x32) in fp32.  Lane l supplies A[row l%32][k l/32] and

@@ -451,14 +451,16 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
   }
 }
 // Smaller-problem variant (fewer 256 x 256 tiles than CUs, e.g. the 1500-row GEMMs of a single
-// window): 128 (n) x 256 (m) tiles with a 32-wide k tile for a 512-thread workgroup (eight
-// wavefronts, 64 x 64 outputs each, two per SIMD so that one's waits overlap the other's MFMAs
-// even when each CU holds a single workgroup, as at one window), three LDS stages of 64-byte rows
-// (chunk c of row r at slot c ^ ((r >> 2) & 3), conflict-free for the 16-lane fragment phases).
+// window): 128 (n) x 256 (m) tiles for a 512-thread workgroup (eight wavefronts, 64 x 64 outputs
+// each, two per SIMD so that one's waits overlap the other's MFMAs even when each CU holds a
+// single workgroup, as at one window), three LDS stages of KB-byte rows: 128 bytes (a 64-wide k
+// tile of 16-bit values, the persistent kernel's row layout, chunk c of row r at slot
+// c ^ ((r >> 1) & 7)) for the launches, or 64 bytes (chunk c at slot c ^ ((r >> 2) & 3)) for
+// MXFP8 k not a multiple of 128; either way conflict-free for the 16-lane fragment phases.
 // The tile copies are inline assembly (lds_copy16), so the kernel's own s_waitcnt vmcnt is the
 // only wait on them.  (Four wavefronts of 64 x 128 read a third fewer fragments per MFMA but
 // leave one wavefront per SIMD at one workgroup per CU: 12-14 % slower on the one-window QKV and
-// fc1 shapes.)
+// fc1 shapes, measured with 64-byte rows.)
 constexpr int H_N = 128, H_M = 256, H_K = 32;
 constexpr int H_WN = 2, H_WM = 4;
 constexpr int H_TN = H_N / H_WN, H_TM = H_M / H_WM;  // 64 x 64 per wavefront
@@ -477,7 +479,7 @@ constexpr int H_THREADS = 64 * H_WAVES;
 // in the same layout and with the same copies; per k tile, wavefront 0 also copies the tile's two
 // 32-k scale blocks of its 128 W rows and wavefront 1 those of its X rows into a 2 KB window after
 // the stage's operand rows.  EPI_BIAS writes fp16; EPI_BIAS_GELU writes MXFP8 (mx.c).
-template <typename T, int EPI, int WM = H_WM, int HM = H_M>
+template <typename T, int EPI, int WM = H_WM, int HM = H_M, int KB = 64>
 __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))) void gemm16_small_kernel(
     const uint16_t* __restrict__ X, int lda, const uint16_t* __restrict__ W,
     const float* __restrict__ bias, const float* residual, void* C, int ldc, int M, int N, int K,
@@ -485,13 +487,17 @@ __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))
   constexpr bool MX = std::is_same<T, mx8_t>::value;
   using OutT = typename std::conditional<MX, f16_t, T>::type;  // type of 16-bit outputs
   constexpr int EB = MX ? 1 : 2;                           // operand bytes per k value
-  constexpr int KT = 64 / EB;                              // k values per 64-byte LDS row
+  static_assert(KB == 64 || KB == 128, "LDS row bytes");
+  constexpr int KT = KB / EB;                              // k values per LDS row (one k tile)
+  constexpr int NSTEP = KB / 32;                           // 16-bit k16 steps per k tile
+  constexpr int RPC = 1024 / KB;                           // rows per 1 KB copy
+  constexpr int BLK = 32 * KB;                             // LDS bytes of 32 rows
   constexpr int HW = H_WN * WM;                            // wavefronts
   constexpr int TM = HM / WM, NB = TM / 32;                // rows per wavefront, 32-row blocks
-  constexpr int HLW = H_N / 16 / HW, HLX = HM / 16 / HW;   // 1 KB copies per wavefront and operand
+  constexpr int HLW = H_N * KB / 1024 / HW, HLX = HM * KB / 1024 / HW;  // 1 KB copies per operand
   // 16-bit elements per stage: the operand rows (+ the MXFP8 scale window, 2 KB).
-  constexpr int HSTAGE = (H_N + HM) * H_K + (MX ? 1024 : 0);
-  constexpr int SCALE_OFF = (H_N + HM) * 64;              // byte offset of the scale window
+  constexpr int HSTAGE = (H_N + HM) * KB / 2 + (MX ? 1024 : 0);
+  constexpr int SCALE_OFF = (H_N + HM) * KB;              // byte offset of the scale window
   // Three stages, or the epilogue's 8 KB (4096 16-bit elements) per wavefront if that is more.
   constexpr int LDS_ELEMS = 3 * HSTAGE > HW * 4096 ? 3 * HSTAGE : HW * 4096;
   static_assert((WM == 4 && (HM == 256 || HM == 128)) || (WM == 2 && HM == 128), "tile shapes");
@@ -544,56 +550,61 @@ __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))
   const u32x4 rWs = buffer_rsrc(mx.w, MX ? (uint32_t)((K / 32) * mx.w_stride) : 0u);
   const u32x4 rXs = buffer_rsrc(mx.x, MX ? (uint32_t)((K / 32) * mx.x_stride) : 0u);
 
-  // Copy i of wavefront w fills 1 KB block (i * HW + w) of its operand: 16 rows of 64 bytes,
-  // lane l row (l >> 2), slot (l & 3) holding chunk slot ^ ((row >> 2) & 3).
-  const int lrow = 16 * wave + (lane >> 2);
-  const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  // Copy i of wavefront w fills 1 KB block (i * HW + w) of its operand.  64-byte rows: 16 rows,
+  // lane l row (l >> 2), slot (l & 3) holding chunk slot ^ ((row >> 2) & 3); 128-byte rows: 8
+  // rows, lane l row (l >> 3), slot (l & 7) holding chunk slot ^ ((row >> 1) & 7) (the persistent
+  // kernel's layout).  Either way each 16-lane phase of a fragment read covers the banks once.
+  const int lrow = RPC * wave + lane / (KB / 16);
+  const int lchunk = KB == 64 ? ((lane & 3) ^ ((lane >> 4) & 3))
+                              : ((lane & 7) ^ ((4 * wave + (lane >> 4)) & 7));
   const int voW = lrow * kw * EB + lchunk * 16, voX = lrow * lda * EB + lchunk * 16;
   // Scale copies: lane l of wavefront 0 (1) copies 16 scale bytes of the tile's W (X) rows, block
-  // l / L of the tile's two, rows 16 (l % L) ..; lanes past 2 L read out of range (zeros) into
-  // the rest of the 1 KB window.  The window holds byte [block][row] at block * rows + row.
-  constexpr int XL = HM / 16;
-  const int sc_off = wave == 0 ? (lane < 16 ? (lane >> 3) * mx.w_stride + n0 + (lane & 7) * 16 : -1)
-                               : (lane < 2 * XL ? (lane / XL) * mx.x_stride + m0 + (lane % XL) * 16 : -1);
+  // l / L of the tile's KB / 32, rows 16 (l % L) ..; the other lanes read out of range (zeros)
+  // into the rest of the 1 KB window.  The window holds byte [block][row] at block * rows + row.
+  constexpr int XL = HM / 16, NBLK = KB / 32;
+  const int sc_off =
+      wave == 0 ? (lane < 8 * NBLK ? (lane >> 3) * mx.w_stride + n0 + (lane & 7) * 16 : -1)
+                : (lane < XL * NBLK ? (lane / XL) * mx.x_stride + m0 + (lane % XL) * 16 : -1);
   auto load_tile = [&](int kt, const uint16_t* st) {
     const uint32_t base = lds_addr(st);
     int ko, kow;
     if constexpr (MX) {
-      ko = kow = kbyte0 + kt * 64;
+      ko = kow = kbyte0 + kt * KB;
       const int blk = ko >> 5;  // first 32-k block of the tile
       if (wave == 0)
         lds_copy16(rWs, base + SCALE_OFF, sc_off < 0 ? 0x7ffffff0 : sc_off + blk * mx.w_stride);
       else if (wave == 1)
         lds_copy16(rXs, base + SCALE_OFF + 1024u, sc_off < 0 ? 0x7ffffff0 : sc_off + blk * mx.x_stride);
     } else {
-      const int ke = kbyte0 / 2 + kt * H_K;  // first k of the tile
+      const int ke = kbyte0 / 2 + kt * KT;  // first k of the tile
       const int seg = (ke >= km.kb) + (ke >= 2 * km.kb), kk = ke - seg * km.kb;
       ko = (((km.xmask >> seg) & 1) * km.kb + kk) * 2;
       kow = (((km.wmask >> seg) & 1) * km.kb + kk) * 2;
     }
 #pragma unroll
     for (int i = 0; i < HLW; ++i)
-      lds_copy16(rW, base + (uint32_t)(i * HW + wave) * 1024u, voW + i * 16 * HW * kw * EB + kow);
+      lds_copy16(rW, base + (uint32_t)(i * HW + wave) * 1024u, voW + i * RPC * HW * kw * EB + kow);
 #pragma unroll
     for (int i = 0; i < HLX; ++i)
-      lds_copy16(rX, base + H_N * 64 + (uint32_t)(i * HW + wave) * 1024u,
-                 voX + i * 16 * HW * lda * EB + ko);
+      lds_copy16(rX, base + H_N * KB + (uint32_t)(i * HW + wave) * 1024u,
+                 voX + i * RPC * HW * lda * EB + ko);
   };
 
-  const int rowA = (wn * H_TN + frow) * 64;
-  const int rowB = (H_N + wm * TM + frow) * 64;
-  int xo[2];
+  const int rowA = (wn * H_TN + frow) * KB;
+  const int rowB = (H_N + wm * TM + frow) * KB;
+  int xo[NSTEP];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) xo[s] = ((2 * s + g) ^ ((lane >> 2) & 3)) << 4;
+  for (int s = 0; s < NSTEP; ++s)
+    xo[s] = (KB == 64 ? ((2 * s + g) ^ ((lane >> 2) & 3)) : ((2 * s + g) ^ ((lane >> 1) & 7))) << 4;
   auto read_frags = [&](const uint16_t* st, int s, u32x4 (&fa)[H_NA], u32x4 (&fb)[NB]) {
     const char* base = reinterpret_cast<const char*>(st);
     fa[0] = *reinterpret_cast<const u32x4*>(base + rowA + xo[s]);
 #pragma unroll
     for (int b = 0; b < NB; ++b)
-      fb[b] = *reinterpret_cast<const u32x4*>(base + rowB + b * 2048 + xo[s]);
+      fb[b] = *reinterpret_cast<const u32x4*>(base + rowB + b * BLK + xo[s]);
 #pragma unroll
     for (int a = 1; a < H_NA; ++a)
-      fa[a] = *reinterpret_cast<const u32x4*>(base + rowA + a * 2048 + xo[s]);
+      fa[a] = *reinterpret_cast<const u32x4*>(base + rowA + a * BLK + xo[s]);
   };
 
   f32x16 acc[H_NA][NB];
@@ -636,24 +647,26 @@ __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))
     // The fragments of tile kt + 1 are read after the barrier that follows tile kt's MFMAs
     // (the compiler gives alternate tiles their own registers, so those reads overlap the MFMAs
     // still running; an explicit second register set measured no faster and cost 27 VGPRs).
-    auto read_scales = [&](const uint16_t* st, int (&sa)[H_NA], int (&sb)[NB]) {
+    // MXFP8 step s of a k tile: chunks of the 16-bit steps 2 s and 2 s + 1, scale block 2 s + g.
+    auto read_scales = [&](const uint16_t* st, int (&sa)[H_NA], int (&sb)[NB], int s = 0) {
       const uint8_t* w = reinterpret_cast<const uint8_t*>(st) + SCALE_OFF;
 #pragma unroll
-      for (int a = 0; a < H_NA; ++a) sa[a] = w[g * H_N + wn * H_TN + a * 32 + frow];
+      for (int a = 0; a < H_NA; ++a) sa[a] = w[(2 * s + g) * H_N + wn * H_TN + a * 32 + frow];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) sb[b] = w[1024 + g * HM + wm * TM + b * 32 + frow];
+      for (int b = 0; b < NB; ++b) sb[b] = w[1024 + (2 * s + g) * HM + wm * TM + b * 32 + frow];
     };
     u32x8 A[H_NA], Bf[NB];
     int SA[H_NA], SB[NB];
-    auto read_mx = [&](const uint16_t* st) {
+    auto read_mx = [&](const uint16_t* st, int s = 0) {
       const char* base = reinterpret_cast<const char*>(st);
-      A[0] = lds_frag8(base + rowA + xo[0], base + rowA + xo[1]);
+      const int lo = xo[2 * s], hi = xo[2 * s + 1];
+      A[0] = lds_frag8(base + rowA + lo, base + rowA + hi);
 #pragma unroll
       for (int b = 0; b < NB; ++b)
-        Bf[b] = lds_frag8(base + rowB + b * 2048 + xo[0], base + rowB + b * 2048 + xo[1]);
+        Bf[b] = lds_frag8(base + rowB + b * BLK + lo, base + rowB + b * BLK + hi);
 #pragma unroll
       for (int a = 1; a < H_NA; ++a)
-        A[a] = lds_frag8(base + rowA + a * 2048 + xo[0], base + rowA + a * 2048 + xo[1]);
+        A[a] = lds_frag8(base + rowA + a * BLK + lo, base + rowA + a * BLK + hi);
     };
     auto mm_row = [&](int a) {
 #pragma unroll
@@ -663,6 +676,32 @@ __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))
     if (nk > 1) load_tile(1, s1);
     wait_copies(nk > 1);
     __syncthreads();
+    if constexpr (KB == 128) {
+      // Two MXFP8 steps per k tile: each step's fragments are read after the previous step's
+      // MFMAs (one register set), and one barrier per tile.
+      auto body2 = [&](int kt, const uint16_t* cur, const uint16_t* ahead) {
+        const bool loads = kt + 2 < nk, next = kt + 1 < nk;
+        if (loads) load_tile(kt + 2, ahead);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          read_mx(cur, s);
+          read_scales(cur, SA, SB, s);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int a = 0; a < H_NA; ++a) mm_row(a);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (next) {
+          wait_copies(loads);
+          __syncthreads();  // tile kt + 1 landed everywhere; every read of tile kt is complete
+        }
+      };
+      for (int kt = 0; kt < nk; kt += 3) {
+        body2(kt, s0, s2);
+        if (kt + 1 < nk) body2(kt + 1, s1, s0);
+        if (kt + 2 < nk) body2(kt + 2, s2, s1);
+      }
+    } else {
     read_mx(s0);
     read_scales(s0, SA, SB);
     auto body = [&](int kt, const uint16_t* nxt, const uint16_t* ahead) {
@@ -684,6 +723,7 @@ __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))
       if (kt + 1 < nk) body(kt + 1, s2, s0);
       if (kt + 2 < nk) body(kt + 2, s0, s1);
     }
+    }
   } else {
     u32x4 fa0[H_NA], fb0[NB], fa1[H_NA], fb1[NB];
     load_tile(0, s0);
@@ -698,6 +738,10 @@ __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))
       const bool loads = kt + 2 < nk, next = kt + 1 < nk;
       if (loads) load_tile(kt + 2, ahead);
       read_frags(cur, 1, fa1, fb1); mm(fa0, fb0); sched();
+      if constexpr (NSTEP == 4) {
+        read_frags(cur, 2, fa0, fb0); mm(fa1, fb1); sched();
+        read_frags(cur, 3, fa1, fb1); mm(fa0, fb0); sched();
+      }
       if (next) {
         if (loads) __builtin_amdgcn_s_waitcnt(0x0F70 | LT);
         else __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -956,6 +1000,13 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int ksplit,
   }
 }
 
+// LDS row bytes of the small kernel's launches: 128, one k tile of 64 16-bit or 128 fp8 values,
+// four 16-bit MFMA steps (two fp8 ones) per barrier.  Measured against 64-byte rows (two steps per
+// barrier, two workgroups per CU where the LDS allowed it), one window: large-v3 stack 5.09 ->
+// 4.60 ms (fp16) and 4.13 -> 3.73 ms (MXFP8), small 1.17 -> 1.07, base 0.441 -> 0.415, tiny
+// 0.073 -> 0.068 ms.  Three 48 KB stages (+ the MXFP8 scale windows) hold one workgroup per CU.
+constexpr int kSmallKB = 128;
+
 // Split-k plan of a residual GEMM: the number of k parts, and the rows (256 or 128) of the small
 // kernel's tiles for them.  Reference device: 256 CUs (the plan fixes the results and the
 // workspace size, so it must not depend on the device).  Split only problems the persistent
@@ -988,7 +1039,7 @@ int linear_split(int m, int n, int k, int dtype, int epilogue) {
   if (dtype == DT_F32 || (epilogue != EPI_BIAS_RESIDUAL && epilogue != EPI_BIAS_GELU_RESIDUAL))
     return 1;
   int rows;
-  return split_plan(m, n, k, &rows, dtype == DT_MX8 ? 64 : H_K);
+  return split_plan(m, n, k, &rows, dtype == DT_MX8 ? kSmallKB : kSmallKB / 2);
 }
 
 // Workgroups of the persistent kernel: the current device's CU count, rounded down to a multiple
@@ -1010,7 +1061,7 @@ static hipError_t launch16_epi(const uint16_t* X, int lda, const uint16_t* W, co
   const long small = (long)((m + H_M - 1) / H_M) * ((n + H_N - 1) / H_N);
   int split_rows = H_M;
   const int split = partial ? linear_split(m, n, k, DT_F16, EPI) : 1;
-  if (split > 1) split_plan(m, n, k, &split_rows);
+  if (split > 1) split_plan(m, n, k, &split_rows, kSmallKB / 2);
   if (ln && (EPI != EPI_BIAS_RESIDUAL || split < 2 || ldc != n)) return hipErrorInvalidValue;
   const int grid = persistent_grid();
   const long small2 = (long)((m + 127) / 128) * ((n + H_N - 1) / H_N);  // 128 x 128 tiles
@@ -1018,11 +1069,11 @@ static hipError_t launch16_epi(const uint16_t* X, int lda, const uint16_t* W, co
     if (split > 1) {
       // Each part's sums do not depend on the tile shape (split_plan picks it).
       if (split_rows == 128)
-        gemm16_small_kernel<T, EPI_PARTIAL, 4, 128><<<dim3((unsigned)(small2 * split)),
+        gemm16_small_kernel<T, EPI_PARTIAL, 4, 128, kSmallKB><<<dim3((unsigned)(small2 * split)),
                                                        dim3(H_THREADS), 0, st>>>(
             X, lda, W, bias, nullptr, partial, n, m, n, k, split, -1, kw, MxPlanes{});
       else
-        gemm16_small_kernel<T, EPI_PARTIAL><<<dim3((unsigned)(small * split)), dim3(H_THREADS),
+        gemm16_small_kernel<T, EPI_PARTIAL, H_WM, H_M, kSmallKB><<<dim3((unsigned)(small * split)), dim3(H_THREADS),
                                               0, st>>>(X, lda, W, bias, nullptr, partial, n, m, n,
                                                        k, split, -1, kw, MxPlanes{});
       if (ln)
@@ -1045,7 +1096,7 @@ static hipError_t launch16_epi(const uint16_t* X, int lda, const uint16_t* W, co
     gemm16_kernel<T, EPI><<<dim3((unsigned)grid), dim3(G_THREADS), 0, st>>>(
         X, lda, W, bias, residual, c, ldc, m, n, k, (int)(halves ? whole : tiles), kw, MxPlanes{});
     if (halves)
-      gemm16_small_kernel<T, EPI><<<dim3((unsigned)(2 * tail)), dim3(H_THREADS), 0, st>>>(
+      gemm16_small_kernel<T, EPI, H_WM, H_M, kSmallKB><<<dim3((unsigned)(2 * tail)), dim3(H_THREADS), 0, st>>>(
           X, lda, W, bias, residual, c, ldc, m, n, k, 1, (int)whole, kw, MxPlanes{});
   } else if (2 * small < grid) {
     // Fewer 128 x 256 tiles than half the CUs: 128 x 128 tiles, eight wavefronts of 64 x 32, twice
@@ -1053,10 +1104,10 @@ static hipError_t launch16_epi(const uint16_t* X, int lda, const uint16_t* W, co
     // of 64 x 64 -> with eight of 64 x 32): d 384 QKV 9.2 -> 7.6 -> 6.4, fc1 12.2 -> 9.6 -> 8.3;
     // d 512 QKV 10.7 -> 8.8 -> 7.5, fc1 14.0 -> 11.0 -> 9.7; d 768 QKV 14.4 -> 12.0 -> 11.0.  With
     // 144 tiles or more (d 768 fc1, d 1280) the 128 x 256 tiles stay as fast or faster.
-    gemm16_small_kernel<T, EPI, 4, 128><<<dim3((unsigned)small2), dim3(H_THREADS), 0, st>>>(
+    gemm16_small_kernel<T, EPI, 4, 128, kSmallKB><<<dim3((unsigned)small2), dim3(H_THREADS), 0, st>>>(
         X, lda, W, bias, residual, c, ldc, m, n, k, 1, -1, kw, MxPlanes{});
   } else {
-    gemm16_small_kernel<T, EPI><<<dim3((unsigned)small), dim3(H_THREADS), 0, st>>>(
+    gemm16_small_kernel<T, EPI, H_WM, H_M, kSmallKB><<<dim3((unsigned)small), dim3(H_THREADS), 0, st>>>(
         X, lda, W, bias, residual, c, ldc, m, n, k, 1, -1, kw, MxPlanes{});
   }
   return hipGetLastError();
@@ -1093,9 +1144,11 @@ static hipError_t launch16(const void* a, int lda, const void* w, const float* b
   return hipErrorInvalidValue;
 }
 
-// MXFP8 operands: always the small kernel (128 x 256 tiles, or 128 x 128 where those would
-// leave more than half the CUs idle), with the same split-k rule as the 16-bit operands.
-template <int EPI>
+// MXFP8 operands, with the same choices as 16-bit ones: whole rounds of 256 x 256 tiles on the
+// persistent kernel (k % 128 == 0), else the small kernel (128 x 256 tiles, or 128 x 128 where
+// those would leave more than half the CUs idle), and the same split-k rule.  KB: the small
+// kernel's LDS row bytes, 128 (two MXFP8 steps per k tile) where k allows, else 64.
+template <int EPI, int KB = kSmallKB>
 static hipError_t launch_mx_epi(const uint16_t* X, const uint16_t* W, const float* bias,
                                 const float* residual, void* c, int ldc, int m, int n, int k,
                                 hipStream_t st, float* partial, const LnFuse* ln,
@@ -1105,16 +1158,16 @@ static hipError_t launch_mx_epi(const uint16_t* X, const uint16_t* W, const floa
   const long small2 = (long)((m + 127) / 128) * ((n + H_N - 1) / H_N);
   int split_rows = H_M;
   const int split = partial ? linear_split(m, n, k, DT_MX8, EPI) : 1;
-  if (split > 1) split_plan(m, n, k, &split_rows, 64);
+  if (split > 1) split_plan(m, n, k, &split_rows, KB);
   if (ln && (EPI != EPI_BIAS_RESIDUAL || split < 2 || ldc != n)) return hipErrorInvalidValue;
   if constexpr (EPI == EPI_BIAS_RESIDUAL || EPI == EPI_BIAS_GELU_RESIDUAL) {
     if (split > 1) {
       if (split_rows == 128)
-        gemm16_small_kernel<mx8_t, EPI_PARTIAL, 4, 128><<<dim3((unsigned)(small2 * split)),
+        gemm16_small_kernel<mx8_t, EPI_PARTIAL, 4, 128, KB><<<dim3((unsigned)(small2 * split)),
                                                            dim3(H_THREADS), 0, st>>>(
             X, k, W, bias, nullptr, partial, n, m, n, k, split, -1, kw, mx);
       else
-        gemm16_small_kernel<mx8_t, EPI_PARTIAL><<<dim3((unsigned)(small * split)),
+        gemm16_small_kernel<mx8_t, EPI_PARTIAL, H_WM, H_M, KB><<<dim3((unsigned)(small * split)),
                                                   dim3(H_THREADS), 0, st>>>(
             X, k, W, bias, nullptr, partial, n, m, n, k, split, -1, kw, mx);
       if (ln)
@@ -1137,13 +1190,13 @@ static hipError_t launch_mx_epi(const uint16_t* X, const uint16_t* W, const floa
     gemm16_kernel<mx8_t, EPI><<<dim3((unsigned)grid), dim3(G_THREADS), 0, st>>>(
         X, k, W, bias, residual, c, ldc, m, n, k, (int)(halves ? whole : tiles), kw, mx);
     if (halves)
-      gemm16_small_kernel<mx8_t, EPI><<<dim3((unsigned)(2 * tail)), dim3(H_THREADS), 0, st>>>(
+      gemm16_small_kernel<mx8_t, EPI, H_WM, H_M, KB><<<dim3((unsigned)(2 * tail)), dim3(H_THREADS), 0, st>>>(
           X, k, W, bias, residual, c, ldc, m, n, k, 1, (int)whole, kw, mx);
   } else if (2 * small < grid) {
-    gemm16_small_kernel<mx8_t, EPI, 4, 128><<<dim3((unsigned)small2), dim3(H_THREADS), 0, st>>>(
+    gemm16_small_kernel<mx8_t, EPI, 4, 128, KB><<<dim3((unsigned)small2), dim3(H_THREADS), 0, st>>>(
         X, k, W, bias, residual, c, ldc, m, n, k, 1, -1, kw, mx);
   } else {
-    gemm16_small_kernel<mx8_t, EPI><<<dim3((unsigned)small), dim3(H_THREADS), 0, st>>>(
+    gemm16_small_kernel<mx8_t, EPI, H_WM, H_M, KB><<<dim3((unsigned)small), dim3(H_THREADS), 0, st>>>(
         X, k, W, bias, residual, c, ldc, m, n, k, 1, -1, kw, mx);
   }
   return hipGetLastError();
@@ -1158,6 +1211,22 @@ static hipError_t launch_mx(const void* a, int lda, const void* w, const float* 
               nullptr, 0};
   auto X = static_cast<const uint16_t*>(a);
   auto W = static_cast<const uint16_t*>(w);
+  if (k % kSmallKB != 0) {  // k tiles of 64: only the unsplit small kernel (no split plan fits)
+    if (partial && linear_split(m, n, k, DT_MX8, epi) > 1) return hipErrorInvalidValue;
+    switch (epi) {
+      case EPI_BIAS: return launch_mx_epi<EPI_BIAS, 64>(X, W, bias, residual, c, ldc, m, n, k, st, nullptr, ln, mx);
+      case EPI_BIAS_GELU:
+        if (ldc != n) return hipErrorInvalidValue;
+        mx.c = static_cast<uint8_t*>(c) + mx_planes_offset(m, n);
+        mx.c_stride = (int)mx_plane_stride(m);
+        return launch_mx_epi<EPI_BIAS_GELU, 64>(X, W, bias, residual, c, ldc, m, n, k, st, nullptr, ln, mx);
+      case EPI_BIAS_RESIDUAL:
+        return launch_mx_epi<EPI_BIAS_RESIDUAL, 64>(X, W, bias, residual, c, ldc, m, n, k, st, nullptr, ln, mx);
+      case EPI_BIAS_GELU_RESIDUAL:
+        return launch_mx_epi<EPI_BIAS_GELU_RESIDUAL, 64>(X, W, bias, residual, c, ldc, m, n, k, st, nullptr, ln, mx);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (epi) {
     case EPI_BIAS:
       return launch_mx_epi<EPI_BIAS>(X, W, bias, residual, c, ldc, m, n, k, st, partial, ln, mx);

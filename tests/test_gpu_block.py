@@ -19,8 +19,9 @@ path does NOT meet MAE <= 1e-3 on the base, small, large-v3 and batched workload
 LayerNorm and GELU output to bf16 (2^-9 relative) before a projection leaves ~1e-3 of error per
 block in the residual stream, growing with depth (measured 1.4e-3 after 6 blocks, 2.8e-3 after 32;
 the fp32 weights of the tiny and base workloads lose 2^-9 more when stored as bf16).  Its tests
-there assert the max relative bound, print the MAE, and hold it under BF16_MAE_CEILING only to
-catch a regression of that known miss; the 1e-3 bar itself is asserted on fp16 and BF16X2.
+there assert the max relative bound, fail outright above BF16_MAE_CEILING (a regression of that
+known miss), and otherwise report the MAE bar as an expected failure (xfail) with the measured
+value; the 1e-3 bar itself is asserted on fp16, BF16X2 and BF16X3.
 """
 
 import os
@@ -60,6 +61,11 @@ def check(e, path, tag, name=None):
     assert e["max_rel"] <= tol["max_rel"], (tag, e)
     if tol["mae"] is not None:
         assert e["mae"] <= tol["mae"], (tag, e)
+    if path == B.WENC_PATH_BF16 and e["mae"] > 1e-3:
+        # The bar is MAE <= 1e-3; literal bf16 operands miss it here (reported as an expected
+        # failure, not passed under a wider bound; the ceiling above only catches a regression).
+        pytest.xfail(f"{tag}: literal bf16 operands miss MAE <= 1e-3 (measured {e['mae']:.2e}); "
+                     "fp16, BF16X2 and BF16X3 meet it")
 
 
 @pytest.fixture(scope="module", autouse=True)

@@ -5,7 +5,8 @@ Each window must come out exactly as if it had been encoded alone: attention per
 row-wise steps over all rows.  References: the oracle per window (``attention_online``,
 ``encoder_stack_varlen``, ``encoder_block_rows``), and, bit for bit, the dense entry points when all
 windows have one length.  Tolerances are the block's (fp32 max_rel 1e-4; 16-bit max_rel 2e-2 and
-MAE 1e-3, bf16 MAE 4e-3 as in the dense block tests) and, for attention, the componentwise bound of the dense attention test.
+MAE 1e-3; literal bf16 as in the dense block tests: above 1e-3 an expected failure, above 4e-3 a
+failure) and, for attention, the componentwise bound of the dense attention test.
 """
 
 import numpy as np
@@ -34,8 +35,9 @@ def _cu(lens):
 
 
 def _check_block(e, path, tag):
-    """The dense block tests' bar: bf16 operands are held to MAE 4e-3 beyond the tiny workload
-    (rounding LayerNorm and GELU outputs to bf16 costs ~1e-3 per block at these magnitudes)."""
+    """The dense block tests' bar.  Literal bf16 operands miss MAE <= 1e-3 beyond the tiny
+    workload (rounding LayerNorm and GELU outputs to bf16 costs ~1e-3 per block at these
+    magnitudes): that is reported as an expected failure, and only a regression past 4e-3 fails."""
     report(f"{tag} [{PATH_NAMES[path]}]", e)
     assert e["finite"], tag
     if path == B.WENC_PATH_FP32:
@@ -43,6 +45,8 @@ def _check_block(e, path, tag):
     else:
         mae = 4e-3 if path == B.WENC_PATH_BF16 else 1e-3
         assert e["max_rel"] <= 2e-2 and e["mae"] <= mae, (tag, e)
+        if e["mae"] > 1e-3:
+            pytest.xfail(f"{tag}: literal bf16 operands miss MAE <= 1e-3 (measured {e['mae']:.2e})")
 
 
 def _attention_varlen(path, lens, heads, seed, cu=None, max_t=None):

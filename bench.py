@@ -38,7 +38,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="large_v3_batch16_block")
-    ap.add_argument("--path", default="fp16", choices=["bf16", "fp16", "fp32"])
+    ap.add_argument("--path", default="fp16", choices=["bf16", "fp16", "fp32", "mxfp8"],
+                    help="operand path of the timed step (mxfp8: its own numerical method, with "
+                         "attention and the out-projection on fp16)")
     ap.add_argument("--compare-paths", default="bf16,bf16x3,mxfp8",
                     help="comma-separated other paths timed the same way (reported, not value): "
                          "bf16, bf16x2, bf16x3, mxfp8, fp32")
@@ -205,16 +207,18 @@ def mx_kernel_breakdown(cfg, reps):
             ach, peak, unit = work / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
         else:
             ach, peak, unit = work / (ms * 1e-3) / 1e12, PEAK_TFLOPS["mxfp8"], "TFLOP/s"
-        out[name] = {"ms": round(ms, 5), "achieved": round(ach, 1), "unit": unit, "peak": peak,
-                     "frac": round(ach / peak, 4)}
+        out[name] = {"ms": round(ms, 5), "bound": bound, "achieved": round(ach, 1), "unit": unit,
+                     "peak": peak, "frac": round(ach / peak, 4), "work": work,
+                     "launches_per_block": 2 if name == "ln" else 1}
     del a, h, wqkv, w1, w2, hid, ln_out, qkv
     torch.cuda.empty_cache()
     return out
 
 
 def mfma_peak(path_name):
-    """Dense 16-bit MFMA rate this GPU sustains on register operands (the probe library beside
-    the encoder library), with the shader clock while it runs; None on the fp32 path."""
+    """Dense 16-bit (or MXFP8) MFMA rate this GPU sustains on register operands (the probe
+    library beside the encoder library), with the shader clock while it runs; None on the fp32
+    path."""
     import ctypes
     import torch
     if path_name == "fp32":
@@ -224,8 +228,8 @@ def mfma_peak(path_name):
     lib.wenc_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p]
     lib.wenc_probe_mfma_flops.restype = ctypes.c_longlong
-    lib.wenc_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
-    dtype = {"fp16": 2, "bf16": 1}[path_name]
+    lib.wenc_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    dtype = {"fp16": 2, "bf16": 1, "mxfp8": 8}[path_name]
     blocks, iters = 256 * 2, 100000  # two wavefronts per SIMD; ~20 ms per launch
     clocks = torch.zeros(2, dtype=torch.int64, device="cuda")
     sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
@@ -240,10 +244,11 @@ def mfma_peak(path_name):
         c = clocks.cpu().tolist()
         if best is None or ms < best:
             best, clk = ms, (c[0] / c[1] * 0.1 if c[1] > 0 else None)  # GHz (100 MHz reference)
-    tf = lib.wenc_probe_mfma_flops(blocks, iters) / (best * 1e-3) / 1e12
+    tf = lib.wenc_probe_mfma_flops(dtype, blocks, iters) / (best * 1e-3) / 1e12
     return {"dtype": path_name, "tflops": round(tf, 1), "shader_clock_ghz": round(clk, 3) if clk else None,
             "rated_tflops": PEAK_TFLOPS[path_name], "rated_clock_ghz": 2.4,
-            "probe": "v_mfma_f32_32x32x16 on register operands, 4 chains x 2 wavefronts per SIMD"}
+            "probe": ("v_mfma_scale_f32_32x32x64_f8f6f4" if path_name == "mxfp8" else
+                      "v_mfma_f32_32x32x16") + " on register operands, 4 chains x 2 wavefronts per SIMD"}
 
 
 def kernel_breakdown(cfg, path_name, reps):
@@ -599,6 +604,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     B.load()
     if args.pmc_run:
+        if args.path == "mxfp8":
+            sys.exit("--pmc-run times the 16-bit block kernels: use --path fp16 or bf16")
         pmc_run(cfg, args.path)
         return
     path = B.PATHS[args.path]
@@ -636,7 +643,15 @@ def main():
     frames = cfg.batch * cfg.t
     flops = cfg.flops()
 
-    kern = kernel_breakdown(cfg, args.path, args.kernel_reps)
+    if args.path == "mxfp8":
+        # The MXFP8 step's own kernels (LN with MXFP8 output, QKV / fc1 / fc2 on MXFP8 operands)
+        # and the fp16 attention and out-projection it keeps.
+        kern16 = kernel_breakdown(cfg, "fp16", args.kernel_reps)
+        kern = mx_kernel_breakdown(cfg, args.kernel_reps)
+        kern["attention"] = kern16["attention"]
+        kern["gemm_out_residual"] = kern16["gemm_out_residual"]
+    else:
+        kern = kernel_breakdown(cfg, args.path, args.kernel_reps)
     # Kernel time per step: every kernel runs once per block (LN twice), n_layers blocks.
     for k in kern.values():
         k["ms_per_step"] = round(k["ms"] * k["launches_per_block"] * cfg.n_layers, 4)
@@ -661,9 +676,16 @@ def main():
     peak = PEAK_TFLOPS[args.path]
     measured = mfma_peak(args.path)
     mpeak = measured["tflops"] if measured else None
+    # On the MXFP8 path attention and the out-projection run fp16 MFMAs: their peaks are fp16's.
+    attn_peak, attn_mpeak = peak, mpeak
+    if args.path == "mxfp8":
+        m16 = mfma_peak("fp16")
+        attn_peak, attn_mpeak = PEAK_TFLOPS["fp16"], m16["tflops"]
+        measured = {"mxfp8": measured, "fp16": m16}
     if mpeak and roof["unit"] == "TFLOP/s":
-        roof["measured_peak"] = mpeak
-        roof["frac_measured_peak"] = round(roof["achieved"] / mpeak, 4)
+        rm = attn_mpeak if dom_name in ("attention", "gemm_out_residual") else mpeak
+        roof["measured_peak"] = rm
+        roof["frac_measured_peak"] = round(roof["achieved"] / rm, 4)
 
     # Every other workload, timed whole (the 32-block large-v3 stack as one call), on the same
     # operand type; and the fp32 fallback path on the bench workload itself.
@@ -677,7 +699,7 @@ def main():
                                                       PEAK_TFLOPS["fp32"], None)
 
     next_steps = {}
-    if not args.no_next_steps:
+    if not args.no_next_steps and args.path != "mxfp8":  # the adjacent steps have no MXFP8 form
         next_steps["stem"] = time_stem(cfg, args.path, args.kernel_reps)
         next_steps["cross_kv"] = time_cross_kv(cfg, args.path, args.kernel_reps)
         next_steps["varlen"] = time_varlen(cfg, args.path, args.kernel_reps, enc_main, ms)
@@ -702,10 +724,13 @@ def main():
                    "operands": args.path, "parallelism": "single GPU"},
         "tflops": {"total": round(flops["total"] / (ms * 1e-3) / 1e12, 1),
                    "gemm": round(gemm_tf, 1), "gemm_frac_peak": round(gemm_tf / peak, 4),
-                   "attention": round(attn_tf, 1), "attention_frac_peak": round(attn_tf / peak, 4),
+                   "attention": round(attn_tf, 1), "attention_frac_peak": round(attn_tf / attn_peak, 4),
                    "peak": peak, "measured_peak": mpeak,
                    "gemm_frac_measured_peak": round(gemm_tf / mpeak, 4) if mpeak else None,
-                   "attention_frac_measured_peak": round(attn_tf / mpeak, 4) if mpeak else None},
+                   "attention_frac_measured_peak": (round(attn_tf / attn_mpeak, 4)
+                                                    if attn_mpeak else None),
+                   "gemm_peak_note": ("the out-projection (fp16) is counted in the GEMM rate, "
+                                      "priced at the fp8 peak" if args.path == "mxfp8" else None)},
         "mfma_peak_measured": measured,
         "configs": configs,
         "roofline": roof,

@@ -9,9 +9,10 @@
 //
 // gfx950 mapping.  One 512-thread workgroup per (256 query rows, head, window); wavefront w owns
 // 32 queries.  (Problems with fewer than 256 blocks of 128 query rows, e.g. one window, run
-// workgroups of four or two wavefronts instead, and split the keys of each query block in two
-// halves when there are fewer than 128 blocks.)  Keys go in tiles of 64 through three LDS stages, each a K tile and a V tile of
-// 64 rows x 128 bytes, loaded global -> LDS directly (buffer_load_dwordx4 ... lds, range-checked
+// workgroups of 128 query rows whose eight wavefronts form two groups over the two halves of the
+// keys, and split the keys again over two workgroups when there are fewer than 128 blocks.)
+// Keys go in tiles of 64 through three LDS stages, each a K tile and a V tile of 64 rows x 128
+// bytes, loaded global -> LDS directly (buffer_load_dwordx4 ... lds, range-checked
 // so that keys past t read as zeros) two tiles ahead of their use.  Chunk c (16 bytes) of row r
 // sits at slot c ^ f(r), f chosen per tile so that the 16-lane phases of its reads hit distinct
 // banks.  The scores are computed transposed, S^T = K . Q^T, with v_mfma_f32_32x32x16: lane l
@@ -85,29 +86,41 @@ template <> struct RowSum<bf16_t> {
 // each query block's keys are split in two halves handled by two workgroups, which write the
 // unnormalised partial O (fp32) and their (m, l) to `part`; attn_merge_kernel combines them.
 // total: rows of the packed batch (batch * tmax for equal windows).
-// Eight-wavefront workgroups run two per CU (four wavefronts per SIMD, 128 VGPRs each); the
-// narrower ones serve grids smaller than the GPU and keep two wavefronts per SIMD.
-template <typename T, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 4 : 2, NW == 8 ? 4 : 2))) void attn16_kernel(const uint16_t* __restrict__ Q,
+// KS = 2: the NW wavefronts form two groups of NW / 2 over the same query rows, each running
+// the recurrence over its own half of the workgroup's key tiles through its own LDS stages; at
+// the end the second group hands its (O, m, l) to the first through LDS, which merges them as
+// attn_merge_kernel does.  This doubles the wavefronts a small grid runs (one window) without
+// the partial results going through memory.  Its 96 KB of stages keep one workgroup per CU.
+// Eight-wavefront workgroups of one group run two per CU (four wavefronts per SIMD, 128 VGPRs
+// each); the two-group form (grids smaller than the GPU) keeps two wavefronts per SIMD.
+template <typename T, int NW, int KS = 1>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8 && KS == 1 ? 4 : 2, NW == 8 && KS == 1 ? 4 : 2))) void attn16_kernel(const uint16_t* __restrict__ Q,
                                                         const uint16_t* __restrict__ Kp,
                                                         const uint16_t* __restrict__ Vp, int ld,
                                                         uint16_t* __restrict__ O, int ldo, int tmax,
                                                         int heads, float c,
                                                         const int* __restrict__ cu, int total,
                                                         int kvs, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(1024))) uint16_t st0[2 * ATILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t st1[2 * ATILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t st2[2 * ATILE];
+  static_assert(KS == 1 || KS == 2, "one or two key groups");
+  constexpr int NQ = NW / KS;  // wavefronts of one key group (one per 32 query rows)
+  // Three stages of 2 * ATILE elements (a K and a V tile) per key group.
+  __shared__ __attribute__((aligned(1024))) uint16_t st0_all[KS * 3 * 2 * ATILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int g = lane >> 5;
   const int frow = lane & 31;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = KS == 1 ? 0 : wave_all / NQ;  // key group
+  const int wave = KS == 1 ? wave_all : wave_all % NQ;  // wavefront within its group
+  // The group's stages.
+  const uint16_t* st0 = st0_all + kg * 6 * ATILE;
+  const uint16_t* st1 = st0 + 2 * ATILE;
+  const uint16_t* st2 = st0 + 4 * ATILE;
   // 1-D grid over (query block, head, window), renumbered so that the query blocks of one
   // (window, head) run on the same XCD and read its K and V through one L2.
-  constexpr int AQ = 32 * NW;  // query rows of the workgroup
-  constexpr int CPW = 8 / NW;   // 8-row blocks of each K and V tile a wavefront copies
+  constexpr int AQ = 32 * NQ;  // query rows of the workgroup
+  constexpr int CPW = 8 / NQ;   // 8-row blocks of each K and V tile a wavefront copies
   const int nqb = (tmax + AQ - 1) / AQ;
   const int vk = xcd_virtual_id(blockIdx.x, gridDim.x);
   const int half = vk % kvs, v = vk / kvs;  // the two halves of a query block are neighbours
@@ -144,22 +157,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8
   const int lr = 8 * wave + (lane >> 3);
   const int kvo = lr * ld * 2 + (((lane & 7) ^ ((lr >> 1) & 7)) << 4);
   const int vvo = lr * ld * 2 + (((lane & 7) ^ (((lr >> 1) & 1) << 2)) << 4);
-  // With NW < 8 wavefront w also copies rows 8 (w + NW i) .. + 7, i < CPW: a shift by a multiple
+  // With NQ < 8 wavefront w also copies rows 8 (w + NQ i) .. + 7, i < CPW: a shift by a multiple
   // of 16 rows leaves both swizzles unchanged.
   const uint32_t blk = (uint32_t)wave * 1024u;
-  // This workgroup's key tiles: all of the window's, or one half of them (kvs = 2).
+  // This workgroup's key tiles: all of the window's, or one half of them (kvs = 2); with KS = 2
+  // the first ceil(n / 2) of those n go to group 0, the rest to group 1.  Both groups run
+  // nloop iterations (one barrier each); a group with fewer tiles idles through its last one.
   const int ntile_all = (t + AK - 1) / AK;
   const int per = (ntile_all + kvs - 1) / kvs;
-  const int kt0 = min(ntile_all, half * per);
-  const int ntiles = min(ntile_all, kt0 + per) - kt0;
+  const int kt0w = min(ntile_all, half * per);
+  const int ntiles_w = min(ntile_all, kt0w + per) - kt0w;
+  const int nloop = (ntiles_w + KS - 1) / KS;
+  const int kt0 = kt0w + kg * nloop;
+  const int ntiles = KS == 1 ? ntiles_w : max(0, min(nloop, ntiles_w - kg * nloop));
   const int kbase = kt0 * AK;  // first key
   auto load_tile = [&](int j0, const uint16_t* st) {
     const uint32_t base = lds_addr(st) + blk;
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
-      const int ro = (j0 + 8 * NW * i) * ld * 2;
-      lds_copy16(rK, base + (uint32_t)(NW * i) * 1024u, kvo + ro);
-      lds_copy16(rV, base + ATILE * 2 + (uint32_t)(NW * i) * 1024u, vvo + ro);
+      const int ro = (j0 + 8 * NQ * i) * ld * 2;
+      lds_copy16(rK, base + (uint32_t)(NQ * i) * 1024u, kvo + ro);
+      lds_copy16(rV, base + ATILE * 2 + (uint32_t)(NQ * i) * 1024u, vvo + ro);
     }
   };
 
@@ -188,29 +206,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8
   float m_run = -INFINITY;  // max used in the exponents (scaled units), per query
   float l_part = 0.f;       // this lane's share of the running denominator
 
-  if (ntiles > 0) load_tile(kbase, st0);
-  if (ntiles > 1) load_tile(kbase + AK, st1);
-
-  // One key tile from stage `cur`; the tile two ahead is loaded into stage `ahead`.
-  auto tile = [&](int it, const uint16_t* cur, const uint16_t* ahead) {
-    const int j0 = kbase + it * AK;
-    // Tile it has landed (this wavefront's copies: only tile it + 1 may still be in flight),
-    // and every wavefront is done with tile it - 1, whose stage is `ahead`.
+  // Tile it's copies have landed (this wavefront's: only tile it + 1's may still be in flight)
+  // and, after the barrier, every wavefront's; the tile two ahead is then loaded into `ahead`,
+  // whose previous tile every wavefront of the group is done with.
+  auto sync_tile = [&](int it, const uint16_t* ahead) {
     if (it + 1 < ntiles)
       __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * CPW));  // the copies of tile it + 1 may be in flight
     else
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    if (it + 2 < ntiles) load_tile(j0 + 2 * AK, ahead);
+    if (it + 2 < ntiles) load_tile(kbase + (it + 2) * AK, ahead);
+  };
 
-    // S^T = K . Q^T for 64 keys x 32 queries.
-    f32x16 sacc[2];
-    const char* kbase = reinterpret_cast<const char*>(cur);
+  // S^T = K . Q^T for the 64 keys of tile it x 32 queries.
+  f32x16 sacc[2];
+  auto scores = [&](int it, const uint16_t* cur) {
+    const int j0 = kbase + it * AK;
+    const char* kb = reinterpret_cast<const char*>(cur);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(kbase + (mb * 32 + frow) * 128 +
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(kb + (mb * 32 + frow) * 128 +
                                                          (((2 * s + g) ^ xk) << 4));
         sacc[mb] = mfma32x32x16<T>(ka, qf[s], s == 0 ? f32x16{} : sacc[mb]);
       }
@@ -224,8 +241,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8
           if (key >= t) sacc[mb][r] = -INFINITY;
         }
     }
-    // Probabilities against the current max, packed for the MFMA; tsum = this lane's sum.
-    u32x4 pb[4];
+  };
+
+  // Probabilities of sacc against the running max, packed for the MFMA (pb), and the running
+  // state updated; the max is raised first when the probabilities would pass the bound.
+  u32x4 pb[4];
+  auto softmax = [&]() {
     float tsum;
     auto exponentiate = [&]() {
       float ts[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial sums (shorter chains)
@@ -264,8 +285,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8
       exponentiate();
     }
     l_part += tsum;
+  };
 
-    // O^T += V^T . P^T, 4 steps of 16 keys; V^T fragments by transposing reads.
+  // O^T += V^T . P^T, 4 steps of 16 keys; V^T fragments by transposing reads.
+  auto pv = [&](const uint16_t* cur) {
     const uint16_t* vtile = cur + ATILE;
 #pragma unroll
     for (int kstep = 0; kstep < 4; ++kstep) {
@@ -282,14 +305,55 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8
       }
     }
   };
+
+  // One key tile per iteration from stage `cur`: scores, softmax, P.V.
+  if (ntiles > 0) load_tile(kbase, st0);
+  if (ntiles > 1) load_tile(kbase + AK, st1);
+  auto tile = [&](int it, const uint16_t* cur, const uint16_t* ahead) {
+    sync_tile(it, ahead);
+    if (KS > 1 && it >= ntiles) return;  // this group's tiles are done; the other's are not
+    scores(it, cur);
+    softmax();
+    pv(cur);
+  };
   int it = 0;
-  for (; it + 3 <= ntiles; it += 3) {
+  for (; it + 3 <= nloop; it += 3) {
     tile(it, st0, st2);
     tile(it + 1, st1, st0);
     tile(it + 2, st2, st1);
   }
-  if (it < ntiles) tile(it, st0, st2);
-  if (it + 1 < ntiles) tile(it + 1, st1, st0);
+  if (it < nloop) tile(it, st0, st2);
+  if (it + 1 < nloop) tile(it + 1, st1, st0);
+
+  if constexpr (KS == 2) {
+    // Group 1 hands (O, m, l) to group 0 through group 0's stages, which every wavefront is done
+    // with after the barrier: O as 32 values per lane (8 KB per wavefront), then m and l per
+    // lane.  Group 0 rescales both to the larger max, exp2(m_g - m) (zero for a group without
+    // keys).
+    __syncthreads();
+    float* xo = reinterpret_cast<float*>(st0_all) + wave * (32 * 64) + lane;
+    float* xml = reinterpret_cast<float*>(st0_all + 4 * ATILE) + wave * 128 + lane;
+    if (kg == 1) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[(a * 16 + r) * 64] = oacc[a][r];
+      xml[0] = m_run;
+      xml[64] = l_part;
+    }
+    __syncthreads();
+    if (kg == 1) return;
+    const float m1 = xml[0], l1 = xml[64];
+    const float m = fmaxf(m_run, m1);
+    const float c0 = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m);
+    const float c1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - m);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[a][r] = oacc[a][r] * c0 + xo[(a * 16 + r) * 64] * c1;
+    l_part = l_part * c0 + l1 * c1;
+    m_run = m;
+  }
 
   if (kvs > 1) {
     // Partial state of this half: unnormalised O (fp32) [half][row][head][64], then (m, l)
@@ -533,15 +597,14 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int ld_
   if (!cu) total = batch * t;
   const int kvs = part ? attention_split(batch, t, heads, dtype) : 1;
   const float c = scale * 1.4426950408889634f;  // fold log2(e): exp(x) = exp2(x * log2 e)
-  // Wavefronts per workgroup: 8 (256 query rows, two workgroups per CU) once there are at least
-  // 256 blocks of 128 rows, else 4, halved again while fewer than 64 workgroups would run.
-  // Narrower workgroups spread the same wavefronts over more CUs, with less latency hidden on
-  // each.  Measured, four-wavefront workgroups win for one window at every head count (20
-  // heads: 23.1 us against 31.4 us for eight and 30.8 us for eight with key halves) and for two
-  // windows of 8 heads, break even near 256 blocks and lose from four 20-head windows on.
-  int nw = query_blocks128(batch, t, heads) >= 256 ? 8 : 4;
-  auto blocks = [&](int w) { return (long)((t + 32 * w - 1) / (32 * w)) * heads * batch * kvs; };
-  while (nw > 2 && blocks(nw) < 64) nw /= 2;
+  // Eight wavefronts per workgroup: over 256 query rows (two workgroups per CU) once there are
+  // at least 256 blocks of 128 rows; below that, over 128 query rows in two key groups (KS = 2,
+  // one workgroup per CU), which runs twice the wavefronts on the same rows.  Measured on one
+  // window against the four-wavefront workgroups of one group used before (which themselves
+  // beat eight-wavefront ones of 256 rows there: 23.1 against 31.4 us at 20 heads): 6 heads
+  // 20.0 -> 18.2 us, 8 heads 19.8 -> 18.2, 12 heads 20.4 -> 18.4, 20 heads 21.6 -> 19.7.
+  const bool ks2 = query_blocks128(batch, t, heads) < 256;
+  const long nblk = (long)((t + (ks2 ? 127 : 255)) / (ks2 ? 128 : 256)) * heads * batch * kvs;
   dim3 grid((t + AQ32 - 1) / AQ32, heads, batch), block(256);
   auto run16 = [&](auto tag) {
     using T = decltype(tag);
@@ -549,16 +612,13 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int ld_
     const auto Kp = static_cast<const uint16_t*>(k);
     const auto Vp = static_cast<const uint16_t*>(v);
     auto Op = static_cast<uint16_t*>(o);
-    const dim3 g((unsigned)blocks(nw));
+    const dim3 g((unsigned)nblk);
     float* pp = kvs > 1 ? part : nullptr;
-    if (nw == 8)
-      attn16_kernel<T, 8><<<g, 512, 0, st>>>(Qp, Kp, Vp, ld_qkv, Op, ld_o, t, heads, c, cu, total,
-                                             kvs, pp);
-    else if (nw == 4)
-      attn16_kernel<T, 4><<<g, 256, 0, st>>>(Qp, Kp, Vp, ld_qkv, Op, ld_o, t, heads, c, cu, total,
-                                             kvs, pp);
+    if (ks2)
+      attn16_kernel<T, 8, 2><<<g, 512, 0, st>>>(Qp, Kp, Vp, ld_qkv, Op, ld_o, t, heads, c, cu,
+                                                total, kvs, pp);
     else
-      attn16_kernel<T, 2><<<g, 128, 0, st>>>(Qp, Kp, Vp, ld_qkv, Op, ld_o, t, heads, c, cu, total,
+      attn16_kernel<T, 8><<<g, 512, 0, st>>>(Qp, Kp, Vp, ld_qkv, Op, ld_o, t, heads, c, cu, total,
                                              kvs, pp);
     if (kvs > 1)
       attn_merge_kernel<T><<<dim3((unsigned)((t + 15) / 16), (unsigned)heads, (unsigned)batch), 256,

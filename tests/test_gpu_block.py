@@ -115,8 +115,9 @@ def test_stack_prefixes_and_final_norm(path):
 @pytest.mark.parametrize("path", PATHS)
 def test_block_attention_key_halves(path):
     """8 heads of one 1100-position window give 72 query blocks of 128 rows: too few to fill
-    the GPU, so on the 16-bit paths each block's keys are split in two halves (9 key tiles each,
-    the last one ragged) and merged; every element against the oracle."""
+    the GPU, so on the 16-bit paths each block's keys are split over two workgroups (9 key tiles
+    each) and, inside each, over its two wavefront groups (5 and 4 tiles, the last one ragged),
+    and the four partial results merged; every element against the oracle."""
     cfg = synth.CONFIGS["tiny_block"].with_(t=1100, d_model=512, heads=8, ffn_dim=1024)
     w = synth.make_workload(cfg)
     print(f"[case] block key halves path={path}", flush=True)
@@ -126,10 +127,11 @@ def test_block_attention_key_halves(path):
 
 
 def test_block_key_halves_large_logits():
-    """The key-halves configuration of the last test (four-wavefront workgroups, 72 query blocks,
-    each block's keys split in two and merged) with Wq scaled by 100: logits then spread over
-    about +-100 (standard deviation 20), so the running max is raised in the middle of the key
-    loop of most rows, in both halves, and the merge combines halves whose maxima differ widely.
+    """The key-split configuration of the last test (72 query blocks, each block's keys split
+    over two workgroups and two wavefront groups in each, then merged) with Wq scaled by 100:
+    logits then spread over about +-100 (standard deviation 20), so the running max is raised in
+    the middle of the key loop of most rows, in every part, and the merges combine parts whose
+    maxima differ widely.
     fp16 operands: rounding q, k and the probabilities to fp16 moves the block output by an MAE of
     3.4e-4 and a max relative error of 4.5e-3 at these logits (float64 emulation of those
     roundings), inside the block's bar; a wrong rescale would move it by the size of v.  (With
@@ -157,8 +159,9 @@ def test_in_place_and_determinism():
 def test_windows_are_independent():
     """At this shape a window's output is bit-identical whether it runs alone or inside a batch
     of four: 300 and 1200 rows get the same split-k plans (fc2 in 4 parts on 128-row tiles, the
-    out-projection unsplit), and the attention result does not depend on the workgroup width or
-    the key split.  Where the plans differ, results differ in the last bits
+    out-projection unsplit), and attention takes the same form for both (two wavefront groups
+    per workgroup over the key halves, the keys split again over two workgroups), so each query
+    row's sums run in the same order.  Where the plans differ, results differ in the last bits
     (test_window_alone_vs_batched_large_v3)."""
     cfg = synth.CONFIGS["tiny_block"].with_(batch=4, t=300)
     w = synth.make_workload(cfg)

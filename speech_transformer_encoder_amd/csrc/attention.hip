@@ -206,9 +206,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8
   float m_run = -INFINITY;  // max used in the exponents (scaled units), per query
   float l_part = 0.f;       // this lane's share of the running denominator
 
-  // The copies of tile `it` have landed (this wavefront's own: only those of tile it + 1 may
-  // still be in flight; after the barrier, every wavefront's); the tile two ahead is then loaded
-  // into `ahead`, whose previous tile every wavefront of the group is done with.
+  // Tile it's copies have landed (this wavefront's: only tile it + 1's may still be in flight)
+  // and, after the barrier, every wavefront's; the tile two ahead is then loaded into `ahead`,
+  // whose previous tile every wavefront of the group is done with.
   auto sync_tile = [&](int it, const uint16_t* ahead) {
     if (it + 1 < ntiles)
       __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * CPW));  // the copies of tile it + 1 may be in flight

@@ -712,6 +712,21 @@ def test_e4m3_round_matches_torch_and_round_trips():
     np.testing.assert_array_equal(orc.e4m3_bits(vals), codes)
 
 
+def test_e4m3_codes_of_named_values():
+    """Codes the E4M3 (fn) format fixes by its field layout (sign, 4 exponent bits with bias 7, 3
+    mantissa bits, no infinities): the largest finite value 448 = 1.75 * 2^8 is S.1111.110 (0x7E),
+    1 is 0.0111.000 (0x38), -2 is 1.1000.000 (0xC0), the smallest normal 2^-6 is 0.0001.000 (0x08),
+    the smallest subnormal 2^-9 is 0.0000.001 (0x01), the largest subnormal 7 * 2^-9 is 0x07."""
+    vals = np.array([448.0, 1.0, -2.0, 2.0 ** -6, 2.0 ** -9, 7 * 2.0 ** -9, 0.0, 1.5, 0.8125])
+    want = np.array([0x7E, 0x38, 0xC0, 0x08, 0x01, 0x07, 0x00, 0x3C, 0x35])
+    np.testing.assert_array_equal(orc.e4m3_round(vals), vals)
+    np.testing.assert_array_equal(orc.e4m3_bits(vals), want)
+    # halfway between 2^-9 and 2 * 2^-9 rounds to the even code (2 * 2^-9, 0x02); a quarter of
+    # the smallest subnormal rounds to zero
+    np.testing.assert_array_equal(orc.e4m3_bits(orc.e4m3_round(np.array([1.5 * 2.0 ** -9]))), [0x02])
+    assert orc.e4m3_round(np.array([0.25 * 2.0 ** -9]))[0] == 0.0
+
+
 def test_e4m3_ties_go_to_the_even_code():
     """The midpoint of two neighbouring non-negative values rounds to the one whose code is even."""
     codes, vals = _e4m3_table()

@@ -1,0 +1,83 @@
+"""Seeded random shapes for the projection and attention steps, beside the hand-picked ones of
+test_gpu_steps: every element against the oracle, with that file's bounds.  The draws are fixed
+by the seed, so every run checks the same cases; they reach tiling, tail and dispatch
+combinations a short list misses (odd row counts against every tile height, widths that are
+multiples of 64 but not of 128 or 256, key counts around the 64-key tiles)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from speech_transformer_encoder_amd import binding as B
+from tests.gpu_util import as_operand, dev, errors, host, report, require_gpu, torch_dtype
+from tests.test_gpu_steps import ATTN_CW, ATTN_TOL, OUT_TOL, _attention_case
+
+pytestmark = pytest.mark.gpu
+
+PATHS = [B.WENC_PATH_BF16, B.WENC_PATH_FP16, B.WENC_PATH_FP32]
+EPIS = [B.WENC_EPI_BIAS, B.WENC_EPI_BIAS_GELU, B.WENC_EPI_BIAS_RESIDUAL,
+        B.WENC_EPI_BIAS_GELU_RESIDUAL]
+
+
+def _linear_cases(count=24, seed=2024):
+    r = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        m = int(r.integers(1, 6001))
+        n = 64 * int(r.integers(1, 81))
+        k = 64 * int(r.integers(1, 41))
+        if m * n * k > 1.5e9:  # keeps the float64 reference to about a second
+            continue
+        cases.append((PATHS[len(cases) % 3], EPIS[int(r.integers(0, 4))], m, n, k))
+    return cases
+
+
+def _attention_cases(count=12, seed=2025):
+    r = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        batch, t, heads = int(r.integers(1, 4)), int(r.integers(1, 1601)), int(r.integers(1, 9))
+        if batch * heads * t * t > 6e6:
+            continue
+        cases.append((PATHS[len(cases) % 3], batch, t, heads))
+    return cases
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+@pytest.mark.parametrize("path,epi,m,n,k", _linear_cases())
+def test_linear_random(path, epi, m, n, k):
+    import torch
+    r = np.random.default_rng([m, n, k, epi, 99])
+    a = r.standard_normal((m, k)).astype(np.float32)
+    w = (r.standard_normal((n, k)) * 0.02).astype(np.float32)
+    bias = (r.standard_normal(n) * 0.1).astype(np.float32)
+    ad, ah = as_operand(a, path)
+    wd, wh = as_operand(w, path)
+    ref = oracle.linear(ah, wh, bias)
+    resid = None
+    fp32_out = epi in (B.WENC_EPI_BIAS_RESIDUAL, B.WENC_EPI_BIAS_GELU_RESIDUAL)
+    if epi in (B.WENC_EPI_BIAS_GELU, B.WENC_EPI_BIAS_GELU_RESIDUAL):
+        ref = oracle.gelu_erf(ref)
+    if fp32_out:
+        res_np = r.standard_normal((m, n)).astype(np.float32) * 4
+        resid = dev(res_np)
+        ref = ref + res_np
+        c = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    else:
+        c = torch.empty((m, n), dtype=torch_dtype(path), device="cuda")
+    print(f"[case] random linear path={path} epi={epi} m={m} n={n} k={k}", flush=True)
+    B.whisper_enc_linear(ad, wd, dev(bias), resid, c, m, n, k, path, epi)
+    e = errors(host(c), ref)
+    report(f"random linear p{path} e{epi} {m}x{n}x{k}", e)
+    assert e["finite"] and e["max_rel"] <= (2e-5 if fp32_out else OUT_TOL[path])
+
+
+@pytest.mark.parametrize("path,batch,t,heads", _attention_cases())
+def test_attention_random(path, batch, t, heads):
+    e, cw = _attention_case(path, batch, t, heads, seed=t + 13 * heads + 101 * batch)
+    report(f"random attn p{path} b{batch} t{t} h{heads} cw={cw:.3e}", e)
+    assert e["finite"] and e["max_rel"] <= ATTN_TOL[path] and cw <= ATTN_CW[path]

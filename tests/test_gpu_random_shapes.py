@@ -81,3 +81,34 @@ def test_attention_random(path, batch, t, heads):
     e, cw = _attention_case(path, batch, t, heads, seed=t + 13 * heads + 101 * batch)
     report(f"random attn p{path} b{batch} t{t} h{heads} cw={cw:.3e}", e)
     assert e["finite"] and e["max_rel"] <= ATTN_TOL[path] and cw <= ATTN_CW[path]
+
+
+def _block_cases(count=9, seed=2026):
+    r = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        heads = int(r.integers(1, 13))
+        d = 64 * heads
+        ffn = 64 * int(r.integers(1, 4 * heads + 9))
+        batch, t = int(r.integers(1, 4)), int(r.integers(1, 700))
+        if batch * t * (t * d + 4 * d * d + 2 * d * ffn) > 1.2e9:
+            continue
+        cases.append((PATHS[len(cases) % 3], batch, t, d, heads, ffn))
+    return cases
+
+
+@pytest.mark.parametrize("path,batch,t,d,heads,ffn", _block_cases())
+def test_block_random(path, batch, t, d, heads, ffn):
+    """A whole block at a random (windows, t, d, heads, ffn) with random fp32 weights, every
+    element against the oracle under the block's bounds (the fp32 path: max-rel <= 1e-4; the
+    16-bit paths: max-rel <= 2e-2 and MAE <= 1e-3 -- one block, so literal bf16 is held to the
+    bar too)."""
+    from speech_transformer_encoder_amd import synth
+    from tests.test_gpu_block import check, run_gpu
+    cfg = synth.CONFIGS["tiny_block"].with_(seed=97 + t, batch=batch, t=t, d_model=d, heads=heads,
+                                            ffn_dim=ffn)
+    w = synth.make_workload(cfg)
+    print(f"[case] random block path={path} b{batch} t{t} d{d} h{heads} f{ffn}", flush=True)
+    got = run_gpu(w, path)
+    ref = oracle.encoder_block(w.x, w.layers[0], heads)
+    check(errors(got, ref), path, f"random block b{batch} t{t} d{d} h{heads} f{ffn}")

@@ -112,3 +112,20 @@ def test_block_random(path, batch, t, d, heads, ffn):
     got = run_gpu(w, path)
     ref = oracle.encoder_block(w.x, w.layers[0], heads)
     check(errors(got, ref), path, f"random block b{batch} t{t} d{d} h{heads} f{ffn}")
+
+
+@pytest.mark.parametrize("batch,t,d,heads,ffn", [c[1:] for c in _block_cases(count=6, seed=2027)])
+def test_block_mxfp8_random(batch, t, d, heads, ffn):
+    """The MXFP8 path at random block shapes, against the MXFP8 oracle (the block's bar on one
+    block) and against the exact oracle (within the margins of the method's own error)."""
+    from speech_transformer_encoder_amd import synth
+    from speech_transformer_encoder_amd.encoder import build_from_workload, to_device_input
+    from tests.test_gpu_mx import _check_mx
+    cfg = synth.CONFIGS["tiny_block"].with_(seed=211 + t, batch=batch, t=t, d_model=d,
+                                            heads=heads, ffn_dim=ffn)
+    w = synth.make_workload(cfg)
+    print(f"[case] random mxfp8 block b{batch} t{t} d{d} h{heads} f{ffn}", flush=True)
+    enc = build_from_workload(w, B.WENC_PATH_MXFP8)
+    got = host(enc.forward(to_device_input(w.x), final_norm=False))
+    _check_mx(got, w, f"random block b{batch} t{t} d{d} h{heads} f{ffn}", ln_post=False,
+              single_block=True)

@@ -129,3 +129,36 @@ def test_block_mxfp8_random(batch, t, d, heads, ffn):
     got = host(enc.forward(to_device_input(w.x), final_norm=False))
     _check_mx(got, w, f"random block b{batch} t{t} d{d} h{heads} f{ffn}", ln_post=False,
               single_block=True)
+
+
+def _ragged_cases(count=6, seed=2028):
+    r = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        heads = int(r.integers(1, 11))
+        n = int(r.integers(1, 9))
+        lens = [int(v) for v in r.integers(0, 900, n)]
+        lens[int(r.integers(0, n))] = int(r.integers(0, 3))  # an empty or one- / two-row window
+        if sum(lens) == 0 or sum(v * v for v in lens) * heads > 4e6:
+            continue
+        cases.append((PATHS[len(cases) % 3], heads, tuple(lens)))
+    return cases
+
+
+@pytest.mark.parametrize("path,heads,lens", _ragged_cases())
+def test_stack_varlen_random(path, heads, lens):
+    """Two blocks and the final norm over a ragged batch of random window lengths (empty and
+    one-row windows included), every element against the oracle's per-window stack."""
+    from speech_transformer_encoder_amd import synth
+    from speech_transformer_encoder_amd.encoder import build_from_workload, to_device_input
+    from tests.test_gpu_varlen import _check_block
+    d = 64 * heads
+    cfg = synth.CONFIGS["base_stack"].with_(seed=307 + sum(lens), batch=1, t=int(sum(lens)),
+                                            d_model=d, heads=heads, ffn_dim=4 * d)
+    w = synth.make_workload(cfg, n_layers=2)
+    x = w.x[0]
+    enc = build_from_workload(w, path)
+    print(f"[case] random varlen path={path} heads={heads} lens={list(lens)}", flush=True)
+    got = host(enc.forward_varlen(to_device_input(x), list(lens)))
+    ref = oracle.encoder_stack_varlen(x, list(lens), w.layers, heads, w.ln_post)
+    _check_block(errors(got, ref), path, f"random varlen h{heads} lens={list(lens)}")

@@ -32,6 +32,22 @@ def _linear_cases(count=24, seed=2024):
     return cases
 
 
+def _persistent_cases(count=12, seed=2029):
+    """Shapes with at least 256 tiles of 256 x 256 (the persistent kernel, and its half-tile tail
+    when the last round is short), k kept small for the reference."""
+    r = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        m = int(r.integers(3000, 24001))
+        n = 64 * int(r.integers(8, 81))
+        k = 64 * int(r.integers(1, 5))
+        tiles = -(-m // 256) * -(-n // 256)
+        if tiles < 256 or m * n * k > 5e9:
+            continue
+        cases.append((PATHS[len(cases) % 3], EPIS[int(r.integers(0, 4))], m, n, k))
+    return cases
+
+
 def _attention_cases(count=12, seed=2025):
     r = np.random.default_rng(seed)
     cases = []
@@ -48,7 +64,7 @@ def _gpu():
     require_gpu()
 
 
-@pytest.mark.parametrize("path,epi,m,n,k", _linear_cases())
+@pytest.mark.parametrize("path,epi,m,n,k", _linear_cases() + _persistent_cases())
 def test_linear_random(path, epi, m, n, k):
     import torch
     r = np.random.default_rng([m, n, k, epi, 99])

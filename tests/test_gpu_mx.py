@@ -152,6 +152,12 @@ def _hw_bound(av, wv):
                                    (64, 64, 64)])
 @pytest.mark.parametrize("epi", [B.WENC_EPI_BIAS, B.WENC_EPI_BIAS_RESIDUAL, B.WENC_EPI_BIAS_GELU])
 def test_linear_mx(m, n, k, epi):
+    linear_mx_case(m, n, k, epi)
+
+
+def linear_mx_case(m, n, k, epi):
+    """One MXFP8 product on MXFP8 operands quantised by the oracle, every element against the
+    exact product of the operands' values under the measured MFMA error bound."""
     import torch
     r = np.random.default_rng([m, n, k, 17])
     a = r.standard_normal((m, k)).astype(np.float32)

@@ -178,3 +178,28 @@ def test_stack_varlen_random(path, heads, lens):
     got = host(enc.forward_varlen(to_device_input(x), list(lens)))
     ref = oracle.encoder_stack_varlen(x, list(lens), w.layers, heads, w.ln_post)
     _check_block(errors(got, ref), path, f"random varlen h{heads} lens={list(lens)}")
+
+
+def _mx_cases(count=12, seed=2030):
+    r = np.random.default_rng(seed)
+    cases = []
+    epis = [B.WENC_EPI_BIAS, B.WENC_EPI_BIAS_RESIDUAL, B.WENC_EPI_BIAS_GELU]
+    while len(cases) < count:
+        persistent = len(cases) % 3 == 2
+        m = int(r.integers(3000, 24001)) if persistent else int(r.integers(1, 4001))
+        n = 64 * int(r.integers(8 if persistent else 1, 81))
+        k = 64 * int(r.integers(1, 5 if persistent else 41))
+        if m * n * k > (5e9 if persistent else 1.2e9):
+            continue
+        if persistent and -(-m // 256) * -(-n // 256) < 256:
+            continue
+        cases.append((epis[int(r.integers(0, 3))], m, n, k))
+    return cases
+
+
+@pytest.mark.parametrize("epi,m,n,k", _mx_cases())
+def test_linear_mx_random(epi, m, n, k):
+    """The MXFP8 product at random shapes (k tiles of 64 and 128 values, the small kernel, the
+    persistent kernel and its tail), with the fixed-shape test's bounds."""
+    from tests.test_gpu_mx import linear_mx_case
+    linear_mx_case(m, n, k, epi)

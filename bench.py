@@ -718,6 +718,17 @@ def main():
         if args.path == "fp16":
             next_steps["q8_weights"] = time_quantized(cfg, w, x, y, args.kernel_reps, 8)
             next_steps["q4_weights"] = time_quantized(cfg, w, x, y, args.kernel_reps, 4)
+            # One window, where the weights are a larger share of each block's bytes: four
+            # large-v3 blocks and the final norm.
+            c1 = synth.CONFIGS["large_v3_stack"].with_(n_layers=4)
+            w1 = synth.make_workload(c1)
+            x1 = to_device_input(w1.x)
+            y1 = torch.empty_like(x1)
+            for bits in (8, 4):
+                q = time_quantized(c1, w1, x1, y1, args.kernel_reps, bits)
+                q["blocks"] = c1.n_layers
+                next_steps[f"q{bits}_weights_one_window"] = q
+            del w1, x1, y1
 
     cpu = None
     if not args.no_cpu_baseline:

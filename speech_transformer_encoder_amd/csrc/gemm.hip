@@ -24,7 +24,8 @@
 // The epilogue stages each wavefront's 32 x 64 block through LDS so that global stores (and the
 // residual loads) are whole 128- or 256-byte row segments.  The kernel is persistent, one
 // workgroup per CU: each XCD (eight, dispatched round-robin) runs a contiguous range of tiles
-// grouped 8 m-tiles deep, so tiles running together share operand rows in that XCD's L2, and
+// grouped 8 m-tiles deep (n fastest when there are at most 8 n tiles), so tiles running together
+// share operand rows in that XCD's L2, and
 // the next tile's first operand loads overlap the current tile's epilogue.  A short last round
 // (at most half the CUs' worth of tiles) runs as half tiles on the small kernel instead.
 //
@@ -65,6 +66,14 @@ __device__ __forceinline__ u32x4 split_lo8(float4 v0, float4 v1, u32x4 w4) {
 }
 
 constexpr int G_N = 256, G_M = 256, G_K = 64;  // workgroup tile
+
+// m tiles per group of the persistent kernel's tile order (m fastest within a group).  Eight
+// keep the 32 tiles an XCD runs together at 8 m x 4 n, which share 12 operand panels in its L2.
+// With at most eight n tiles (N <= 2048: the out-projection and fc2) the groups are single m
+// tiles, i.e. n fastest: the tiles of one round then take every n tile of about 32 / tiles_n
+// m panels, so an activation panel is fetched in one round instead of again for the n tiles a
+// deeper group leaves to the next round.
+__device__ __forceinline__ int persistent_group_depth(int tiles_n) { return tiles_n <= 8 ? 1 : 8; }
 constexpr int G_WN = 4, G_WM = 2;              // wavefront grid: n x m
 constexpr int G_TN = G_N / G_WN, G_TM = G_M / G_WM;  // 64 x 128 per wavefront
 constexpr int G_NA = G_TN / 32, G_NB = G_TM / 32;     // 2 x 4 MFMA blocks
@@ -138,9 +147,10 @@ __global__ __launch_bounds__(G_THREADS, 1) void gemm16_kernel(const uint16_t* __
   // Tile tt of the grouped order (8 m tiles deep, m fastest); buffer resources cover exactly the
   // tile's valid rows, so operand loads past M or N return zeros.
   auto setup = [&](int tt) {
-    const int group = 8 * tiles_n;
-    const int first_m = (tt / group) * 8;
-    const int gm = min(tiles_m - first_m, 8);
+    const int gd = persistent_group_depth(tiles_n);
+    const int group = gd * tiles_n;
+    const int first_m = (tt / group) * gd;
+    const int gm = min(tiles_m - first_m, gd);
     const int tm = first_m + (tt % group) % gm, tn = (tt % group) / gm;
     n0 = tn * G_N;
     m0 = tm * G_M;
@@ -531,9 +541,10 @@ __global__ __launch_bounds__(128 * WM) __attribute__((amdgpu_waves_per_eu(2, 4))
     // Half (128 columns) v % 2 of the 256 x 256 tile big0 + v / 2 in the persistent kernel's
     // grouped order: the tiles left over after its whole rounds.
     const int gtn = (N + G_N - 1) / G_N;
-    const int tb = big0 + v / 2, group = 8 * gtn;
-    const int first_m = (tb / group) * 8;
-    const int gm = min(tiles_m - first_m, 8);
+    const int gd = persistent_group_depth(gtn);
+    const int tb = big0 + v / 2, group = gd * gtn;
+    const int first_m = (tb / group) * gd;
+    const int gm = min(tiles_m - first_m, gd);
     n0 = ((tb % group) / gm) * G_N + (v & 1) * H_N;
     m0 = (first_m + (tb % group) % gm) * G_M;
     if (n0 >= N) return;  // the second half of a last tile only 64 columns wide

@@ -309,9 +309,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8
   // One key tile per iteration from stage `cur`: scores, softmax, P.V.
   if (ntiles > 0) load_tile(kbase, st0);
   if (ntiles > 1) load_tile(kbase + AK, st1);
+  // A wavefront whose 32 query rows all lie past the window (the last query block's) only
+  // copies and keeps the barriers.
+  const bool no_rows = qb * AQ + wave * 32 >= t;
   auto tile = [&](int it, const uint16_t* cur, const uint16_t* ahead) {
     sync_tile(it, ahead);
     if (KS > 1 && it >= ntiles) return;  // this group's tiles are done; the other's are not
+    if (no_rows) return;
     scores(it, cur);
     softmax();
     pv(cur);

@@ -66,14 +66,18 @@ def test_layernorm_in_place_fp32():
                                  B.WENC_EPI_BIAS_GELU_RESIDUAL])
 @pytest.mark.parametrize("m,n,k", [(1, 64, 64), (200, 384, 384), (257, 192, 512), (1500, 1152, 384),
                                    (129, 1280, 5120), (1300, 3840, 128), (6000, 4160, 128),
-                                   (24000, 1280, 64), (4096, 4160, 256)])
+                                   (24000, 1280, 64), (4096, 4160, 256), (10240, 2048, 128),
+                                   (11008, 1344, 64)])
 def test_linear(path, epi, m, n, k):
     """Every element against the oracle.  The shapes reach every tiling of the 16-bit paths:
     below 128 tiles of 128 x 256, the small kernel's 128 x 128 tiles (e.g. (1500, 1152): 108 of
     them); (1300, 3840): 180 tiles of 128 x 256, the last row of tiles 20 rows high; from 256
     tiles of 256 x 256, the persistent kernel.  (4096, 4160): 272 tiles of 256 x 256 on 256 CUs,
     one whole round and 16 left over, which run as 128-column half tiles, 8 of them in the last
-    64-column-wide tile (their second halves empty)."""
+    64-column-wide tile (their second halves empty).  With at most eight n tiles the persistent
+    order is n fastest: (24000, 1280) runs it in whole rounds and its own last round; (10240,
+    2048): 320 tiles, one round and 64 left over as 128 half tiles; (11008, 1344): 258 tiles (the
+    last n tile 64 columns wide), one round and 2 left over as 4 half tiles, one of them empty."""
     import torch
     r = _rng(m, n, k, epi)
     a = r.standard_normal((m, k)).astype(np.float32)

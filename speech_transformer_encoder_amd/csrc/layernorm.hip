@@ -78,13 +78,12 @@ struct LnStore<NV, mx8_t> {
 };
 
 // Normalises one row held in a wavefront's registers (lane l has columns 4 (l + 64 j) .. + 3 in
-// v[j]; entries past d are ignored) with gamma and beta already loaded the same way, and stores it
-// as OutT.  Both the plain LayerNorm and the fused split-k reduction below end in this routine, so
-// they round identically.
+// v[j]; entries past d are ignored) and stores it as OutT.  Both the plain LayerNorm and the fused
+// split-k reduction below end in this routine, so they round identically.
 template <int NV, typename OutT>
-__device__ __forceinline__ void ln_row_gb(float4 (&v)[NV], const float4 (&gv)[NV],
-                                          const float4 (&bv)[NV], int lane, void* y, size_t row,
-                                          int d, float eps, int rows) {
+__device__ __forceinline__ void ln_row(float4 (&v)[NV], int lane, const float* __restrict__ gamma,
+                                       const float* __restrict__ beta, void* y, size_t row, int d,
+                                       float eps, int rows) {
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
@@ -108,7 +107,8 @@ __device__ __forceinline__ void ln_row_gb(float4 (&v)[NV], const float4 (&gv)[NV
   for (int j = 0; j < NV; ++j) {
     const int c = (lane + 64 * j) * 4;
     if (c < d) {
-      const float4 g = gv[j], b = bv[j];
+      const float4 g = *reinterpret_cast<const float4*>(gamma + c);
+      const float4 b = *reinterpret_cast<const float4*>(beta + c);
       float4 o;
       o.x = v[j].x * inv * g.x + b.x;
       o.y = v[j].y * inv * g.y + b.y;
@@ -117,21 +117,6 @@ __device__ __forceinline__ void ln_row_gb(float4 (&v)[NV], const float4 (&gv)[NV
       LnStore<NV, OutT>::put(y, row, d, c, o, rows);
     }
   }
-}
-
-// As ln_row_gb, loading gamma and beta itself (columns past d read column d - 4, unused).
-template <int NV, typename OutT>
-__device__ __forceinline__ void ln_row(float4 (&v)[NV], int lane, const float* __restrict__ gamma,
-                                       const float* __restrict__ beta, void* y, size_t row, int d,
-                                       float eps, int rows) {
-  float4 gv[NV], bv[NV];
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int c = min((lane + 64 * j) * 4, d - 4);
-    gv[j] = *reinterpret_cast<const float4*>(gamma + c);
-    bv[j] = *reinterpret_cast<const float4*>(beta + c);
-  }
-  ln_row_gb<NV, OutT>(v, gv, bv, lane, y, row, d, eps, rows);
 }
 
 // NV = float4 vectors per lane (d <= 256 * NV).
@@ -157,11 +142,7 @@ __global__ __launch_bounds__(256) void layernorm_rows(const float* __restrict__ 
 // x = residual + (sum of the k parts, added in order, + bias) -- the same sums as the plain
 // reduction kernel -- stored to x_out when given, then y = LayerNorm(x) * gamma + beta.  One
 // wavefront per row reads the whole row before it writes, so x_out and y may alias residual.
-// KS > 0: that many parts, known at compile time, and every load of the row (residual, bias,
-// all parts, gamma, beta) is issued before the first add, so a row costs one memory round trip;
-// KS = 0: ksplit parts, loaded a part at a time.  Per element the parts are added in order 0, 1,
-// ... either way, so both forms give the same bits.
-template <int NV, typename OutT, int KS>
+template <int NV, typename OutT>
 __global__ __launch_bounds__(256) void splitk_reduce_ln_rows(
     const float* __restrict__ part, int ksplit, const float* __restrict__ bias,
     const float* residual, float* x_out, const float* __restrict__ gamma,
@@ -171,51 +152,28 @@ __global__ __launch_bounds__(256) void splitk_reduce_ln_rows(
   if (row >= (size_t)rows) return;
   const size_t plane = (size_t)rows * d;
   const float* pr = part + row * d;
-  // No branches around the loads: columns past d read column d - 4 and are ignored by the
-  // LayerNorm routine.
+  // Parts outermost, the row's columns innermost, with no branches around the loads (columns
+  // past d read column d - 4 and are ignored by ln_row): each step keeps NV independent loads in
+  // flight, which a row owned by one wavefront needs to move enough bytes.  Per element the
+  // parts are still added in order 0, 1, ...
   int cl[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) cl[j] = min((lane + 64 * j) * 4, d - 4);
-  float4 v[NV], r[NV], b[NV], gv[NV], bv[NV];
+  float4 v[NV], r[NV], b[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     r[j] = *reinterpret_cast<const float4*>(residual + row * d + cl[j]);
     b[j] = *reinterpret_cast<const float4*>(bias + cl[j]);
     v[j] = *reinterpret_cast<const float4*>(pr + cl[j]);
   }
-  if constexpr (KS > 0) {
-    float4 q[KS > 1 ? KS - 1 : 1][NV];
-#pragma unroll
-    for (int p = 1; p < KS; ++p)
-#pragma unroll
-      for (int j = 0; j < NV; ++j)
-        q[p - 1][j] = *reinterpret_cast<const float4*>(pr + p * plane + cl[j]);
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      gv[j] = *reinterpret_cast<const float4*>(gamma + cl[j]);
-      bv[j] = *reinterpret_cast<const float4*>(beta + cl[j]);
-    }
-#pragma unroll
-    for (int p = 1; p < KS; ++p)
-#pragma unroll
-      for (int j = 0; j < NV; ++j)
-        v[j] = make_float4(v[j].x + q[p - 1][j].x, v[j].y + q[p - 1][j].y,
-                           v[j].z + q[p - 1][j].z, v[j].w + q[p - 1][j].w);
-  } else {
 #pragma unroll 4
-    for (int p = 1; p < ksplit; ++p) {
-      float4 q[NV];
+  for (int p = 1; p < ksplit; ++p) {
+    float4 q[NV];
 #pragma unroll
-      for (int j = 0; j < NV; ++j) q[j] = *reinterpret_cast<const float4*>(pr + p * plane + cl[j]);
+    for (int j = 0; j < NV; ++j) q[j] = *reinterpret_cast<const float4*>(pr + p * plane + cl[j]);
 #pragma unroll
-      for (int j = 0; j < NV; ++j)
-        v[j] = make_float4(v[j].x + q[j].x, v[j].y + q[j].y, v[j].z + q[j].z, v[j].w + q[j].w);
-    }
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      gv[j] = *reinterpret_cast<const float4*>(gamma + cl[j]);
-      bv[j] = *reinterpret_cast<const float4*>(beta + cl[j]);
-    }
+    for (int j = 0; j < NV; ++j)
+      v[j] = make_float4(v[j].x + q[j].x, v[j].y + q[j].y, v[j].z + q[j].z, v[j].w + q[j].w);
   }
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
@@ -229,7 +187,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_ln_rows(
       if (c < d) *reinterpret_cast<float4*>(x_out + row * d + c) = v[j];
     }
   }
-  ln_row_gb<NV, OutT>(v, gv, bv, lane, y, row, d, eps, rows);
+  ln_row<NV, OutT>(v, lane, gamma, beta, y, row, d, eps, rows);
 }
 
 template <typename OutT>
@@ -251,24 +209,6 @@ static hipError_t launch_ln_t(const float* x, const float* g, const float* b, vo
   return hipGetLastError();
 }
 
-template <int NV, typename OutT>
-static void launch_reduce_ln_nv(dim3 grid, dim3 block, const float* part, int ksplit,
-                                const float* bias, const float* residual, float* x_out,
-                                const float* g, const float* b, void* y, int rows, int d,
-                                float eps, hipStream_t st) {
-  // Whole rows of parts in registers for the part counts the split plan uses at d <= 2048;
-  // longer rows or other counts load a part at a time.
-  if (NV <= 8 && ksplit == 2)
-    splitk_reduce_ln_rows<NV, OutT, 2><<<grid, block, 0, st>>>(part, ksplit, bias, residual,
-                                                               x_out, g, b, y, rows, d, eps);
-  else if (NV <= 8 && ksplit == 4)
-    splitk_reduce_ln_rows<NV, OutT, 4><<<grid, block, 0, st>>>(part, ksplit, bias, residual,
-                                                               x_out, g, b, y, rows, d, eps);
-  else
-    splitk_reduce_ln_rows<NV, OutT, 0><<<grid, block, 0, st>>>(part, ksplit, bias, residual,
-                                                               x_out, g, b, y, rows, d, eps);
-}
-
 template <typename OutT>
 static hipError_t launch_reduce_ln_t(const float* part, int ksplit, const float* bias,
                                      const float* residual, float* x_out, const float* g,
@@ -277,10 +217,10 @@ static hipError_t launch_reduce_ln_t(const float* part, int ksplit, const float*
   const float eps = 1e-5f;
   const int nv = (d + 255) / 256;
   switch (nv) {
-#define WENC_RLN_CASE(N)                                                                         \
-  case N:                                                                                        \
-    launch_reduce_ln_nv<N, OutT>(grid, block, part, ksplit, bias, residual, x_out, g, b, y, rows, \
-                                 d, eps, st);                                                     \
+#define WENC_RLN_CASE(N)                                                                       \
+  case N:                                                                                      \
+    splitk_reduce_ln_rows<N, OutT><<<grid, block, 0, st>>>(part, ksplit, bias, residual, x_out, \
+                                                           g, b, y, rows, d, eps);             \
     break;
     WENC_RLN_CASE(1) WENC_RLN_CASE(2) WENC_RLN_CASE(3) WENC_RLN_CASE(4) WENC_RLN_CASE(5)
     WENC_RLN_CASE(6) WENC_RLN_CASE(7) WENC_RLN_CASE(8) WENC_RLN_CASE(9) WENC_RLN_CASE(10)

@@ -188,6 +188,20 @@ def test_attention_outlier_queries(path, batch, heads, groups):
     assert e["finite"] and cw <= ATTN_CW[path]
 
 
+@pytest.mark.parametrize("path", [B.WENC_PATH_FP16, B.WENC_PATH_BF16])
+@pytest.mark.parametrize("batch,t,heads", [(4, 1300, 6), (4, 257, 24), (16, 1, 16)])
+def test_attention_batched_partial_query_blocks(path, batch, t, heads):
+    """The one-group workgroups of 256 query rows (at least 256 blocks of 128 rows) when the last
+    query block of each (window, head) is mostly past the window: t = 1300 leaves 20 rows in it
+    (wavefronts 1-7 hold none), t = 257 one row, t = 1 one row in the only block.  Wavefronts
+    without rows only copy their share of the key and value tiles; the rows that exist must
+    still see every key."""
+    assert ((t + 127) // 128) * heads * batch >= 256
+    e, cw = _attention_case(path, batch, t, heads, seed=3 * t + heads)
+    report(f"attn-partial p{path} b{batch} t{t} h{heads} cw={cw:.3e}", e)
+    assert e["finite"] and e["max_rel"] <= ATTN_TOL[path] and cw <= ATTN_CW[path]
+
+
 def test_attention_separate_buffers():
     e, cw = _attention_case(B.WENC_PATH_BF16, 2, 200, 3, seed=3, packed=False)
     assert e["max_rel"] <= ATTN_TOL[B.WENC_PATH_BF16] and cw <= ATTN_CW[B.WENC_PATH_BF16]
